@@ -1,0 +1,209 @@
+"""Benchmark of the quantized paged KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the hot path over the workload: quantize-on-write of the step's new K/V
+tokens into the paged cache, then decode (or MTP-verify) attention over the whole context.
+Default workload: one full-attention layer of a Qwen3.5-MoE-style model with int8 group-64 K and
+V at 131,072 tokens of context (GQA 16:2, head_dim 256, page size 16, seeded random page
+table).  Inputs are resident in HBM before the timed region.  The cache is replicated so that
+consecutive steps read different copies whose total exceeds the 256 MB last-level (Infinity)
+cache: every step streams its codes and scales from HBM.
+
+Prints ONE JSON line.  `value` is microseconds per step (lower is better); `roofline` reports
+the decode attention launch (split-K kernel + log-sum-exp combine, timed with HIP events on the
+stream it runs on) against the 8 TB/s HBM peak on its algorithmic bytes; `cpu_baseline` times
+the CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+METRIC = "decode-attn µs/step + achieved HBM GB/s vs peak, int8 KV @128K ctx"
+
+
+def make_workload(name: str):
+    import synth
+    if name == "moe_int8_decode":
+        return synth.moe_int8_decode(ctx=131072)
+    if name == "moe_int8_decode_64k":
+        return synth.moe_int8_decode(ctx=65536)
+    if name == "k8v4_verify":
+        return synth.k8v4_verify()
+    if name == "batched_int8_decode":
+        return synth.batched_int8_decode()
+    if name == "tiny_int8_decode":
+        return synth.tiny_int8_decode()
+    raise SystemExit(f"unknown workload {name}")
+
+
+def algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v):
+    """Bytes one decode launch must move: every visible cell's codes and scales, the page-table
+    entries it walks, q in, out."""
+    cells = int(np.sum(np.maximum(w.seq_lens, 0)))
+    per_cell = w.n_kv_heads * ((cb_k + 2 * ns_k) + (cb_v + 2 * ns_v))
+    pages = int(np.sum((w.seq_lens + w.page_size - 1) // w.page_size))
+    q = w.batch * w.n_q * w.n_q_heads * w.head_dim * 2
+    out = w.batch * w.n_q * w.n_q_heads * w.head_dim * 4
+    return cells * per_cell + pages * 4 + q + out
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """Time the oracle's step (encode the step's tokens, then fp64 attention over the dequantised
+    cache) on the host cores; the oracle's cache is filled first, outside the timing."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import attention as oatt
+    from oracle import paged as opaged
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sv = opaged.Store.empty(w.fmt_v, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    for b in range(w.batch):
+        P = int(w.seq_lens[b]) - w.n_step
+        opaged.append(sk, w.block_table, np.full(P, b), np.arange(P), w.k[b][:P], w.page_size, quat=w.quat)
+        opaged.append(sv, w.block_table, np.full(P, b), np.arange(P), w.v[b][:P], w.page_size, quat=w.quat)
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        for b in range(w.batch):
+            L = int(w.seq_lens[b])
+            pos = np.arange(L - w.n_step, L)
+            opaged.append(sk, w.block_table, np.full(w.n_step, b), pos, w.k[b][L - w.n_step:], w.page_size, quat=w.quat)
+            opaged.append(sv, w.block_table, np.full(w.n_step, b), pos, w.v[b][L - w.n_step:], w.page_size, quat=w.quat)
+        oatt.decode(sk, sv, w.block_table, w.seq_lens, w.q, w.page_size, w.sm_scale, q_lens=w.q_lens, quat=w.quat)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > budget_s or len(times) >= 20:
+            break
+    per_step = float(np.median(times))
+    return {"value": per_step * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full steps of the same workload (median); numpy fp32 encode of the "
+                      f"step's tokens + fp64 attention over all {int(np.sum(w.seq_lens))} cells"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="moe_int8_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replicas", type=int, default=0, help="cache copies to rotate (0 = enough to exceed the MALL)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the hot path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_paged_kv_kvq_amd as kvq
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from kvq_testutil import dev_bf16, dev_i32, token_lists
+
+    torch.cuda.set_device(0)
+    kvq.lib()
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    w = make_workload(args.workload)
+    cb_k, ns_k = kvq.cell_bytes(w.fmt_k, w.head_dim)
+    cb_v, ns_v = kvq.cell_bytes(w.fmt_v, w.head_dim)
+    cache_bytes = w.num_pages * w.n_kv_heads * 16 * ((cb_k + 2 * ns_k) + (cb_v + 2 * ns_v))
+    R = args.replicas or max(2, int(np.ceil(3 * MALL_BYTES / cache_bytes)) + 1)
+
+    pre = token_lists(w, "prefix")
+    step = token_lists(w, "step")
+    block_table = dev_i32(w.block_table)
+    seq_lens = dev_i32(w.seq_lens)
+    pages = kvq.Pages(block_table, seq_lens)
+    caches = []
+    for r in range(R):
+        c = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, w.fmt_k, w.fmt_v, quat=w.quat)
+        if pre is not None:
+            kvq.kvq_append(c, pages, dev_bf16(pre[2]), dev_bf16(pre[3]), dev_i32(pre[0]), dev_i32(pre[1]))
+        caches.append(c)
+    s_seq, s_pos, s_k, s_v = (dev_i32(step[0]), dev_i32(step[1]), dev_bf16(step[2]), dev_bf16(step[3]))
+    q = dev_bf16(w.q)
+    q_lens = dev_i32(w.q_lens) if w.q_lens is not None else None
+    out = torch.empty((w.batch, w.n_q, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ws_bytes = kvq.kvq_decode_workspace_bytes(caches[0], w.batch, w.max_pages, w.n_q, w.n_q_heads)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] {R} cache replicas of {cache_bytes / 1e6:.1f} MB; warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def one_step(i, timed):
+        c = caches[i % R]
+        kvq.kvq_append(c, pages, s_k, s_v, s_seq, s_pos, stream=stream)
+        if timed:
+            ev[i][0].record(stream)
+        kvq.kvq_decode_attn(c, pages, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out, workspace=ws, stream=stream)
+        if timed:
+            ev[i][1].record(stream)
+
+    for i in range(args.warmup):
+        one_step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    dec_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    dec_avg = float(np.mean(dec_us))
+    algo = algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v)
+    achieved = algo / (dec_avg * 1e-6) / 1e9
+    print(f"[bench] decode launch avg {dec_avg:.2f} us (p10 {np.percentile(dec_us, 10):.2f}, p90 "
+          f"{np.percentile(dec_us, 90):.2f}), step {ms_per_step * 1e3:.2f} us, {achieved:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if w.fmt_v == "int8" else "int8/q4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "context": int(w.seq_lens.max()), "n_q": w.n_q,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "k_format": w.fmt_k, "v_format": w.fmt_v,
+                   "step": "append new K/V token(s) + decode attention", "cache_replicas": R},
+        "decode_us": round(dec_avg, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode attention launch (split-K partials + combine)",
+                     "algorithmic_bytes": int(algo)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

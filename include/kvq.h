@@ -1,0 +1,232 @@
+/*
+ * kvq.h -- C ABI of the quantized paged KV-cache library (MI355X / gfx950).
+ *
+ * The hot path: new bf16 K/V tokens are quantised as they are written into a
+ * paged cache of packed cells (quantize-on-write), and attention then reads the
+ * codes and their FP16 scales page by page and dequantises them inside the
+ * attention loop.
+ *
+ * Sources (the pages this library implements):
+ *   [FT398]  FreeToken PR #398, "feat(kvcache): add ISO3/ISO4 KV-cache quantization
+ *            (--kv-cache-iso)" -- sections "What", "Correctness", "Caveats".
+ *   [ST2698] strata PR #2698, "qwen35/q36: --kv - int8 K/V caches (codes + a FP16
+ *            scale per 64 values)" -- sections "What it does", "Not in this PR".
+ *   [ST120]  strata PR #120, "--kv k8v4: hybrid KV cache -- INT8 K + Hadamard-rotated
+ *            Q4_0 V (816 B/cell)" -- sections "What", "How", "Tests".
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer (cache slabs, page tables, lengths,
+ *     q/k/v, outputs, workspaces).  The library allocates nothing and keeps no
+ *     per-call state; it only caches per-device properties.
+ *   - Pointers marked "device" are HIP device pointers; "host" pointers are read
+ *     during the call only.  Nothing is retained after a call returns.
+ *   - Execution: every call enqueues its kernels on `stream` (a hipStream_t; NULL =
+ *     the legacy default stream) and returns without synchronising.
+ *   - Errors: arguments are validated on the host BEFORE any HIP call; on failure
+ *     the call returns a status, enqueues nothing, and kvq_last_error() gives a
+ *     thread-local message.  Unsupported combinations are refused, never silently
+ *     downgraded (the pages refuse unsupported modes with a message at config
+ *     time: [ST2698] "What it does"/"Not in this PR", [FT398] "Caveats").
+ *     A failed launch returns KVQ_ERR_HIP.
+ *   - Device-side data (page-table entries, lengths, token positions) cannot be
+ *     checked without a synchronisation.  Kernels clamp page ids to
+ *     [0, num_pages) and lengths to [0, max_pages * page_size), so bad device
+ *     data yields wrong values but never an out-of-bounds access.
+ *
+ * Cache layout (one "store" = the K side or the V side)
+ *   scales : float16 [num_pages][n_kv_heads][page_size][n_scales]
+ *   codes  : uint8, one of two byte orders inside a (page, KV head) tile:
+ *     token-major  [num_pages][n_kv_heads][page_size][code_bytes]
+ *                  -- every K store, and ISO3 V stores;
+ *     d-major      [num_pages][n_kv_heads][code_bytes][page_size]
+ *                  -- INT8_G64 and Q4_0_H256 V stores: code byte c of the cell in slot
+ *                  s sits at offset c * page_size + s of the tile.  Attention contracts
+ *                  V over tokens, so this order hands each lane the bytes of consecutive
+ *                  tokens at one position of head_dim.
+ *   Logical token j of sequence b is the cell (page = block_table[b][j / page_size],
+ *   slot = j % page_size).  Codes and scales are separate slabs ([ST2698] "What it
+ *   does"); the page table may be any mapping ([ST120] "Tests" checks a
+ *   non-identity one).  page_size must be 16.
+ *
+ * Formats (code_bytes / n_scales per (token, KV head) cell of one store, D = head_dim)
+ *   KVQ_FMT_INT8_G64  D / D/64.  int8 two's-complement codes; scale = fp16(absmax/127)
+ *                     of each 64 consecutive values; code = clamp(rint(x / (absmax/127)),
+ *                     -127, 127) with the binary32 divisor, ties to even; an all-zero
+ *                     group stores scale +0 and codes 0.  D % 64 == 0, D <= 512.
+ *                     ([ST2698] "What it does"; ties-to-even: [ST120] "Tests".)
+ *   KVQ_FMT_Q4_0_H256 D/2 / D/32.  V only.  The vector is rotated by the orthonormal
+ *                     Walsh-Hadamard transform H = H_256/16 (Sylvester order; binary32
+ *                     butterflies of span 1, 2, ..., 128, then x 1/16), then q4_0: per
+ *                     32 values d = m / -8 with m the first value of largest magnitude,
+ *                     stored fp16; code = clamp(rint(z / d) + 8, 0, 15); byte j holds
+ *                     code 2j (low nibble) and 2j+1 (high nibble); a zero block stores
+ *                     d = +0, codes 8.  Values stay in the rotated basis; attention
+ *                     rotates its output back.  D == 256.
+ *                     ([ST120] "What"/"How"; [ST2698] "Not in this PR".)
+ *   KVQ_FMT_ISO3      D/128*48 / D/128.  Per 128 values: n = ||x|| (binary32 pairwise
+ *                     halving sum of squares, then sqrt); u = x / n; each 4-group
+ *                     (w,x,y,z) is left-multiplied by the unit quaternion iso_quat; each
+ *                     value takes the index of the nearest of the 8 Lloyd-Max centroids
+ *                     {+-0.2451, +-0.7560, +-1.3440, +-2.1520}/sqrt(128) (binary32
+ *                     distances, lowest index on ties); the stored norm is
+ *                     fp16(n / ||chosen centroids||).  Codes are a little-endian 3-bit
+ *                     stream (code i in bits 3i..3i+2, 8 codes per 3 bytes).
+ *                     Dequant: conj(iso_quat) * centroid group, times the norm.
+ *                     D % 128 == 0, D <= 512.  ([FT398] "What".)
+ *
+ * Arithmetic contract of the encoders and of kvq_dequant_gather (F32 output):
+ * binary32, one rounding per operation (no fused multiply-add), correctly rounded
+ * division and square root, round-half-even, binary16 subnormals kept.  Under it
+ * the library's codes, scales and norms are a pure function of the inputs.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_PAGE_SIZE 16
+#define KVQ_MAX_HEAD_DIM 512
+#define KVQ_MAX_Q_HEADS 256
+#define KVQ_MAX_ROWS_PER_KV_HEAD 32   /* n_q * (query heads of one KV head) in decode */
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,         /* a required pointer is NULL */
+  KVQ_ERR_SHAPE = 2,        /* a count or size is out of range or inconsistent */
+  KVQ_ERR_UNSUPPORTED = 3,  /* a format / head_dim / path combination the library refuses */
+  KVQ_ERR_WORKSPACE = 4,    /* workspace missing, too small or misaligned */
+  KVQ_ERR_HIP = 5           /* a HIP runtime call or a kernel launch failed */
+} kvq_status;
+
+typedef enum {
+  KVQ_FMT_INT8_G64 = 1,
+  KVQ_FMT_Q4_0_H256 = 2,
+  KVQ_FMT_ISO3 = 3
+} kvq_fmt;
+
+typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1, KVQ_OUT_BF16 = 2 } kvq_out_dtype;
+
+/* One store.  Both pointers are device pointers, 16-byte aligned; the byte order of
+ * `codes` follows from the store's role and format (see "Cache layout"). */
+typedef struct {
+  int32_t fmt;     /* kvq_fmt */
+  void* codes;     /* uint8 [num_pages][n_kv_heads] tiles of page_size * code_bytes */
+  void* scales;    /* fp16  [num_pages][n_kv_heads][page_size][n_scales] */
+} kvq_store;
+
+/* The cache: geometry plus the K and V stores ([ST120] "How": separate K/V pointers). */
+typedef struct {
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;      /* must be KVQ_PAGE_SIZE */
+  int32_t num_pages;
+  kvq_store k;
+  kvq_store v;
+  float iso_quat[4];      /* (w, x, y, z) used by ISO3 stores; ignored otherwise */
+} kvq_cache;
+
+/* Page table and lengths of a batch of sequences (device pointers). */
+typedef struct {
+  const int32_t* block_table;  /* int32 [batch][max_pages] */
+  const int32_t* seq_lens;     /* int32 [batch]: cells of each sequence that attention reads */
+  int32_t batch;
+  int32_t max_pages;
+} kvq_pages;
+
+/* Quantize-on-write ([FT398] "What": decode tokens are quantised as they are written;
+ * [ST2698] "What it does").  Encodes n_tok bf16 vectors per store and writes each into
+ * the cell of (tok_seq[i], tok_pos[i]) through pages->block_table.  seq_lens is not read
+ * or changed: the caller advances it.
+ *   k_new, v_new : device bf16 [n_tok][n_kv_heads][head_dim]; either may be NULL to skip
+ *                  that store.
+ *   tok_seq      : device int32 [n_tok], sequence index in [0, batch)
+ *   tok_pos      : device int32 [n_tok], logical position in [0, max_pages*page_size)
+ * Out-of-range device indices are clamped (see the conventions above).  Two tokens
+ * writing the same cell in one call race.  n_tok == 0 is a no-op. */
+kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages,
+                      const void* k_new, const void* v_new,
+                      const int32_t* tok_seq, const int32_t* tok_pos,
+                      int32_t n_tok, void* stream);
+
+/* Decode / MTP-verify attention over the packed cache, dequantising K and V inside the
+ * attention loop ([ST2698] "What it does": decode and verify windows dequantise on the
+ * fly; [ST120] "How"/"Tests": per-query step arrays for verify; k8v4 rotates V and the
+ * output only, never q).  Split-K over the context with a log-sum-exp combine.
+ *   q        : device bf16 [batch][n_q][n_q_heads][head_dim]
+ *   q_lens   : device int32 [batch][n_q], cells visible to each query token, or NULL
+ *              (every query token of sequence b sees seq_lens[b] cells)
+ *   head_map : host int32 [n_q_heads], KV head of each query head, or NULL for
+ *              h / (n_q_heads / n_kv_heads) (then n_q_heads % n_kv_heads == 0)
+ *   sm_scale : softmax scale (the caller's 1/sqrt(head_dim) for plain attention)
+ *   out      : device fp32 [batch][n_q][n_q_heads][head_dim]; a query with no visible
+ *              cell gets zeros.  With a Q4_0_H256 V store the output is rotated back.
+ *   workspace: device, >= kvq_decode_workspace_bytes(...) bytes, 256-byte aligned.
+ * Requires n_q * (largest number of query heads of one KV head) <= 32, and a K store
+ * of format INT8_G64 (the V store may be INT8_G64 or Q4_0_H256). */
+kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
+                           const void* q, int32_t n_q, int32_t n_q_heads,
+                           const int32_t* q_lens, const int32_t* head_map,
+                           float sm_scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvq_decode_attn needs for this geometry (0 on invalid arguments). */
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages,
+                                  int32_t n_q, int32_t n_q_heads, const int32_t* head_map);
+
+/* Extend (prefill chunk) attention ([FT398] "What"): new token i of sequence b sits at
+ * position seq_lens[b] + i and attends the seq_lens[b] packed cells (dequantised) plus
+ * new tokens 0..i of its own sequence unquantised (bf16).  With pack_after != 0 the new
+ * tokens are quantised into cells seq_lens[b] + i after the attention, on the same
+ * stream (deferred packing: the chunk never reads its own quantised K/V).  The caller
+ * then advances seq_lens.
+ *   q            : device bf16 [n_new][n_q_heads][head_dim]
+ *   k_new, v_new : device bf16 [n_new][n_kv_heads][head_dim]
+ *   cu_new       : device int32 [batch + 1], offsets of each sequence's new tokens
+ *   max_new      : host bound on cu_new[b+1] - cu_new[b] (sizes the grid)
+ *   out          : device fp32 [n_new][n_q_heads][head_dim]
+ * Requires both stores in the same format, ISO3 or INT8_G64. */
+kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages,
+                           const void* q, const void* k_new, const void* v_new,
+                           const int32_t* cu_new, int32_t n_new, int32_t max_new,
+                           int32_t n_q_heads, const int32_t* head_map,
+                           float sm_scale, float* out, int32_t pack_after,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvq_extend_attn needs (0 on invalid arguments). */
+size_t kvq_extend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages,
+                                  int32_t n_new, int32_t max_new, int32_t n_q_heads);
+
+/* Dequantise cells [start, start+count) of sequence `seq` of one store into a contiguous
+ * buffer ([ST120] "Tests": gather through the page table; [FT398] "What": the one-time
+ * dequant of a packed prefix into a bf16 scratch; [ST2698] "What it does": dequantise a
+ * cache range for a prompt chunk).
+ *   which     : 0 = K store, 1 = V store
+ *   out_dtype : kvq_out_dtype; F32 output is exact (it equals the encoder contract's
+ *               dequantised value), F16/BF16 round it to nearest even
+ *   unrotate  : for a Q4_0_H256 store, nonzero applies H (binary32 butterflies) so the
+ *               output is in the original basis; otherwise the rotated values.
+ *   out       : device [count][n_kv_heads][head_dim] of out_dtype
+ * Requires 0 <= seq < batch, start >= 0, start + count <= max_pages * page_size. */
+kvq_status kvq_dequant_gather(const kvq_cache* cache, const kvq_pages* pages, int32_t which,
+                              int32_t seq, int32_t start, int32_t count, int32_t out_dtype,
+                              int32_t unrotate, void* out, void* stream);
+
+/* Bytes of one (token, KV head) cell of one store: returns code_bytes + 2 * n_scales and
+ * writes the two parts if the pointers are non-NULL; -1 if fmt/head_dim are unsupported. */
+int32_t kvq_cell_bytes(int32_t fmt, int32_t head_dim, int32_t* code_bytes, int32_t* n_scales);
+
+const char* kvq_status_str(kvq_status status);
+const char* kvq_last_error(void);   /* thread-local message of the last failed call */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,74 @@
+"""Build libkvq.so (HIP for gfx950) in place, next to this file.
+
+    python -m quantized_paged_kv_kvq_amd.build [--asm]
+
+The encoder and gather translation units are compiled with -ffp-contract=off so that every
+binary32 product and sum rounds on its own (their output must equal the arithmetic contract
+stated in include/kvq.h bit for bit).  Packed FP32 instructions are disabled for all HIP code.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libkvq.so")
+
+ARCH = "gfx950"
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
+# translation unit -> extra flags
+UNITS = {
+    "kvq_api.hip": [],
+    "append.hip": ["-ffp-contract=off"],
+    "gather.hip": ["-ffp-contract=off"],
+    "decode.hip": [],
+    "extend.hip": [],
+}
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def _compile(unit: str, extra, asm: bool) -> str:
+    src = os.path.join(CSRC, unit)
+    obj = os.path.join(BUILD, unit.replace(".hip", ".o"))
+    cmd = [_hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {unit}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if asm:
+        s = os.path.join(BUILD, unit.replace(".hip", f"-{ARCH}.s"))
+        subprocess.run([_hipcc(), *COMMON, *extra, "--cuda-device-only", "-S", src, "-o", s],
+                       capture_output=True, text=True, check=True)
+    return obj
+
+
+def build(asm: bool = False, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    units = [u for u in UNITS if os.path.exists(os.path.join(CSRC, u))]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(units))) as ex:
+        objs = list(ex.map(lambda u: _compile(u, UNITS[u], asm), units))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(asm="--asm" in sys.argv)

@@ -1,0 +1,272 @@
+// Quantize-on-write kernels: encode bf16 K/V head vectors into paged cells.
+//
+// Built with -ffp-contract=off: every binary32 product and sum is rounded on its own,
+// division and sqrt are the correctly rounded HIP defaults, rintf rounds half to even,
+// and the binary32 -> binary16 conversion rounds to nearest even.  Under that contract
+// each encoder is a pure function of its input vector.
+//
+//   INT8_G64   strata PR #2698, "What it does" (int8 codes + one FP16 scale = absmax/127 per
+//              64 values); strata PR #120, "Tests" (INT8 rounding ties to even).
+//   Q4_0_H256  strata PR #120, "What"/"How" and strata PR #2698, "Not in this PR"
+//              (orthonormal FWHT-256 of V, then q4_0 blocks of 32 with d = signed max-abs / -8).
+//   ISO3       FreeToken PR #398, "What" (per 128 values: L2-normalise, rotate each 4-group by a
+//              unit quaternion, nearest 3-bit Lloyd-Max centroid, corrected norm).
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// (tile, slot) of appended token `tok`: tile = page * hkv + head is added by the caller.
+// Device-side indices are clamped so a bad entry can never address outside the slabs.
+__device__ __forceinline__ void locate(const AppendArgs& a, int tok, int& page, int& slot) {
+  int seq, pos;
+  if (a.cu_new) {
+    int lo = 0, hi = a.batch - 1;                 // last b with cu_new[b] <= tok
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (a.cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    seq = lo;
+    pos = a.seq_lens[seq] + (tok - a.cu_new[seq]);
+  } else {
+    seq = a.tok_seq[tok];
+    pos = a.tok_pos[tok];
+  }
+  seq = clampi(seq, 0, a.batch - 1);
+  pos = clampi(pos, 0, a.max_pages * KVQ_PAGE_SIZE - 1);
+  page = clampi(a.bt[(size_t)seq * a.max_pages + pos / KVQ_PAGE_SIZE], 0, a.num_pages - 1);
+  slot = pos % KVQ_PAGE_SIZE;
+}
+
+// ---------------------------------------------------------------------------------------------
+// INT8_G64.  One thread encodes 4 consecutive values; the 16 threads of a 64-group are 16
+// consecutive lanes, so the group max-abs is a 4-step xor-shuffle reduction (max is exact).
+__global__ __launch_bounds__(256) void k_append_int8(AppendArgs a, const uint16_t* __restrict__ x,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint16_t* __restrict__ scales, int D, int d_major) {
+  const int tpc = D >> 2;                          // threads per cell
+  const int cpb = blockDim.x / tpc;                // cells per block
+  const int local = threadIdx.x / tpc;
+  const int part = threadIdx.x - local * tpc;      // values 4*part .. 4*part+3
+  const long cell = (long)blockIdx.x * cpb + local;
+  const long n_cells = (long)a.n_tok * a.hkv;
+  const bool active = cell < n_cells;
+  const long c = active ? cell : 0;
+  const int tok = (int)(c / a.hkv), head = (int)(c % a.hkv);
+
+  const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * D + 4 * part);
+  float v[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
+                bf16_to_f32(raw.y >> 16)};
+  float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  am = fmaxf(am, __shfl_xor(am, 8));
+  am = fmaxf(am, __shfl_xor(am, 4));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  const float s = am / 127.0f;                     // binary32 scale; fp16 is only its storage
+
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    int q = 0;
+    if (am > 0.0f) q = (int)fminf(fmaxf(rintf(v[e] / s), -127.0f), 127.0f);
+    packed |= (uint32_t)(q & 0xff) << (8 * e);
+  }
+  if (!active) return;
+  int page, slot;
+  locate(a, tok, page, slot);
+  const size_t tile = (size_t)page * a.hkv + head;
+  if (!d_major) {
+    *reinterpret_cast<uint32_t*>(codes + (tile * KVQ_PAGE_SIZE + slot) * D + 4 * part) = packed;
+  } else {
+    uint8_t* base = codes + tile * KVQ_PAGE_SIZE * D + slot;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) base[(size_t)(4 * part + e) * KVQ_PAGE_SIZE] = (uint8_t)(packed >> (8 * e));
+  }
+  if ((part & 15) == 0)
+    scales[(tile * KVQ_PAGE_SIZE + slot) * (D / 64) + (part >> 4)] = f32_to_f16_bits(am > 0.0f ? s : 0.0f);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Q4_0_H256 (V only, d-major).  One wave per cell; lane l holds elements 4l .. 4l+3.
+// FWHT butterflies run in the order of spans 1, 2, 4, ..., 128: spans 1 and 2 inside a lane,
+// spans 4..128 between lanes l and l ^ (span / 4).  Each butterfly maps (a, b) -> (a + b, a - b)
+// for the pair (i, i + span), exactly as the definition, so the result is bit-identical to any
+// other evaluation of the same sequence of stages.
+__device__ __forceinline__ void fwht256_lane(float y[4], int lane) {
+  float a0 = y[0] + y[1], a1 = y[0] - y[1], a2 = y[2] + y[3], a3 = y[2] - y[3];   // span 1
+  y[0] = a0 + a2; y[2] = a0 - a2; y[1] = a1 + a3; y[3] = a1 - a3;                   // span 2
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {                                                // spans 4..128
+    const bool upper = (lane & o) != 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float other = __shfl_xor(y[e], o);
+      y[e] = upper ? (other - y[e]) : (y[e] + other);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = y[e] * 0.0625f;
+}
+
+__global__ __launch_bounds__(256) void k_append_q4h(AppendArgs a, const uint16_t* __restrict__ x,
+                                                    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const long cell = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const bool active = cell < (long)a.n_tok * a.hkv;
+  const long c = active ? cell : 0;
+  const int tok = (int)(c / a.hkv), head = (int)(c % a.hkv);
+
+  const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * 256 + 4 * lane);
+  float y[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
+                bf16_to_f32(raw.y >> 16)};
+  fwht256_lane(y, lane);
+
+  // Signed max-abs of each block of 32 (= 8 lanes): the first index with the largest magnitude.
+  float best = y[0];
+  int bidx = 4 * lane;
+#pragma unroll
+  for (int e = 1; e < 4; ++e)
+    if (fabsf(y[e]) > fabsf(best)) { best = y[e]; bidx = 4 * lane + e; }
+#pragma unroll
+  for (int o = 4; o >= 1; o >>= 1) {
+    const float ob = __shfl_xor(best, o);
+    const int oi = __shfl_xor(bidx, o);
+    if (fabsf(ob) > fabsf(best) || (fabsf(ob) == fabsf(best) && oi < bidx)) { best = ob; bidx = oi; }
+  }
+  const float d = best / -8.0f;
+  uint32_t q[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    q[e] = 8;
+    if (best != 0.0f) q[e] = (uint32_t)fminf(fmaxf(rintf(y[e] / d) + 8.0f, 0.0f), 15.0f);
+  }
+  if (!active) return;
+  int page, slot;
+  locate(a, tok, page, slot);
+  const size_t tile = (size_t)page * a.hkv + head;
+  uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128 + slot;       // d-major: byte j at j*16 + slot
+  base[(size_t)(2 * lane) * KVQ_PAGE_SIZE] = (uint8_t)(q[0] | (q[1] << 4));
+  base[(size_t)(2 * lane + 1) * KVQ_PAGE_SIZE] = (uint8_t)(q[2] | (q[3] << 4));
+  if ((lane & 7) == 0)
+    scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)] = f32_to_f16_bits(best != 0.0f ? d : 0.0f);
+}
+
+// ---------------------------------------------------------------------------------------------
+// ISO3.  One wave per 128-value block; lane l holds elements l and l + 64, so the pairwise
+// halving sum (upper half onto lower half: spans 64, 32, ..., 1) is an in-lane add followed by
+// xor-shuffles 32 .. 1.
+constexpr double kSqrt128 = 11.3137084989847603904135327140;
+__constant__ float kCentroid[8] = {
+    (float)(-2.1520 / kSqrt128), (float)(-1.3440 / kSqrt128), (float)(-0.7560 / kSqrt128),
+    (float)(-0.2451 / kSqrt128), (float)(0.2451 / kSqrt128),  (float)(0.7560 / kSqrt128),
+    (float)(1.3440 / kSqrt128),  (float)(2.1520 / kSqrt128)};
+
+__device__ __forceinline__ float halving_sum128(float lo, float hi) {
+  float s = lo + hi;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s = s + __shfl_xor(s, o);
+  return s;
+}
+
+// Component `comp` of the Hamilton product (w,x,y,z) * (a,b,c,d), each evaluated left to right.
+__device__ __forceinline__ float hamilton(int comp, float w, float x, float y, float z, float a, float b,
+                                          float c, float d) {
+  const float r0 = ((w * a - x * b) - y * c) - z * d;
+  const float r1 = ((w * b + x * a) + y * d) - z * c;
+  const float r2 = ((w * c - x * d) + y * a) + z * b;
+  const float r3 = ((w * d + x * c) - y * b) + z * a;
+  return comp == 0 ? r0 : comp == 1 ? r1 : comp == 2 ? r2 : r3;
+}
+
+__device__ __forceinline__ int nearest_centroid(float r) {
+  int best = 0;
+  float bd = fabsf(r - kCentroid[0]);
+#pragma unroll
+  for (int k = 1; k < 8; ++k) {
+    const float dk = fabsf(r - kCentroid[k]);
+    if (dk < bd) { bd = dk; best = k; }
+  }
+  return best;
+}
+
+__device__ __forceinline__ float rotate_component(float u, int lane, float w, float x, float y, float z) {
+  const int base = lane & ~3;
+  const float a = __shfl(u, base + 0), b = __shfl(u, base + 1), c = __shfl(u, base + 2), d = __shfl(u, base + 3);
+  return hamilton(lane & 3, w, x, y, z, a, b, c, d);
+}
+
+__global__ __launch_bounds__(256) void k_append_iso3(AppendArgs a, const uint16_t* __restrict__ x,
+                                                     uint8_t* __restrict__ codes, uint16_t* __restrict__ norms,
+                                                     int D, float qw, float qx, float qy, float qz) {
+  __shared__ uint8_t lds_codes[4][128];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nb = D / 128;
+  const long blk_id = (long)blockIdx.x * 4 + wv;
+  const bool active = blk_id < (long)a.n_tok * a.hkv * nb;
+  const long bi = active ? blk_id : 0;
+  const long cell = bi / nb;
+  const int blk = (int)(bi % nb);
+  const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
+
+  const uint16_t* src = x + ((size_t)tok * a.hkv + head) * D + blk * 128;
+  const float x0 = bf16_to_f32(src[lane]), x1 = bf16_to_f32(src[64 + lane]);
+  const float n = sqrtf(halving_sum128(x0 * x0, x1 * x1));
+  const float u0 = n > 0.0f ? x0 / n : 0.0f;
+  const float u1 = n > 0.0f ? x1 / n : 0.0f;
+  const float r0 = rotate_component(u0, lane, qw, qx, qy, qz);
+  const float r1 = rotate_component(u1, lane, qw, qx, qy, qz);
+  const int c0 = nearest_centroid(r0), c1 = nearest_centroid(r1);
+  const float k0 = kCentroid[c0], k1 = kCentroid[c1];
+  const float cn = sqrtf(halving_sum128(k0 * k0, k1 * k1));
+  const float norm = n / cn;
+
+  lds_codes[wv][lane] = (uint8_t)c0;
+  lds_codes[wv][64 + lane] = (uint8_t)c1;
+  __syncthreads();
+  if (!active) return;
+  int page, slot;
+  locate(a, tok, page, slot);
+  const size_t tile = (size_t)page * a.hkv + head;
+  const int cb = nb * 48;
+  if (lane < 48) {
+    const int t = lane / 3;                          // 3 bytes hold codes 8t .. 8t+7
+    uint32_t word = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) word |= (uint32_t)lds_codes[wv][8 * t + m] << (3 * m);
+    codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 48 + lane] = (uint8_t)(word >> (8 * (lane % 3)));
+  }
+  if (lane == 0) norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = f32_to_f16_bits(norm);
+}
+
+}  // namespace
+
+hipError_t launch_append(int fmt, bool d_major, const uint16_t* x, uint8_t* codes, uint16_t* scales,
+                         int D, const float quat[4], const AppendArgs& a, hipStream_t s) {
+  const long cells = (long)a.n_tok * a.hkv;
+  if (cells == 0) return hipSuccess;
+  if (fmt == KVQ_FMT_INT8_G64) {
+    const int tpc = D / 4;
+    const int cpb = tpc >= 256 ? 1 : 256 / tpc;
+    const long grid = (cells + cpb - 1) / cpb;
+    k_append_int8<<<dim3((unsigned)grid), dim3(cpb * tpc), 0, s>>>(a, x, codes, scales, D, d_major ? 1 : 0);
+  } else if (fmt == KVQ_FMT_Q4_0_H256) {
+    const long grid = (cells + 3) / 4;
+    k_append_q4h<<<dim3((unsigned)grid), dim3(256), 0, s>>>(a, x, codes, scales);
+  } else {
+    const long blocks = cells * (D / 128);
+    const long grid = (blocks + 3) / 4;
+    k_append_iso3<<<dim3((unsigned)grid), dim3(256), 0, s>>>(a, x, codes, scales, D, quat[0], quat[1], quat[2],
+                                                             quat[3]);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,300 @@
+// C ABI of libkvq: argument validation on the host (before any HIP call), format dispatch,
+// workspace sizing and kernel launches.  Declarations and the contract of every entry point are
+// in include/kvq.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+namespace {
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool fmt_known(int f) { return f == KVQ_FMT_INT8_G64 || f == KVQ_FMT_Q4_0_H256 || f == KVQ_FMT_ISO3; }
+
+// Geometry rules of a store format (the pages validate head_dim at config time with a message).
+kvq_status check_store_fmt(int fmt, int D, bool is_v) {
+  if (!fmt_known(fmt)) return fail(KVQ_ERR_UNSUPPORTED, "unknown store format %d", fmt);
+  if (fmt == KVQ_FMT_INT8_G64 && (D % 64 != 0 || D > KVQ_MAX_HEAD_DIM))
+    return fail(KVQ_ERR_UNSUPPORTED, "INT8_G64 needs head_dim %% 64 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
+  if (fmt == KVQ_FMT_Q4_0_H256 && D != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "Q4_0_H256 needs head_dim == 256 (got %d)", D);
+  if (fmt == KVQ_FMT_Q4_0_H256 && !is_v)
+    return fail(KVQ_ERR_UNSUPPORTED, "Q4_0_H256 is a V-store format (K would need q rotated as well)");
+  if (fmt == KVQ_FMT_ISO3 && (D % 128 != 0 || D > KVQ_MAX_HEAD_DIM))
+    return fail(KVQ_ERR_UNSUPPORTED, "ISO3 needs head_dim %% 128 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_cache* c) {
+  if (!c) return fail(KVQ_ERR_NULL, "cache descriptor is NULL");
+  if (c->page_size != KVQ_PAGE_SIZE) return fail(KVQ_ERR_UNSUPPORTED, "page_size must be %d (got %d)", KVQ_PAGE_SIZE, c->page_size);
+  if (c->n_kv_heads < 1 || c->n_kv_heads > KVQ_MAX_Q_HEADS) return fail(KVQ_ERR_SHAPE, "n_kv_heads %d out of range", c->n_kv_heads);
+  if (c->head_dim < 1) return fail(KVQ_ERR_SHAPE, "head_dim %d out of range", c->head_dim);
+  if (c->num_pages < 1) return fail(KVQ_ERR_SHAPE, "num_pages must be >= 1 (got %d)", c->num_pages);
+  return KVQ_OK;
+}
+
+kvq_status check_store(const kvq_cache* c, const kvq_store& s, bool is_v) {
+  kvq_status st = check_store_fmt(s.fmt, c->head_dim, is_v);
+  if (st != KVQ_OK) return st;
+  if (!s.codes || !s.scales) return fail(KVQ_ERR_NULL, "%s store has a NULL codes or scales pointer", is_v ? "V" : "K");
+  if (((uintptr_t)s.codes & 15) || ((uintptr_t)s.scales & 15))
+    return fail(KVQ_ERR_SHAPE, "%s store slabs must be 16-byte aligned", is_v ? "V" : "K");
+  return KVQ_OK;
+}
+
+kvq_status check_pages(const kvq_pages* p) {
+  if (!p) return fail(KVQ_ERR_NULL, "pages descriptor is NULL");
+  if (!p->block_table || !p->seq_lens) return fail(KVQ_ERR_NULL, "block_table or seq_lens is NULL");
+  if (p->batch < 1 || p->batch > 65535) return fail(KVQ_ERR_SHAPE, "batch %d out of range [1, 65535]", p->batch);
+  if (p->max_pages < 1) return fail(KVQ_ERR_SHAPE, "max_pages must be >= 1 (got %d)", p->max_pages);
+  if ((long)p->max_pages * KVQ_PAGE_SIZE > (1L << 30)) return fail(KVQ_ERR_SHAPE, "max_pages %d too large", p->max_pages);
+  return KVQ_OK;
+}
+
+bool d_major(const kvq_store& s, bool is_v) { return is_v && (s.fmt == KVQ_FMT_INT8_G64 || s.fmt == KVQ_FMT_Q4_0_H256); }
+
+kvq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVQ_OK;
+  return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Rows per KV head for decode: builds head_off / head_list from an explicit or default map.
+kvq_status build_head_lists(int hq, int hkv, const int32_t* head_map, int16_t* off, int16_t* list, int* max_g) {
+  if (hq < 1 || hq > KVQ_MAX_Q_HEADS) return fail(KVQ_ERR_SHAPE, "n_q_heads %d out of range [1, %d]", hq, KVQ_MAX_Q_HEADS);
+  std::vector<int> m(hq);
+  if (head_map) {
+    for (int h = 0; h < hq; ++h) {
+      if (head_map[h] < 0 || head_map[h] >= hkv)
+        return fail(KVQ_ERR_SHAPE, "head_map[%d] = %d outside [0, %d)", h, head_map[h], hkv);
+      m[h] = head_map[h];
+    }
+  } else {
+    if (hq % hkv) return fail(KVQ_ERR_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", hq, hkv);
+    for (int h = 0; h < hq; ++h) m[h] = h / (hq / hkv);
+  }
+  int pos = 0;
+  *max_g = 0;
+  for (int j = 0; j < hkv; ++j) {
+    off[j] = (int16_t)pos;
+    int g = 0;
+    for (int h = 0; h < hq; ++h)
+      if (m[h] == j) { list[pos++] = (int16_t)h; ++g; }
+    if (g > *max_g) *max_g = g;
+  }
+  off[hkv] = (int16_t)pos;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> counts;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)counts.size() <= dev) counts.resize(dev + 1, 0);
+  if (!counts[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_last_error(void) { return g_err; }
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "null pointer";
+    case KVQ_ERR_SHAPE: return "bad shape or size";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported format or geometry";
+    case KVQ_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case KVQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int32_t kvq_cell_bytes(int32_t fmt, int32_t D, int32_t* code_bytes, int32_t* n_scales) {
+  int cb = -1, ns = -1;
+  if (fmt == KVQ_FMT_INT8_G64 && D > 0 && D % 64 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = D; ns = D / 64; }
+  if (fmt == KVQ_FMT_Q4_0_H256 && D == 256) { cb = D / 2; ns = D / 32; }
+  if (fmt == KVQ_FMT_ISO3 && D > 0 && D % 128 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = D / 128 * 48; ns = D / 128; }
+  if (cb < 0) return -1;
+  if (code_bytes) *code_bytes = cb;
+  if (n_scales) *n_scales = ns;
+  return cb + 2 * ns;
+}
+
+kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages, const void* k_new, const void* v_new,
+                      const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok, void* stream) {
+  kvq_status st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if ((st = check_pages(pages)) != KVQ_OK) return st;
+  if (n_tok < 0) return fail(KVQ_ERR_SHAPE, "n_tok must be >= 0 (got %d)", n_tok);
+  if (k_new && (st = check_store(cache, cache->k, false)) != KVQ_OK) return st;
+  if (v_new && (st = check_store(cache, cache->v, true)) != KVQ_OK) return st;
+  if (n_tok == 0 || (!k_new && !v_new)) return KVQ_OK;
+  if (!tok_seq || !tok_pos) return fail(KVQ_ERR_NULL, "tok_seq or tok_pos is NULL");
+  if ((long)n_tok * cache->n_kv_heads > (1L << 31) / 4) return fail(KVQ_ERR_SHAPE, "n_tok %d too large", n_tok);
+  AppendArgs a{tok_seq, tok_pos, pages->block_table, n_tok, pages->batch, pages->max_pages, cache->num_pages,
+               cache->n_kv_heads, nullptr, nullptr};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k_new) {
+    hipError_t e = launch_append(cache->k.fmt, false, static_cast<const uint16_t*>(k_new),
+                                 static_cast<uint8_t*>(cache->k.codes), static_cast<uint16_t*>(cache->k.scales),
+                                 cache->head_dim, cache->iso_quat, a, s);
+    if (e != hipSuccess) return hip_status(e, "append K launch");
+  }
+  if (v_new) {
+    hipError_t e = launch_append(cache->v.fmt, d_major(cache->v, true), static_cast<const uint16_t*>(v_new),
+                                 static_cast<uint8_t*>(cache->v.codes), static_cast<uint16_t*>(cache->v.scales),
+                                 cache->head_dim, cache->iso_quat, a, s);
+    if (e != hipSuccess) return hip_status(e, "append V launch");
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_dequant_gather(const kvq_cache* cache, const kvq_pages* pages, int32_t which, int32_t seq,
+                              int32_t start, int32_t count, int32_t out_dtype, int32_t unrotate, void* out,
+                              void* stream) {
+  kvq_status st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if ((st = check_pages(pages)) != KVQ_OK) return st;
+  if (which != 0 && which != 1) return fail(KVQ_ERR_SHAPE, "which must be 0 (K) or 1 (V), got %d", which);
+  const kvq_store& sto = which ? cache->v : cache->k;
+  if ((st = check_store(cache, sto, which == 1)) != KVQ_OK) return st;
+  if (seq < 0 || seq >= pages->batch) return fail(KVQ_ERR_SHAPE, "seq %d outside [0, %d)", seq, pages->batch);
+  if (start < 0 || count < 0 || (long)start + count > (long)pages->max_pages * KVQ_PAGE_SIZE)
+    return fail(KVQ_ERR_SHAPE, "cells [%d, %d+%d) outside the page table's %d cells", start, start, count,
+                pages->max_pages * KVQ_PAGE_SIZE);
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_BF16)
+    return fail(KVQ_ERR_SHAPE, "unknown out_dtype %d", out_dtype);
+  if (count == 0) return KVQ_OK;
+  if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
+  if ((uintptr_t)out & 15) return fail(KVQ_ERR_SHAPE, "out must be 16-byte aligned");
+  GatherArgs g{pages->block_table, pages->max_pages, cache->num_pages, cache->n_kv_heads, seq, start, count};
+  hipError_t e = launch_gather(sto.fmt, d_major(sto, which == 1), static_cast<const uint8_t*>(sto.codes),
+                               static_cast<const uint16_t*>(sto.scales), cache->head_dim, cache->iso_quat, g,
+                               out_dtype, unrotate != 0, out, static_cast<hipStream_t>(stream));
+  return hip_status(e, "gather launch");
+}
+
+static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t max_pages, int32_t n_q,
+                               int32_t n_q_heads, const int32_t* head_map, DecodeArgs* a, DecodePlan* plan) {
+  kvq_status st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if ((st = check_store_fmt(cache->k.fmt, cache->head_dim, false)) != KVQ_OK) return st;
+  if ((st = check_store_fmt(cache->v.fmt, cache->head_dim, true)) != KVQ_OK) return st;
+  if (cache->k.fmt != KVQ_FMT_INT8_G64)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode needs an INT8_G64 K store (got format %d)", cache->k.fmt);
+  if (cache->v.fmt == KVQ_FMT_ISO3)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode over an ISO3 V store is not provided; use INT8_G64 or Q4_0_H256");
+  const int D = cache->head_dim;
+  if (D != 64 && D != 128 && D != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode supports head_dim 64, 128 or 256 (got %d)", D);
+  if (batch < 1 || batch > 65535) return fail(KVQ_ERR_SHAPE, "batch %d out of range", batch);
+  if (max_pages < 1) return fail(KVQ_ERR_SHAPE, "max_pages must be >= 1");
+  if (n_q < 1) return fail(KVQ_ERR_SHAPE, "n_q must be >= 1 (got %d)", n_q);
+  int max_g = 0;
+  if ((st = build_head_lists(n_q_heads, cache->n_kv_heads, head_map, a->head_off, a->head_list, &max_g)) != KVQ_OK)
+    return st;
+  if ((long)n_q * max_g > KVQ_MAX_ROWS_PER_KV_HEAD)
+    return fail(KVQ_ERR_UNSUPPORTED, "n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
+                KVQ_MAX_ROWS_PER_KV_HEAD);
+  *plan = plan_decode(D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages, int32_t n_q,
+                                  int32_t n_q_heads, const int32_t* head_map) {
+  DecodeArgs a;
+  DecodePlan plan;
+  if (decode_setup(cache, batch, max_pages, n_q, n_q_heads, head_map, &a, &plan) != KVQ_OK) return 0;
+  return plan.part_bytes;
+}
+
+kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, int32_t n_q,
+                           int32_t n_q_heads, const int32_t* q_lens, const int32_t* head_map, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  kvq_status st;
+  if ((st = check_pages(pages)) != KVQ_OK) return st;
+  DecodeArgs a;
+  DecodePlan plan;
+  if ((st = decode_setup(cache, pages->batch, pages->max_pages, n_q, n_q_heads, head_map, &a, &plan)) != KVQ_OK)
+    return st;
+  if ((st = check_store(cache, cache->k, false)) != KVQ_OK) return st;
+  if ((st = check_store(cache, cache->v, true)) != KVQ_OK) return st;
+  if (!q || !out) return fail(KVQ_ERR_NULL, "q or out is NULL");
+  if (((uintptr_t)q & 15) || ((uintptr_t)out & 15)) return fail(KVQ_ERR_SHAPE, "q and out must be 16-byte aligned");
+  if (!(sm_scale == sm_scale)) return fail(KVQ_ERR_SHAPE, "sm_scale is NaN");
+  if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.part_bytes);
+  if ((uintptr_t)workspace & 255) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.part_bytes)
+    return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, decode needs %zu", workspace_bytes, plan.part_bytes);
+  a.k_codes = static_cast<const uint8_t*>(cache->k.codes);
+  a.k_scales = static_cast<const uint16_t*>(cache->k.scales);
+  a.v_codes = static_cast<const uint8_t*>(cache->v.codes);
+  a.v_scales = static_cast<const uint16_t*>(cache->v.scales);
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_lens = q_lens;
+  a.seq_lens = pages->seq_lens;
+  a.bt = pages->block_table;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.hkv = cache->n_kv_heads;
+  a.num_pages = cache->num_pages;
+  a.max_pages = pages->max_pages;
+  a.batch = pages->batch;
+  a.n_q = n_q;
+  a.n_q_heads = n_q_heads;
+  a.pages_per_split = plan.pages_per_split;
+  a.n_splits = plan.n_splits;
+  a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+size_t kvq_extend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages, int32_t n_new,
+                                  int32_t max_new, int32_t n_q_heads) {
+  (void)cache; (void)batch; (void)max_pages; (void)n_new; (void)max_new; (void)n_q_heads;
+  return 0;
+}
+
+kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, const void* k_new,
+                           const void* v_new, const int32_t* cu_new, int32_t n_new, int32_t max_new,
+                           int32_t n_q_heads, const int32_t* head_map, float sm_scale, float* out,
+                           int32_t pack_after, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)pages; (void)q; (void)k_new; (void)v_new; (void)cu_new; (void)n_new; (void)max_new; (void)n_q_heads;
+  (void)head_map; (void)sm_scale; (void)out; (void)pack_after; (void)workspace; (void)workspace_bytes; (void)stream;
+  kvq_status st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  return fail(KVQ_ERR_UNSUPPORTED, "extend attention is not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Library-internal declarations shared by the HIP translation units of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// Where appended tokens go: the page table of a batch plus the per-token (sequence, position).
+struct AppendArgs {
+  const int32_t* tok_seq;   // [n_tok]
+  const int32_t* tok_pos;   // [n_tok]
+  const int32_t* bt;        // [batch][max_pages]
+  int n_tok;
+  int batch;
+  int max_pages;
+  int num_pages;
+  int hkv;
+  // Extend's deferred packing derives (seq, pos) from the chunk layout instead of tok_seq/tok_pos:
+  // token i of the chunk belongs to the sequence b with cu_new[b] <= i < cu_new[b+1] and sits at
+  // position seq_lens[b] + (i - cu_new[b]).
+  const int32_t* cu_new;    // [batch + 1] or nullptr
+  const int32_t* seq_lens;  // [batch] (only with cu_new)
+};
+
+hipError_t launch_append(int fmt, bool d_major, const uint16_t* x, uint8_t* codes, uint16_t* scales,
+                         int head_dim, const float quat[4], const AppendArgs& a, hipStream_t s);
+
+struct GatherArgs {
+  const int32_t* bt;
+  int max_pages;
+  int num_pages;
+  int hkv;
+  int seq;
+  int start;
+  int count;
+};
+
+hipError_t launch_gather(int fmt, bool d_major, const uint8_t* codes, const uint16_t* scales,
+                         int head_dim, const float quat[4], const GatherArgs& g, int out_dtype,
+                         bool unrotate, void* out, hipStream_t s);
+
+// Decode: one row per (query token, query head) of a KV head; rows of KV head j are
+// head_list[head_off[j] .. head_off[j+1]) repeated for every query token.
+struct DecodeArgs {
+  const uint8_t* k_codes;
+  const uint16_t* k_scales;
+  const uint8_t* v_codes;
+  const uint16_t* v_scales;
+  const uint16_t* q;        // bf16 [batch][n_q][n_q_heads][head_dim]
+  const int32_t* q_lens;    // [batch][n_q] or nullptr
+  const int32_t* seq_lens;  // [batch]
+  const int32_t* bt;        // [batch][max_pages]
+  float* part;              // split partials
+  float* out;               // fp32 [batch][n_q][n_q_heads][head_dim]
+  int hkv;
+  int num_pages;
+  int max_pages;
+  int batch;
+  int n_q;
+  int n_q_heads;
+  int pages_per_split;
+  int n_splits;
+  float scale_log2;         // sm_scale * log2(e)
+  int16_t head_off[KVQ_MAX_Q_HEADS + 1];
+  int16_t head_list[KVQ_MAX_Q_HEADS];
+};
+
+struct DecodePlan {
+  int row_tiles;        // 16-row MFMA column tiles per KV head (1 or 2)
+  int waves;            // waves per workgroup
+  int pages_per_split;
+  int n_splits;
+  size_t part_bytes;
+};
+
+DecodePlan plan_decode(int head_dim, int hkv, int batch, int max_pages, int max_rows);
+hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const DecodeArgs& a,
+                         hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace kvq

@@ -1,0 +1,254 @@
+"""Python binding of libkvq (ctypes).  Argument marshalling only: every step of the hot path
+runs in the HIP kernels behind the C ABI declared in include/kvq.h, and each function here has
+the name of the entry point it calls.  PyTorch provides device memory and streams.
+
+There is no fallback: if libkvq.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_size_t, c_void_p
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+FMT = {"int8": 1, "q4h": 2, "iso3": 3}
+OUT_DTYPE = {"f32": (0, torch.float32), "f16": (1, torch.float16), "bf16": (2, torch.bfloat16)}
+PAGE_SIZE = 16
+
+STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_SHAPE", 3: "KVQ_ERR_UNSUPPORTED",
+          4: "KVQ_ERR_WORKSPACE", 5: "KVQ_ERR_HIP"}
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class KvqStore(ctypes.Structure):
+    _fields_ = [("fmt", c_int32), ("codes", c_void_p), ("scales", c_void_p)]
+
+
+class KvqCache(ctypes.Structure):
+    _fields_ = [("n_kv_heads", c_int32), ("head_dim", c_int32), ("page_size", c_int32), ("num_pages", c_int32),
+                ("k", KvqStore), ("v", KvqStore), ("iso_quat", c_float * 4)]
+
+
+class KvqPages(ctypes.Structure):
+    _fields_ = [("block_table", c_void_p), ("seq_lens", c_void_p), ("batch", c_int32), ("max_pages", c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so (built in place by quantized_paged_kv_kvq_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m quantized_paged_kv_kvq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        cp, ip = POINTER(KvqCache), POINTER(KvqPages)
+        L.kvq_append.argtypes = [cp, ip, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
+        L.kvq_decode_attn.argtypes = [cp, ip, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_float, c_void_p,
+                                      c_void_p, c_size_t, c_void_p]
+        L.kvq_decode_workspace_bytes.argtypes = [cp, c_int32, c_int32, c_int32, c_int32, c_void_p]
+        L.kvq_decode_workspace_bytes.restype = c_size_t
+        L.kvq_extend_attn.argtypes = [cp, ip, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                      c_void_p, c_float, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
+        L.kvq_extend_workspace_bytes.argtypes = [cp, c_int32, c_int32, c_int32, c_int32, c_int32]
+        L.kvq_extend_workspace_bytes.restype = c_size_t
+        L.kvq_dequant_gather.argtypes = [cp, ip, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                         c_void_p]
+        L.kvq_cell_bytes.argtypes = [c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)]
+        L.kvq_cell_bytes.restype = c_int32
+        L.kvq_status_str.argtypes = [c_int32]
+        L.kvq_status_str.restype = ctypes.c_char_p
+        L.kvq_last_error.restype = ctypes.c_char_p
+        L.kvq_abi_version.restype = c_int32
+        for name in ("kvq_append", "kvq_decode_attn", "kvq_extend_attn", "kvq_dequant_gather"):
+            getattr(L, name).restype = c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise KVQError(status, lib().kvq_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def cell_bytes(fmt: str, head_dim: int):
+    """(code bytes, fp16 scale count) of one (token, KV head) cell of one store."""
+    cb, ns = c_int32(), c_int32()
+    if lib().kvq_cell_bytes(FMT[fmt], head_dim, ctypes.byref(cb), ctypes.byref(ns)) < 0:
+        raise KVQError(3, f"format {fmt} does not support head_dim {head_dim}")
+    return cb.value, ns.value
+
+
+class PagedKVCache:
+    """Device slabs of a paged quantised KV cache (owned here as torch tensors) and their descriptor.
+
+    codes:  uint8  [num_pages][n_kv_heads][page_size * code_bytes]  (byte order per include/kvq.h)
+    scales: fp16   [num_pages][n_kv_heads][page_size][n_scales]
+    """
+
+    def __init__(self, num_pages: int, n_kv_heads: int, head_dim: int, fmt_k: str = "int8", fmt_v: str = "int8",
+                 device="cuda", quat: Sequence[float] = (1.0, 0.0, 0.0, 0.0)):
+        self.num_pages, self.n_kv_heads, self.head_dim = num_pages, n_kv_heads, head_dim
+        self.fmt_k, self.fmt_v = fmt_k, fmt_v
+        self.quat = [float(x) for x in quat]
+        cbk, nsk = cell_bytes(fmt_k, head_dim)
+        cbv, nsv = cell_bytes(fmt_v, head_dim)
+        self.k_codes = torch.zeros((num_pages, n_kv_heads, PAGE_SIZE * cbk), dtype=torch.uint8, device=device)
+        self.k_scales = torch.zeros((num_pages, n_kv_heads, PAGE_SIZE, nsk), dtype=torch.float16, device=device)
+        self.v_codes = torch.zeros((num_pages, n_kv_heads, PAGE_SIZE * cbv), dtype=torch.uint8, device=device)
+        self.v_scales = torch.zeros((num_pages, n_kv_heads, PAGE_SIZE, nsv), dtype=torch.float16, device=device)
+        self._desc = None
+
+    def descriptor(self) -> KvqCache:
+        if self._desc is None:
+            d = KvqCache()
+            d.n_kv_heads, d.head_dim, d.page_size, d.num_pages = (self.n_kv_heads, self.head_dim, PAGE_SIZE,
+                                                                  self.num_pages)
+            d.k = KvqStore(FMT[self.fmt_k], self.k_codes.data_ptr(), self.k_scales.data_ptr())
+            d.v = KvqStore(FMT[self.fmt_v], self.v_codes.data_ptr(), self.v_scales.data_ptr())
+            d.iso_quat = (c_float * 4)(*self.quat)
+            self._desc = d
+        return self._desc
+
+
+class Pages:
+    """Page table int32 [batch][max_pages] and lengths int32 [batch], both on the device."""
+
+    def __init__(self, block_table: torch.Tensor, seq_lens: torch.Tensor):
+        if block_table.dim() != 2:
+            raise ValueError("block_table must be [batch][max_pages]")
+        self.block_table, self.seq_lens = block_table, seq_lens
+        d = KvqPages()
+        d.block_table = _ptr(block_table, torch.int32, "block_table")
+        d.seq_lens = _ptr(seq_lens, torch.int32, "seq_lens")
+        d.batch, d.max_pages = block_table.shape[0], block_table.shape[1]
+        self._desc = d
+
+    @property
+    def batch(self) -> int:
+        return self._desc.batch
+
+    @property
+    def max_pages(self) -> int:
+        return self._desc.max_pages
+
+    def descriptor(self) -> KvqPages:
+        return self._desc
+
+
+def _head_map_arg(head_map):
+    if head_map is None:
+        return None, None
+    arr = (c_int32 * len(head_map))(*[int(h) for h in head_map])
+    return arr, ctypes.cast(arr, c_void_p)
+
+
+def kvq_append(cache: PagedKVCache, pages: Pages, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+               tok_seq: torch.Tensor, tok_pos: torch.Tensor, stream=None) -> None:
+    """Quantise bf16 [n_tok][n_kv_heads][head_dim] K and/or V into the cells (tok_seq[i], tok_pos[i])."""
+    n_tok = tok_seq.numel()
+    _check(lib().kvq_append(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
+                            _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+                            _ptr(tok_seq, torch.int32, "tok_seq"), _ptr(tok_pos, torch.int32, "tok_pos"),
+                            n_tok, _stream(stream)))
+
+
+def kvq_decode_workspace_bytes(cache: PagedKVCache, batch: int, max_pages: int, n_q: int, n_q_heads: int,
+                               head_map=None) -> int:
+    keep, hm = _head_map_arg(head_map)
+    n = lib().kvq_decode_workspace_bytes(ctypes.byref(cache.descriptor()), batch, max_pages, n_q, n_q_heads, hm)
+    del keep
+    if n == 0:
+        raise KVQError(2, lib().kvq_last_error().decode())
+    return n
+
+
+def kvq_decode_attn(cache: PagedKVCache, pages: Pages, q: torch.Tensor, q_lens: Optional[torch.Tensor] = None,
+                    head_map=None, sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode / verify attention.  q: bf16 [batch][n_q][n_q_heads][head_dim] -> fp32 of the same shape."""
+    B, n_q, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = kvq_decode_workspace_bytes(cache, pages.batch, pages.max_pages, n_q, Hq, head_map)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    keep, hm = _head_map_arg(head_map)
+    _check(lib().kvq_decode_attn(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
+                                 _ptr(q, torch.bfloat16, "q"), n_q, Hq, _ptr(q_lens, torch.int32, "q_lens"), hm,
+                                 float(sm_scale), _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    del keep
+    return out
+
+
+def kvq_extend_workspace_bytes(cache: PagedKVCache, batch: int, max_pages: int, n_new: int, max_new: int,
+                               n_q_heads: int) -> int:
+    return int(lib().kvq_extend_workspace_bytes(ctypes.byref(cache.descriptor()), batch, max_pages, n_new, max_new,
+                                                n_q_heads))
+
+
+def kvq_extend_attn(cache: PagedKVCache, pages: Pages, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    cu_new: torch.Tensor, max_new: int, head_map=None, sm_scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, pack_after: bool = True,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Extend (prefill chunk) attention.  q: bf16 [n_new][n_q_heads][D]; k/v_new: bf16 [n_new][n_kv_heads][D]."""
+    N, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = kvq_extend_workspace_bytes(cache, pages.batch, pages.max_pages, N, max_new, Hq)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    keep, hm = _head_map_arg(head_map)
+    _check(lib().kvq_extend_attn(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
+                                 _ptr(q, torch.bfloat16, "q"), _ptr(k_new, torch.bfloat16, "k_new"),
+                                 _ptr(v_new, torch.bfloat16, "v_new"), _ptr(cu_new, torch.int32, "cu_new"), N,
+                                 int(max_new), Hq, hm, float(sm_scale), _ptr(out, torch.float32, "out"),
+                                 1 if pack_after else 0, _ptr(workspace, None, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    del keep
+    return out
+
+
+def kvq_dequant_gather(cache: PagedKVCache, pages: Pages, which: str, seq: int, start: int, count: int,
+                       out_dtype: str = "f32", unrotate: bool = False, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Dequantised cells [start, start+count) of sequence `seq`: [count][n_kv_heads][head_dim]."""
+    code, tdt = OUT_DTYPE[out_dtype]
+    if out is None:
+        out = torch.empty((count, cache.n_kv_heads, cache.head_dim), dtype=tdt, device=cache.k_codes.device)
+    _check(lib().kvq_dequant_gather(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
+                                    {"k": 0, "v": 1}[which], seq, start, count, code, 1 if unrotate else 0,
+                                    _ptr(out, tdt, "out"), _stream(stream)))
+    return out

@@ -1,0 +1,126 @@
+"""Helpers shared by the tests: move seeded synthetic inputs to the device, run the library's
+entry points, run the oracle on the same inputs, and compare.
+
+Only the seeded generators in synth.py feed both sides; nothing computed by the HIP path is
+ever used as an oracle input or expected value.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import attention as oatt
+from oracle import paged as opaged
+from synth import Workload
+
+ATOL = 1e-3          # max-abs error bound on attention outputs
+MIN_COS = 0.9999     # cosine bound, whole tensor and every row
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def dev_i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
+
+
+def token_lists(w: Workload, which: str):
+    """(tok_seq, tok_pos, bf16 rows) of the prefix ('prefix') or of the step's own tokens ('step')."""
+    seqs, poss, rows = [], [], []
+    src = w.k, w.v
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        P = L - w.n_step
+        lo, hi = (0, P) if which == "prefix" else (P, L)
+        if hi <= lo:
+            continue
+        seqs.append(np.full(hi - lo, b, np.int32))
+        poss.append(np.arange(lo, hi, dtype=np.int32))
+        rows.append((src[0][b][lo:hi], src[1][b][lo:hi]))
+    if not seqs:
+        return None
+    return (np.concatenate(seqs), np.concatenate(poss), np.concatenate([r[0] for r in rows]),
+            np.concatenate([r[1] for r in rows]))
+
+
+def gpu_cache(w: Workload):
+    import quantized_paged_kv_kvq_amd as kvq
+    cache = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, w.fmt_k, w.fmt_v, quat=w.quat)
+    pages = kvq.Pages(dev_i32(w.block_table), dev_i32(w.seq_lens))
+    return cache, pages
+
+
+def gpu_append(w: Workload, cache, pages, which: str):
+    import quantized_paged_kv_kvq_amd as kvq
+    t = token_lists(w, which)
+    if t is None:
+        return
+    seq, pos, k, v = t
+    kvq.kvq_append(cache, pages, dev_bf16(k), dev_bf16(v), dev_i32(seq), dev_i32(pos))
+
+
+def oracle_stores(w: Workload):
+    """Oracle slabs holding every cell of every sequence (prefix and step tokens)."""
+    sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sv = opaged.Store.empty(w.fmt_v, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        if L == 0:
+            continue
+        pos = np.arange(L)
+        opaged.append(sk, w.block_table, np.full(L, b), pos, w.k[b], w.page_size, quat=w.quat)
+        opaged.append(sv, w.block_table, np.full(L, b), pos, w.v[b], w.page_size, quat=w.quat)
+    return sk, sv
+
+
+def gpu_slabs_token_major(cache, which: str):
+    """The device slabs of one store as numpy, codes re-ordered to [page][head][slot][code byte]."""
+    codes = (cache.k_codes if which == "k" else cache.v_codes).cpu().numpy()
+    scales = (cache.k_scales if which == "k" else cache.v_scales).cpu().numpy()
+    fmt = cache.fmt_k if which == "k" else cache.fmt_v
+    npg, hkv, nbytes = codes.shape
+    cb = nbytes // 16
+    if which == "v" and fmt in ("int8", "q4h"):          # d-major V tiles: [code byte][slot]
+        codes = codes.reshape(npg, hkv, cb, 16).transpose(0, 1, 3, 2)
+    else:
+        codes = codes.reshape(npg, hkv, 16, cb)
+    return np.ascontiguousarray(codes), scales
+
+
+def assert_slabs_equal(cache, sk, sv):
+    for which, st in (("k", sk), ("v", sv)):
+        codes, scales = gpu_slabs_token_major(cache, which)
+        bad = np.argwhere(codes != st.codes)
+        assert len(bad) == 0, f"{which} codes differ at {len(bad)} bytes, first {bad[:5].tolist()}"
+        sb = scales.view(np.uint16)
+        ob = st.scales.view(np.uint16)
+        bad = np.argwhere(sb != ob)
+        assert len(bad) == 0, (f"{which} scales differ at {len(bad)} places, first {bad[:5].tolist()} "
+                               f"gpu={sb[tuple(bad[0])]:#06x} oracle={ob[tuple(bad[0])]:#06x}")
+
+
+def oracle_decode(w: Workload, sk, sv, head_map=None, seqs=None):
+    return oatt.decode(sk, sv, w.block_table, w.seq_lens, w.q, w.page_size, w.sm_scale, q_lens=w.q_lens,
+                       head_map=head_map, quat=w.quat, seqs=seqs)
+
+
+def attention_errors(got: np.ndarray, ref: np.ndarray):
+    """(max-abs error, whole-tensor cosine, min row cosine over rows that are not all zero)."""
+    g = got.astype(np.float64).reshape(-1, got.shape[-1])
+    r = ref.astype(np.float64).reshape(-1, ref.shape[-1])
+    maxabs = float(np.max(np.abs(g - r))) if g.size else 0.0
+    cos = float(np.sum(g * r) / max(np.linalg.norm(g) * np.linalg.norm(r), 1e-300)) if g.size else 1.0
+    rn, gn = np.linalg.norm(r, axis=1), np.linalg.norm(g, axis=1)
+    live = rn > 0
+    row_cos = np.sum(g[live] * r[live], axis=1) / np.maximum(gn[live] * rn[live], 1e-300)
+    assert np.all(gn[~live] == 0), "rows with no visible cell must be exactly zero"
+    return maxabs, cos, float(row_cos.min()) if live.any() else 1.0
+
+
+def assert_attention_close(got, ref, atol=ATOL, min_cos=MIN_COS):
+    maxabs, cos, row_cos = attention_errors(got, ref)
+    assert maxabs <= atol and cos > min_cos and row_cos > min_cos, \
+        f"max-abs {maxabs:.3e} (<= {atol}), cosine {cos:.7f}, min row cosine {row_cos:.7f} (> {min_cos})"
+    return maxabs, cos, row_cos

@@ -1,0 +1,120 @@
+"""CPU tests of the C-ABI library: it loads, exports every entry point include/kvq.h declares,
+reports cell sizes that match the oracle, and refuses invalid arguments on the host before any
+HIP call (so none of these need a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_paged_kv_kvq_amd import kvq
+from oracle import paged as opaged
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvq.h")
+FAKE = 1 << 20          # a non-NULL, aligned pointer value that validation never dereferences
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = declared_functions()
+    assert {"kvq_append", "kvq_decode_attn", "kvq_extend_attn", "kvq_dequant_gather"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    ver = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.kvq_abi_version() == ver
+
+
+@pytest.mark.parametrize("fmt,D", [("int8", 64), ("int8", 128), ("int8", 256), ("int8", 512), ("q4h", 256),
+                                   ("iso3", 128), ("iso3", 256)])
+def test_cell_bytes_match_oracle(fmt, D):
+    assert kvq.cell_bytes(fmt, D) == opaged.cell_bytes(fmt, D)
+
+
+def test_cell_bytes_refuses_bad_geometry():
+    L = kvq.lib()
+    for fmt, D in ((1, 100), (2, 128), (3, 64), (9, 128), (1, 1024)):
+        assert L.kvq_cell_bytes(fmt, D, None, None) == -1
+
+
+def make_cache(fk=1, fv=1, D=256, hkv=2, page=16, npages=64):
+    c = kvq.KvqCache()
+    c.n_kv_heads, c.head_dim, c.page_size, c.num_pages = hkv, D, page, npages
+    c.k = kvq.KvqStore(fk, FAKE, FAKE)
+    c.v = kvq.KvqStore(fv, FAKE, FAKE)
+    return c
+
+
+def make_pages(batch=1, max_pages=64):
+    p = kvq.KvqPages()
+    p.block_table, p.seq_lens, p.batch, p.max_pages = FAKE, FAKE, batch, max_pages
+    return p
+
+
+def decode(c, p, n_q=1, hq=16, head_map=None, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    L = kvq.lib()
+    hm = None
+    if head_map is not None:
+        arr = (ctypes.c_int32 * len(head_map))(*head_map)
+        hm = ctypes.cast(arr, ctypes.c_void_p)
+    return L.kvq_decode_attn(ctypes.byref(c) if c else None, ctypes.byref(p) if p else None, q, n_q, hq, None, hm,
+                             0.0625, out, ws, ws_bytes, None)
+
+
+def test_decode_validation_errors():
+    L = kvq.lib()
+    assert decode(None, make_pages()) == 1
+    assert decode(make_cache(), None) == 1
+    assert decode(make_cache(page=8), make_pages()) == 3
+    assert decode(make_cache(fk=2), make_pages()) == 3                 # q4_0 K refused
+    assert decode(make_cache(fk=3, fv=3, D=128), make_pages()) == 3     # ISO3 decode not provided
+    assert decode(make_cache(D=100), make_pages()) == 3                 # int8 needs head_dim % 64
+    assert decode(make_cache(fv=2, D=128), make_pages()) == 3           # Hadamard V needs 256
+    assert decode(make_cache(), make_pages(), hq=15) == 2               # Hq % Hkv
+    assert decode(make_cache(), make_pages(), hq=4, head_map=[0, 1, 2, 0]) == 2   # map out of range
+    assert decode(make_cache(), make_pages(), n_q=5) == 3               # 5 * 8 rows > 32
+    assert decode(make_cache(), make_pages(), n_q=0) == 2
+    assert decode(make_cache(), make_pages(), q=None) == 1
+    assert decode(make_cache(), make_pages(), q=FAKE + 2) == 2          # misaligned
+    assert decode(make_cache(), make_pages(), ws=None) == 4
+    assert decode(make_cache(), make_pages(), ws_bytes=16) == 4
+    assert decode(make_cache(), make_pages(), ws=FAKE + 16) == 4       # needs 256-byte alignment
+    assert decode(make_cache(), make_pages(batch=0)) == 2
+    c = make_cache()
+    c.v = kvq.KvqStore(1, None, FAKE)
+    assert decode(c, make_pages()) == 1
+
+
+def test_decode_workspace_size_formula():
+    L = kvq.lib()
+    c = make_cache()
+    n = L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 1, 16, None)
+    assert n > 0 and n % (16 * (256 + 2) * 4) == 0
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 5, 16, None) == 0
+
+
+def test_append_and_gather_validation_errors():
+    L = kvq.lib()
+    c, p = make_cache(), make_pages()
+    A = lambda c, p, k, v, n, ts=FAKE, tp=FAKE: L.kvq_append(ctypes.byref(c), ctypes.byref(p), k, v, ts, tp, n, None)
+    assert A(c, p, FAKE, FAKE, -1) == 2
+    assert A(c, p, FAKE, FAKE, 0) == 0                 # no-op, nothing launched
+    assert A(c, p, None, None, 5) == 0
+    assert A(c, p, FAKE, FAKE, 5, ts=None) == 1
+    assert A(make_cache(fk=2), p, FAKE, None, 5) == 3   # q4_0 K store refused
+    assert A(make_cache(page=32), p, FAKE, FAKE, 1) == 3
+    G = lambda c, p, which, seq, start, count, dt=0, out=FAKE: L.kvq_dequant_gather(
+        ctypes.byref(c), ctypes.byref(p), which, seq, start, count, dt, 0, out, None)
+    assert G(c, p, 2, 0, 0, 1) == 2
+    assert G(c, p, 0, 1, 0, 1) == 2                    # seq outside the batch
+    assert G(c, p, 0, 0, 64 * 16 - 1, 2) == 2          # past the page table
+    assert G(c, p, 0, 0, -1, 2) == 2
+    assert G(c, p, 0, 0, 0, 1, dt=7) == 2
+    assert G(c, p, 0, 0, 0, 1, out=None) == 1
+    assert G(c, p, 0, 0, 0, 0) == 0
+    assert L.kvq_status_str(3) == b"unsupported format or geometry"
