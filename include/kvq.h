@@ -35,14 +35,20 @@
  *
  * Cache layout (one "store" = the K side or the V side)
  *   scales : float16 [num_pages][n_kv_heads][page_size][n_scales]
- *   codes  : uint8, one of two byte orders inside a (page, KV head) tile:
- *     token-major  [num_pages][n_kv_heads][page_size][code_bytes]
- *                  -- every K store, and ISO3 V stores;
- *     d-major      [num_pages][n_kv_heads][code_bytes][page_size]
- *                  -- INT8_G64 and Q4_0_H256 V stores: code byte c of the cell in slot
- *                  s sits at offset c * page_size + s of the tile.  Attention contracts
- *                  V over tokens, so this order hands each lane the bytes of consecutive
- *                  tokens at one position of head_dim.
+ *   codes  : uint8 [num_pages][n_kv_heads] tiles of page_size * code_bytes bytes.  Inside a tile,
+ *            code byte c (0 <= c < code_bytes) of the cell in slot t (0 <= t < 16) sits at
+ *     INT8_G64 K store            ((c / 16) * 16 + t) * 16 + c % 16
+ *                                 (16-byte chunks, chunk-major: one wave load of 16 bytes per
+ *                                 lane covers a contiguous kilobyte of chunks 0..3 of 16 slots);
+ *     INT8_G64 / Q4_0_H256 V store (((c / 64) * 16 + c % 16) * 4 + t / 4) * 16
+ *                                 + ((c / 16) % 4) * 4 + t % 4
+ *                                 (attention contracts V over tokens: 4 consecutive slots of one
+ *                                 code byte form a 32-bit word, and the words of code bytes c,
+ *                                 c+16, c+32, c+48 form one 16-byte unit);
+ *     ISO3 store (K or V)         t * code_bytes + c   (token-major).
+ *   Every fp16 scale in the slabs must be finite, including those of slots no append has
+ *   written yet (zero-initialise new slabs): attention weighs cells past a sequence's length
+ *   by exact zeros, which a NaN or infinite scale would turn into NaN.
  *   Logical token j of sequence b is the cell (page = block_table[b][j / page_size],
  *   slot = j % page_size).  Codes and scales are separate slabs ([ST2698] "What it
  *   does"); the page table may be any mapping ([ST120] "Tests" checks a

@@ -49,16 +49,16 @@ __device__ __forceinline__ void locate(const AppendArgs& a, int tok, int& page, 
 // ---------------------------------------------------------------------------------------------
 // INT8_G64.  One thread encodes 4 consecutive values; the 16 threads of a 64-group are 16
 // consecutive lanes, so the group max-abs is a 4-step xor-shuffle reduction (max is exact).
-__global__ __launch_bounds__(256) void k_append_int8(AppendArgs a, const uint16_t* __restrict__ x,
-                                                     uint8_t* __restrict__ codes,
-                                                     uint16_t* __restrict__ scales, int D, int d_major) {
+__device__ __forceinline__ void append_int8(const AppendArgs& a, const uint16_t* __restrict__ x,
+                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int D,
+                                            bool is_v, int block) {
   const int tpc = D >> 2;                          // threads per cell
   const int cpb = blockDim.x / tpc;                // cells per block
   const int local = threadIdx.x / tpc;
   const int part = threadIdx.x - local * tpc;      // values 4*part .. 4*part+3
-  const long cell = (long)blockIdx.x * cpb + local;
+  const long cell = (long)block * cpb + local;
   const long n_cells = (long)a.n_tok * a.hkv;
-  const bool active = cell < n_cells;
+  const bool active = local < cpb && cell < n_cells;
   const long c = active ? cell : 0;
   const int tok = (int)(c / a.hkv), head = (int)(c % a.hkv);
 
@@ -83,19 +83,19 @@ __global__ __launch_bounds__(256) void k_append_int8(AppendArgs a, const uint16_
   int page, slot;
   locate(a, tok, page, slot);
   const size_t tile = (size_t)page * a.hkv + head;
-  if (!d_major) {
-    *reinterpret_cast<uint32_t*>(codes + (tile * KVQ_PAGE_SIZE + slot) * D + 4 * part) = packed;
+  uint8_t* base = codes + tile * KVQ_PAGE_SIZE * D;
+  if (!is_v) {
+    *reinterpret_cast<uint32_t*>(base + k_tile_offset(4 * part, slot)) = packed;   // 4 bytes of one chunk
   } else {
-    uint8_t* base = codes + tile * KVQ_PAGE_SIZE * D + slot;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) base[(size_t)(4 * part + e) * KVQ_PAGE_SIZE] = (uint8_t)(packed >> (8 * e));
+    for (int e = 0; e < 4; ++e) base[v_tile_offset(4 * part + e, slot)] = (uint8_t)(packed >> (8 * e));
   }
   if ((part & 15) == 0)
     scales[(tile * KVQ_PAGE_SIZE + slot) * (D / 64) + (part >> 4)] = f32_to_f16_bits(am > 0.0f ? s : 0.0f);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Q4_0_H256 (V only, d-major).  One wave per cell; lane l holds elements 4l .. 4l+3.
+// Q4_0_H256 (V only).  One wave per cell; lane l holds elements 4l .. 4l+3.
 // FWHT butterflies run in the order of spans 1, 2, 4, ..., 128: spans 1 and 2 inside a lane,
 // spans 4..128 between lanes l and l ^ (span / 4).  Each butterfly maps (a, b) -> (a + b, a - b)
 // for the pair (i, i + span), exactly as the definition, so the result is bit-identical to any
@@ -116,10 +116,10 @@ __device__ __forceinline__ void fwht256_lane(float y[4], int lane) {
   for (int e = 0; e < 4; ++e) y[e] = y[e] * 0.0625f;
 }
 
-__global__ __launch_bounds__(256) void k_append_q4h(AppendArgs a, const uint16_t* __restrict__ x,
-                                                    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+__device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* __restrict__ x,
+                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int block) {
   const int lane = threadIdx.x & 63;
-  const long cell = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const long cell = (long)block * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const bool active = cell < (long)a.n_tok * a.hkv;
   const long c = active ? cell : 0;
   const int tok = (int)(c / a.hkv), head = (int)(c % a.hkv);
@@ -152,9 +152,9 @@ __global__ __launch_bounds__(256) void k_append_q4h(AppendArgs a, const uint16_t
   int page, slot;
   locate(a, tok, page, slot);
   const size_t tile = (size_t)page * a.hkv + head;
-  uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128 + slot;       // d-major: byte j at j*16 + slot
-  base[(size_t)(2 * lane) * KVQ_PAGE_SIZE] = (uint8_t)(q[0] | (q[1] << 4));
-  base[(size_t)(2 * lane + 1) * KVQ_PAGE_SIZE] = (uint8_t)(q[2] | (q[3] << 4));
+  uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128;
+  base[v_tile_offset(2 * lane, slot)] = (uint8_t)(q[0] | (q[1] << 4));
+  base[v_tile_offset(2 * lane + 1, slot)] = (uint8_t)(q[2] | (q[3] << 4));
   if ((lane & 7) == 0)
     scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)] = f32_to_f16_bits(best != 0.0f ? d : 0.0f);
 }
@@ -203,13 +203,14 @@ __device__ __forceinline__ float rotate_component(float u, int lane, float w, fl
   return hamilton(lane & 3, w, x, y, z, a, b, c, d);
 }
 
-__global__ __launch_bounds__(256) void k_append_iso3(AppendArgs a, const uint16_t* __restrict__ x,
-                                                     uint8_t* __restrict__ codes, uint16_t* __restrict__ norms,
-                                                     int D, float qw, float qx, float qy, float qz) {
+__device__ __forceinline__ void append_iso3(const AppendArgs& a, const uint16_t* __restrict__ x,
+                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ norms, int D,
+                                            const float quat[4], int block) {
   __shared__ uint8_t lds_codes[4][128];
+  const float qw = quat[0], qx = quat[1], qy = quat[2], qz = quat[3];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nb = D / 128;
-  const long blk_id = (long)blockIdx.x * 4 + wv;
+  const long blk_id = (long)block * 4 + wv;
   const bool active = blk_id < (long)a.n_tok * a.hkv * nb;
   const long bi = active ? blk_id : 0;
   const long cell = bi / nb;
@@ -246,26 +247,52 @@ __global__ __launch_bounds__(256) void k_append_iso3(AppendArgs a, const uint16_
   if (lane == 0) norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = f32_to_f16_bits(norm);
 }
 
+// Blocks needed by one store's encoder for n_tok tokens (256 threads per block).
+long blocks_for(int fmt, int D, long cells) {
+  if (fmt == KVQ_FMT_INT8_G64) {
+    const int cpb = 256 / (D / 4);
+    return (cells + cpb - 1) / cpb;
+  }
+  if (fmt == KVQ_FMT_Q4_0_H256) return (cells + 3) / 4;
+  return (cells * (D / 128) + 3) / 4;
+}
+
+struct StoreArgs {
+  int fmt;
+  int is_v;
+  const uint16_t* x;
+  uint8_t* codes;
+  uint16_t* scales;
+  long blocks;
+};
+
+// One launch encodes both stores: blockIdx.y picks K (0) or V (1); blocks past a store's count exit.
+__global__ __launch_bounds__(256) void k_append(AppendArgs a, StoreArgs k, StoreArgs v, int D, float qw, float qx,
+                                                float qy, float qz) {
+  const StoreArgs& st = blockIdx.y == 0 ? k : v;
+  if ((long)blockIdx.x >= st.blocks) return;
+  const float quat[4] = {qw, qx, qy, qz};
+  if (st.fmt == KVQ_FMT_INT8_G64) append_int8(a, st.x, st.codes, st.scales, D, st.is_v != 0, blockIdx.x);
+  else if (st.fmt == KVQ_FMT_Q4_0_H256) append_q4h(a, st.x, st.codes, st.scales, blockIdx.x);
+  else append_iso3(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
+}
+
 }  // namespace
 
-hipError_t launch_append(int fmt, bool d_major, const uint16_t* x, uint8_t* codes, uint16_t* scales,
-                         int D, const float quat[4], const AppendArgs& a, hipStream_t s) {
+hipError_t launch_append_kv(int fmt_k, const uint16_t* xk, uint8_t* codes_k, uint16_t* scales_k, int fmt_v,
+                            const uint16_t* xv, uint8_t* codes_v, uint16_t* scales_v, int D, const float quat[4],
+                            const AppendArgs& a, hipStream_t s) {
   const long cells = (long)a.n_tok * a.hkv;
-  if (cells == 0) return hipSuccess;
-  if (fmt == KVQ_FMT_INT8_G64) {
-    const int tpc = D / 4;
-    const int cpb = tpc >= 256 ? 1 : 256 / tpc;
-    const long grid = (cells + cpb - 1) / cpb;
-    k_append_int8<<<dim3((unsigned)grid), dim3(cpb * tpc), 0, s>>>(a, x, codes, scales, D, d_major ? 1 : 0);
-  } else if (fmt == KVQ_FMT_Q4_0_H256) {
-    const long grid = (cells + 3) / 4;
-    k_append_q4h<<<dim3((unsigned)grid), dim3(256), 0, s>>>(a, x, codes, scales);
-  } else {
-    const long blocks = cells * (D / 128);
-    const long grid = (blocks + 3) / 4;
-    k_append_iso3<<<dim3((unsigned)grid), dim3(256), 0, s>>>(a, x, codes, scales, D, quat[0], quat[1], quat[2],
-                                                             quat[3]);
+  if (cells == 0 || (!xk && !xv)) return hipSuccess;
+  StoreArgs k{fmt_k, 0, xk, codes_k, scales_k, xk ? blocks_for(fmt_k, D, cells) : 0};
+  StoreArgs v{fmt_v, 1, xv, codes_v, scales_v, xv ? blocks_for(fmt_v, D, cells) : 0};
+  const long gx = k.blocks > v.blocks ? k.blocks : v.blocks;
+  dim3 grid((unsigned)gx, xv ? 2 : 1);
+  if (!xk) {                                 // V only: make it the y == 0 slot
+    k = v;
+    grid.y = 1;
   }
+  k_append<<<grid, dim3(256), 0, s>>>(a, k, v, D, quat[0], quat[1], quat[2], quat[3]);
   return hipGetLastError();
 }
 

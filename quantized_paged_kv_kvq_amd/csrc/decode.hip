@@ -39,6 +39,23 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
+// Launch shapes: waves per workgroup, pages per wave per split (a split is NW * PPW pages), pages
+// each wave keeps in flight ahead of the one it processes, and waves per SIMD the registers allow.
+struct Shape { int nw, ppw, pd, occ; };
+constexpr Shape kShapes[] = {{4, 16, 2, 2}, {4, 8, 1, 2}, {8, 8, 1, 2}};
+constexpr int kDefaultShape = 0;
+
+int shape_index() {
+  static int idx = -1;
+  if (idx < 0) {
+    idx = kDefaultShape;
+    if (const char* e = getenv("KVQ_DECODE_SHAPE")) {
+      const int v = atoi(e);
+      if (v >= 0 && v < (int)(sizeof(kShapes) / sizeof(kShapes[0]))) idx = v;
+    }
+  }
+  return idx;
+}
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 __device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -90,12 +107,41 @@ __device__ __forceinline__ void split_bf16(const float x[4], s16x4& hi, s16x4& l
   lo = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
 }
 
+// Values of lanes l ^ 16 and l ^ 32 through the gfx950 VALU lane swaps (no LDS round trip).
+__device__ __forceinline__ float partner16(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float partner32(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float max_over_row_lanes(float x) {     // max over lanes l, l^16, l^32, l^48
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_row_lanes(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float s1 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s1), __float_as_uint(s1), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The cache is streamed once per step: non-temporal loads keep it from displacing reusable lines.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int N>
 __device__ __forceinline__ void load_words(uint32_t (&dst)[N], const uint32_t* src) {
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int c = 0; c < N / 4; ++c) {
-      const uint4 t = reinterpret_cast<const uint4*>(src)[c];
+      const uint4 t = stream_load(src + 4 * c);
       dst[4 * c] = t.x; dst[4 * c + 1] = t.y; dst[4 * c + 2] = t.z; dst[4 * c + 3] = t.w;
     }
   } else {
@@ -105,13 +151,34 @@ __device__ __forceinline__ void load_words(uint32_t (&dst)[N], const uint32_t* s
   }
 }
 
+__device__ __forceinline__ uint32_t word_of(const uint4& q, int k) {
+  return k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
+}
+
+// One page of one KV head as a lane holds it.  Every code load is one 16-byte load per lane that
+// covers a contiguous kilobyte of the tile across the wave (see the tile byte orders in kvq.h).
+// One part of the hi/lo split, as the bf16 B operand and as the fp32 values it represents: the
+// truncated bf16 hi part (lo_mask == 0) or the truncated bf16 part of the remainder x - hi
+// (lo_mask == ~0).  hi + lo keeps 16 significant bits of x.
+__device__ __forceinline__ void split_bf16_select(const float x[4], uint32_t lo_mask, s16x4& part, float used[4]) {
+  uint32_t b[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t xb = __float_as_uint(x[e]);
+    b[e] = __float_as_uint(x[e] - __uint_as_float(xb & 0xffff0000u & lo_mask)) & 0xffff0000u;
+    used[e] = __uint_as_float(b[e]);
+  }
+  part = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(b[1], b[0], 0x07060302u),
+                                              __builtin_amdgcn_perm(b[3], b[2], 0x07060302u)));
+}
+
 template <int D, int VF>
 struct PageBuf {
-  static constexpr int NG = D / 64;                      // K scale groups
+  static constexpr int NG = D / 64;                      // K scale groups (one 16-byte K load each)
   static constexpr int NVG = VF == 1 ? D / 64 : D / 32;  // V scale groups
-  static constexpr int NVW = VF == 1 ? D / 16 : D / 32;  // V dwords per lane
-  uint4 k[NG];                // K codes: token lane%16, bytes 64g + 16*(lane/16) .. +15
-  uint32_t v[NVW];            // V codes: 4 tokens 4*(lane/16).. at one head_dim position (or pair)
+  static constexpr int NVQ = VF == 1 ? D / 64 : D / 128; // 16-byte V loads
+  uint4 k[NG];                // K: token lane%16, head_dim 64g + 16*(lane/16) .. +15
+  uint4 v[NVQ];               // V: word k of v[G] = 4 tokens 4*(lane/16).. at one head_dim row of tile 4G+k
   uint32_t ks[2 * NG];        // fp16 pairs: K scale of token 4*(lane/16) + k, group g is half k*NG + g
   uint32_t vs[2 * NVG];       // V scales likewise
   __device__ __forceinline__ float kscale(int k, int g) const { return half_at(ks, k * NG + g); }
@@ -127,172 +194,292 @@ __device__ __forceinline__ void load_page(PageBuf<D, VF>& pb, const DecodeArgs& 
   constexpr int NG = PageBuf<D, VF>::NG, NVG = PageBuf<D, VF>::NVG;
   const int i16 = lane & 15, j4 = lane >> 4;
   const size_t tile = (size_t)page * a.hkv + kvh;
-  const uint8_t* kb = a.k_codes + tile * (16 * D) + (size_t)i16 * D + 16 * j4;
+  // K tile: 16-byte chunk c of slot t at (c * 16 + t) * 16; this lane's chunk for group g is 4g + j4
+  const uint4* kb = reinterpret_cast<const uint4*>(a.k_codes + tile * (16 * D)) + lane;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) pb.k[g] = *reinterpret_cast<const uint4*>(kb + 64 * g);
-  const uint8_t* vb = a.v_codes + tile * (16 * (VF == 1 ? D : D / 2)) + (size_t)i16 * 16 + 4 * j4;
+  for (int g = 0; g < NG; ++g) pb.k[g] = stream_load(kb + 64 * g);
+  load_words<2 * NG>(pb.ks, reinterpret_cast<const uint32_t*>(a.k_scales + (tile * 16 + 4 * j4) * NG));
+  // V tile: 16-byte unit (64*G + 4*i16 + j4) holds tiles 4G..4G+3 (one word each) of row i16
+  const uint4* vb = reinterpret_cast<const uint4*>(a.v_codes + tile * (16 * (VF == 1 ? D : D / 2))) + 4 * i16 + j4;
 #pragma unroll
-  for (int t = 0; t < PageBuf<D, VF>::NVW; ++t) pb.v[t] = *reinterpret_cast<const uint32_t*>(vb + 256 * t);
-  // scales of this lane's 4 tokens: 4*NG (resp. 4*NVG) consecutive fp16 values
-  const uint32_t* ksb = reinterpret_cast<const uint32_t*>(a.k_scales + (tile * 16 + 4 * j4) * NG);
-  const uint32_t* vsb = reinterpret_cast<const uint32_t*>(a.v_scales + (tile * 16 + 4 * j4) * NVG);
-  load_words<2 * NG>(pb.ks, ksb);
-  load_words<2 * NVG>(pb.vs, vsb);
+  for (int G = 0; G < PageBuf<D, VF>::NVQ; ++G) pb.v[G] = stream_load(vb + 64 * G);
+  load_words<2 * NVG>(pb.vs, reinterpret_cast<const uint32_t*>(a.v_scales + (tile * 16 + 4 * j4) * NVG));
 }
 
-template <int D, int RT, int VF>
-__device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j4, const int (&Lrow)[RT],
-                                          const f16x8 (&qf)[RT][D / 64][2], const float (&qmul)[RT],
+// One page of one wave: QK on MFMA, online softmax, PV on MFMA.
+// DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the bf16 hi part of
+// the softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both.
+template <int D, int RT, int VF, bool DUP>
+__device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j4, bool lo_col, const int (&Lrow)[RT],
+                                          const f16x8* __restrict__ qf, const float (&qmul)[RT],
                                           float (&m_run)[RT], float (&l_run)[RT],
                                           float (&ls)[RT][VF == 1 ? D / 64 : D / 32], f32x4 (&O)[RT][D / 16]) {
   constexpr int NG = D / 64;
   constexpr int NVG = VF == 1 ? D / 64 : D / 32;
   constexpr int NT = D / 16;
 
-    // ---- QK: S^T[token 4*j4 + k][row] per 64-group
-    f32x4 acc[RT][NG];
+  // ---- QK: S^T[token 4*j4 + k][row] per 64-group
+  f32x4 acc[RT][NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const f16x8 a0 = codes_to_f16(pb.k[g].x, pb.k[g].y);
-      const f16x8 a1 = codes_to_f16(pb.k[g].z, pb.k[g].w);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        acc[rt][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[rt][g][0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        acc[rt][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf[rt][g][1], acc[rt][g], 0, 0, 0);
-      }
-    }
-    const int tok0 = p * KVQ_PAGE_SIZE + 4 * j4;
-
+  for (int g = 0; g < NG; ++g) {
+    const f16x8 a0 = codes_to_f16(pb.k[g].x, pb.k[g].y);
+    const f16x8 a1 = codes_to_f16(pb.k[g].z, pb.k[g].w);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float s[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float v = 0.0f;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) v += acc[rt][g][k] * pb.kscale(k, g);
-        s[k] = (tok0 + k < Lrow[rt]) ? v * qmul[rt] : kNegInf;
-      }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[rt], mx);
-      const float m_use = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
-      m_run[rt] = m_new;
-      float pk[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_use);
-      l_run[rt] = l_run[rt] * alpha + ((pk[0] + pk[1]) + (pk[2] + pk[3]));
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) O[rt][t] *= alpha;
-#pragma unroll
-        for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
-      }
+      const f16x8 b0 = qf[((rt * NG + g) * 2 + 0) * 64], b1 = qf[((rt * NG + g) * 2 + 1) * 64];
+      acc[rt][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      acc[rt][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[rt][g], 0, 0, 0);
+    }
+  }
+  const int tok0 = p * KVQ_PAGE_SIZE + 4 * j4;
 
-      // ---- PV per V scale group
 #pragma unroll
-      for (int g = 0; g < NVG; ++g) {
-        float pw[4];
+  for (int rt = 0; rt < RT; ++rt) {
+    float s[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pw[k] = (tok0 + k < Lrow[rt]) ? pk[k] * pb.vscale(k, g) : 0.0f;
-        ls[rt][g] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-        s16x4 bhi, blo;
-        split_bf16(pw, bhi, blo);
-        if constexpr (VF == 1) {
+    for (int k = 0; k < 4; ++k) {
+      float v = acc[rt][0][k] * pb.kscale(k, 0);
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {              // tiles 4g .. 4g+3 (head_dim 64g .. 64g+63)
-            const int t = 4 * g + tt;
-            const s16x4 av = codes_to_bf16_biased(pb.v[t]);
-            O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bhi, O[rt][t], 0, 0, 0);
-            O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, blo, O[rt][t], 0, 0, 0);
-          }
-        } else {
-          const uint32_t w = pb.v[g];                  // pair rows 16g + i16: d = 32g + 2*i16 (+1)
-          const s16x4 alo = nibbles_to_bf16_biased(w & 0x0f0f0f0fu);
-          const s16x4 ahi = nibbles_to_bf16_biased((w >> 4) & 0x0f0f0f0fu);
-          O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bhi, O[rt][2 * g], 0, 0, 0);
-          O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, O[rt][2 * g], 0, 0, 0);
-          O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bhi, O[rt][2 * g + 1], 0, 0, 0);
-          O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, O[rt][2 * g + 1], 0, 0, 0);
-        }
-      }
+      for (int g = 1; g < NG; ++g) v = fmaf(acc[rt][g][k], pb.kscale(k, g), v);
+      s[k] = (tok0 + k < Lrow[rt]) ? v * qmul[rt] : kNegInf;
+    }
+    const float mx = max_over_row_lanes(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    const float m_new = fmaxf(m_run[rt], mx);
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
+    m_run[rt] = m_new;
+    float pk[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_use);
+    l_run[rt] = l_run[rt] * alpha + ((pk[0] + pk[1]) + (pk[2] + pk[3]));
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) O[rt][t] *= alpha;
+#pragma unroll
+      for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
     }
 
+    // ---- PV per V scale group
+#pragma unroll
+    for (int g = 0; g < NVG; ++g) {
+      float pw[4];
+#pragma unroll
+      // masked tokens have pk == 0; the scales of cells past a sequence's length are finite by
+      // contract (zero-initialised slabs), so their weights are exact zeros without a select
+      for (int k = 0; k < 4; ++k) pw[k] = pk[k] * pb.vscale(k, g);
+      s16x4 bhi, blo;
+      if constexpr (DUP) {
+        float used[4];
+        split_bf16_select(pw, lo_col ? 0xffffffffu : 0u, bhi, used);
+        ls[rt][g] += (used[0] + used[1]) + (used[2] + used[3]);
+        if constexpr (VF == 1) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int t = 4 * g + tt;
+            O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(codes_to_bf16_biased(word_of(pb.v[g], tt)), bhi,
+                                                                 O[rt][t], 0, 0, 0);
+          }
+        } else {
+          const uint32_t w = word_of(pb.v[g >> 2], g & 3);
+          O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nibbles_to_bf16_biased(w & 0x0f0f0f0fu), bhi,
+                                                                   O[rt][2 * g], 0, 0, 0);
+          O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              nibbles_to_bf16_biased((w >> 4) & 0x0f0f0f0fu), bhi, O[rt][2 * g + 1], 0, 0, 0);
+        }
+        continue;
+      }
+      ls[rt][g] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+      split_bf16(pw, bhi, blo);
+      if constexpr (VF == 1) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {              // tiles 4g .. 4g+3 (head_dim 64g .. 64g+63)
+          const int t = 4 * g + tt;
+          const s16x4 av = codes_to_bf16_biased(word_of(pb.v[g], tt));
+          O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bhi, O[rt][t], 0, 0, 0);
+          O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, blo, O[rt][t], 0, 0, 0);
+        }
+      } else {
+        const uint32_t w = word_of(pb.v[g >> 2], g & 3);   // pair row 16g + i16: d = 32g + 2*i16 (+1)
+        const s16x4 alo = nibbles_to_bf16_biased(w & 0x0f0f0f0fu);
+        const s16x4 ahi = nibbles_to_bf16_biased((w >> 4) & 0x0f0f0f0fu);
+        O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bhi, O[rt][2 * g], 0, 0, 0);
+        O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, O[rt][2 * g], 0, 0, 0);
+        O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bhi, O[rt][2 * g + 1], 0, 0, 0);
+        O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, O[rt][2 * g + 1], 0, 0, 0);
+      }
+    }
+  }
 }
 
-template <int D, int RT, int VF, int NW>
-__global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void k_decode_split(const DecodeArgs a) {
+// y <- sum over butterflies of the rotated-basis row held as 64 values by the 4 lanes of a row
+// (k8v4): value (t, k) of O is head_dim 32*(t/2) + 8*j4 + 2*k + (t&1).  Applies H = H_256/16.
+template <int RT>
+__device__ __forceinline__ void hadamard_rows(f32x4 (&O)[RT][16], int lane) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    // bit 0 of head_dim: tile parity
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e = O[rt][2 * b][k], o = O[rt][2 * b + 1][k];
+        O[rt][2 * b][k] = e + o; O[rt][2 * b + 1][k] = e - o;
+      }
+    // bits 1, 2: k
+#pragma unroll
+    for (int kb = 1; kb <= 2; kb <<= 1)
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (!(k & kb)) {
+            const float x = O[rt][t][k], y = O[rt][t][k | kb];
+            O[rt][t][k] = x + y; O[rt][t][k | kb] = x - y;
+          }
+    // bits 3, 4: lane groups (xor 16, 32)
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const bool upper = (lane & o) != 0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float other = o == 16 ? partner16(O[rt][t][k], lane) : partner32(O[rt][t][k], lane);
+          O[rt][t][k] = upper ? (other - O[rt][t][k]) : (O[rt][t][k] + other);
+        }
+    }
+    // bits 5..7: block index b = t/2
+#pragma unroll
+    for (int bb = 1; bb <= 4; bb <<= 1)
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if (!(b & bb))
+#pragma unroll
+          for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float x = O[rt][2 * b + par][k], y = O[rt][2 * (b | bb) + par][k];
+              O[rt][2 * b + par][k] = x + y; O[rt][2 * (b | bb) + par][k] = x - y;
+            }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) O[rt][t] *= 0.0625f;
+  }
+}
+
+template <int D, int RT, int VF, int NW, int PPW, int PD, int OCC, bool DUP>
+__global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs a) {
   constexpr int NG = D / 64;
   constexpr int NVG = VF == 1 ? D / 64 : D / 32;
   constexpr int NT = D / 16;                                // PV tiles of 16 head_dim rows
   constexpr int RA = 16 * RT;                               // allocated rows
   constexpr float kOff = VF == 1 ? 128.0f : 136.0f;         // bias carried by the V A-operand
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // wave-uniform wave index: page ids then come through scalar loads, which do not wait on the
+  // vector-memory counter that tracks the prefetched page
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, j4 = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
 
-  const int h0 = a.head_off[kvh];
-  const int G = a.head_off[kvh + 1] - h0;
+  // ---- rows of this KV head.  With the default grouping (query head h reads KV head h / G) the
+  // q addresses are arithmetic on kernel arguments; an explicit head map goes through the lists.
+  int G, h0;
+  if (a.g_uniform > 0) {
+    G = a.g_uniform;
+    h0 = kvh * G;
+  } else {
+    h0 = a.head_off[kvh];
+    G = a.head_off[kvh + 1] - h0;
+  }
   const int R = a.n_q * G;
   const int cap = a.max_pages * KVQ_PAGE_SIZE;
+  const bool lo_col = DUP && i16 >= 8;
+  int Lrow[RT];
+  bool valid[RT];
+  int qrow[RT];
   const int seq_len = clampi(a.seq_lens[b], 0, cap);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = DUP ? (i16 & 7) : 16 * rt + i16;
+    valid[rt] = r < R;
+    const int t = valid[rt] ? r / G : 0;
+    const int i = valid[rt] ? r % G : 0;
+    const int hq = a.g_uniform > 0 ? h0 + i : a.head_list[h0 + i];
+    qrow[rt] = (b * a.n_q + t) * a.n_q_heads + hq;
+    Lrow[rt] = valid[rt] ? (a.q_lens ? clampi(a.q_lens[(size_t)b * a.n_q + t], 0, cap) : seq_len) : 0;
+  }
+  // ---- then q (one batch), then this wave's first PD pages.  Vector-memory waits are in issue
+  // order, so everything the prologue needs is issued before the page stream; the pages depend
+  // only on page-table entries of this split (clamped to the table), not on lengths or rows, and a
+  // page past the sequence's end is loaded but never processed.
+  uint4 raw[RT][NG][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const uint16_t* qp = a.q + (size_t)qrow[rt] * D + 16 * j4;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      raw[rt][g][0] = *reinterpret_cast<const uint4*>(qp + 64 * g);
+      raw[rt][g][1] = *reinterpret_cast<const uint4*>(qp + 64 * g + 8);
+    }
+  }
+  const int* bt_row = a.bt + (size_t)b * a.max_pages;
+  const int p_begin = split * a.pages_per_split;
+  const int p0 = p_begin + wv;
+  const int p_cap = min(p_begin + a.pages_per_split, a.max_pages) - 1;
+  PageBuf<D, VF> buf[PD + 1];
+#pragma unroll
+  for (int i = 0; i < PD && i < PPW; ++i)
+    load_page<D, VF>(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, lane);
+
   int Lmax = 0;
   for (int t = 0; t < a.n_q; ++t)
     Lmax = max(Lmax, a.q_lens ? clampi(a.q_lens[(size_t)b * a.n_q + t], 0, cap) : seq_len);
   const int npages = (Lmax + KVQ_PAGE_SIZE - 1) / KVQ_PAGE_SIZE;
-  const int p_begin = split * a.pages_per_split;
   const int p_end = min(p_begin + a.pages_per_split, npages);
-  float* part = a.part + ((size_t)(b * a.hkv + kvh) * a.n_splits + split) * (RA * (D + 2));
+  // partials: m/l [B][Hkv][RA][n_splits][2], then O [B][Hkv][RA][n_splits][D]
+  const size_t row0 = (size_t)(b * a.hkv + kvh) * RA;
+  float* part_ml = a.part;
+  float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   if (R == 0) return;
   if (p_begin >= p_end) {                                   // nothing visible in this split
-    if (threadIdx.x < RA) { part[2 * threadIdx.x] = kNegInf; part[2 * threadIdx.x + 1] = 0.0f; }
+    if (threadIdx.x < RA) {
+      float* ml = part_ml + ((row0 + threadIdx.x) * a.n_splits + split) * 2;
+      ml[0] = kNegInf; ml[1] = 0.0f;
+    }
     return;
   }
 
-  // ---- per-row state; lane's column is row r = 16*rt + i16
-  int Lrow[RT];
-  f16x8 qf[RT][NG][2];
+  // q fragments of this lane (B operand of QK) live in LDS: [wave][rt][g][half][lane] x 16 bytes
+  __shared__ f16x8 lds_q[NW * RT * NG * 2 * 64];
+  f16x8* qf = lds_q + wv * (RT * NG * 2 * 64) + lane;
   float qmul[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + i16;
-    const bool valid = r < R;
-    const int t = valid ? r / G : 0;
-    const int hq = a.head_list[h0 + (valid ? r % G : 0)];
-    Lrow[rt] = valid ? (a.q_lens ? clampi(a.q_lens[(size_t)b * a.n_q + t], 0, cap) : seq_len) : 0;
-    const uint16_t* qp = a.q + (((size_t)b * a.n_q + t) * a.n_q_heads + hq) * D + 16 * j4;
     float mx = 0.0f;
-    uint4 raw[NG][2];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      raw[g][0] = *reinterpret_cast<const uint4*>(qp + 64 * g);
-      raw[g][1] = *reinterpret_cast<const uint4*>(qp + 64 * g + 8);
-      if (!valid) { raw[g][0] = make_uint4(0, 0, 0, 0); raw[g][1] = make_uint4(0, 0, 0, 0); }
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint32_t w[4] = {raw[g][h].x, raw[g][h].y, raw[g][h].z, raw[g][h].w};
+        if (!valid[rt]) raw[rt][g][h] = make_uint4(0, 0, 0, 0);
+        const uint32_t w[4] = {raw[rt][g][h].x, raw[rt][g][h].y, raw[rt][g][h].z, raw[rt][g][h].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           mx = fmaxf(mx, fmaxf(fabsf(bf16f(w[e] & 0xffffu)), fabsf(bf16f(w[e] >> 16))));
       }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_row_lanes(mx);
     int ex = 0;
     if (mx > 0.0f) { frexpf(mx, &ex); ex = 15 - ex; }        // max * 2^ex in [2^14, 2^15)
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint32_t w[4] = {raw[g][h].x, raw[g][h].y, raw[g][h].z, raw[g][h].w};
+        const uint32_t w[4] = {raw[rt][g][h].x, raw[rt][g][h].y, raw[rt][g][h].z, raw[rt][g][h].w};
+        f16x8 f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qf[rt][g][h][2 * e] = (_Float16)ldexpf(bf16f(w[e] & 0xffffu), ex);
-          qf[rt][g][h][2 * e + 1] = (_Float16)ldexpf(bf16f(w[e] >> 16), ex);
+          f[2 * e] = (_Float16)ldexpf(bf16f(w[e] & 0xffffu), ex);
+          f[2 * e + 1] = (_Float16)ldexpf(bf16f(w[e] >> 16), ex);
         }
+        qf[((rt * NG + g) * 2 + h) * 64] = f;
       }
     qmul[rt] = ldexpf(a.scale_log2, -ex);
   }
@@ -309,30 +496,33 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void k_decode_split(const
     for (int t = 0; t < NT; ++t) O[rt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  const int* bt_row = a.bt + (size_t)b * a.max_pages;
-  PageBuf<D, VF> b0, b1;
-  int p = p_begin + wv;
-  if (p < p_end) load_page<D, VF>(b0, a, clampi(bt_row[p], 0, a.num_pages - 1), kvh, lane);
-  while (p < p_end) {
-    if (p + NW < p_end) load_page<D, VF>(b1, a, clampi(bt_row[p + NW], 0, a.num_pages - 1), kvh, lane);
-    page_step<D, RT, VF>(b0, p, j4, Lrow, qf, qmul, m_run, l_run, ls, O);
-    p += NW;
-    if (p >= p_end) break;
-    if (p + NW < p_end) load_page<D, VF>(b0, a, clampi(bt_row[p + NW], 0, a.num_pages - 1), kvh, lane);
-    page_step<D, RT, VF>(b1, p, j4, Lrow, qf, qmul, m_run, l_run, ls, O);
-    p += NW;
+  // Each wave takes pages p_begin + wv, + NW, ... (at most PPW of them) and keeps PD pages in
+  // flight ahead of the one it processes, in a ring of PD + 1 register buffers (the first PD were
+  // issued at kernel entry).  The page loop is
+  // fully unrolled, so the ring index is a constant and the code is straight-line with forward
+  // exits only: every wait on the vector memory counter then covers exactly the page about to be
+  // processed.  Prefetches past the wave's last page re-read that page (an L2 hit), so no branch
+  // guards a load.
+  if (p0 < p_end) {
+    const int n_mine = (p_end - 1 - p0) / NW + 1;          // pages of this wave, >= 1
+    const int p_last = p0 + (n_mine - 1) * NW;
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int pc = p0 + i * NW;
+      if (i + PD < PPW)
+        load_page<D, VF>(buf[(i + PD) % (PD + 1)], a, clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1),
+                         kvh, lane);
+      page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qf, qmul, m_run, l_run, ls, O);
+      if (i + 1 >= n_mine) break;
+    }
   }
 
   // ---- per-wave totals: row sums over the 4 lane groups; remove the V operand bias
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    l_run[rt] += __shfl_xor(l_run[rt], 16);
-    l_run[rt] += __shfl_xor(l_run[rt], 32);
+    l_run[rt] = sum_over_row_lanes(l_run[rt]);
 #pragma unroll
-    for (int g = 0; g < NVG; ++g) {
-      ls[rt][g] += __shfl_xor(ls[rt][g], 16);
-      ls[rt][g] += __shfl_xor(ls[rt][g], 32);
-    }
+    for (int g = 0; g < NVG; ++g) ls[rt][g] = sum_over_row_lanes(ls[rt][g]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int g = VF == 1 ? t / 4 : t / 2;
@@ -380,15 +570,28 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void k_decode_split(const
     }
   }
   if (wv != 0) return;
+  if constexpr (DUP) {            // column r + 8 holds the lo-part sums of row r: add them in
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = O[0][t][k];
+        O[0][t][k] = x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+      }
+  }
+  // k8v4: rotate the (unnormalised) partial back now; the combine is linear, so H commutes with it
+  if constexpr (VF == 2) hadamard_rows<RT>(O, lane);
 
-  // ---- write the workgroup's partial: rows r < R, layout [RA][2] (m, l) then [RA][D]
-  float* po = part + 2 * RA;
+  // ---- write the workgroup's partial for rows r < R
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = 16 * rt + i16;
-    if (r >= R) continue;
-    if (j4 == 0) { part[2 * r] = m_run[rt]; part[2 * r + 1] = l_run[rt]; }
-    float* row = po + (size_t)r * D;
+    if (r >= R || (DUP && i16 >= 8)) continue;
+    if (j4 == 0) {
+      float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
+      ml[0] = m_run[rt]; ml[1] = l_run[rt];
+    }
+    float* row = part_o + ((row0 + r) * a.n_splits + split) * D;
     if constexpr (VF == 1) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)   // lane holds d = 16t + 4*j4 + k
@@ -404,26 +607,30 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void k_decode_split(const
   }
 }
 
-// Log-sum-exp combine of the split partials of one row; k8v4 rows are rotated back by H.
-template <int D, bool ROT>
+// Log-sum-exp combine of the split partials.  One workgroup per (64 head_dim values, row, KV head,
+// sequence): the split weights 2^(m_s - M) are computed once into LDS, then 16 groups of 16 lanes
+// stream the splits' 64-value slices and a final LDS reduction normalises.
+constexpr int kMaxSplits = 8192;
+
+template <int D>
 __global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int row_alloc) {
-  __shared__ float w_s[1024];
+  __shared__ float w_s[kMaxSplits];
   __shared__ float red[256];
-  __shared__ float acc_s[1024];
-  const int r = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int h0 = a.head_off[kvh];
-  const int G = a.head_off[kvh + 1] - h0;
+  __shared__ float4 acc_s[256];
+  constexpr int NC = D / 64;
+  const int c = blockIdx.x % NC, r = blockIdx.x / NC, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int h0 = a.g_uniform > 0 ? kvh * a.g_uniform : a.head_off[kvh];
+  const int G = a.g_uniform > 0 ? a.g_uniform : a.head_off[kvh + 1] - h0;
   if (r >= a.n_q * G) return;
-  const int t = r / G, hq = a.head_list[h0 + r % G];
-  const size_t stride = (size_t)row_alloc * (D + 2);
-  const float* base = a.part + (size_t)(b * a.hkv + kvh) * a.n_splits * stride;
+  const int t = r / G, hq = a.g_uniform > 0 ? h0 + r % G : a.head_list[h0 + r % G];
   const int S = a.n_splits;
+  const size_t row = (size_t)(b * a.hkv + kvh) * row_alloc + r;
+  const float* ml = a.part + row * S * 2;
+  const float* po = a.part + (size_t)a.batch * a.hkv * row_alloc * S * 2 + row * S * D + 64 * c;
 
   float mx = kNegInf;
-  for (int s = tid; s < S; s += 256) {
-    const float l = base[s * stride + 2 * r + 1];
-    if (l > 0.0f) mx = fmaxf(mx, base[s * stride + 2 * r]);
-  }
+  for (int s = tid; s < S; s += 256)
+    if (ml[2 * s + 1] > 0.0f) mx = fmaxf(mx, ml[2 * s]);
   red[tid] = mx;
   __syncthreads();
   for (int o = 128; o >= 1; o >>= 1) {
@@ -434,8 +641,8 @@ __global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int 
   __syncthreads();
   float den = 0.0f;
   for (int s = tid; s < S; s += 256) {
-    const float l = base[s * stride + 2 * r + 1];
-    const float w = l > 0.0f ? __builtin_amdgcn_exp2f(base[s * stride + 2 * r] - M) : 0.0f;
+    const float l = ml[2 * s + 1];
+    const float w = l > 0.0f ? __builtin_amdgcn_exp2f(ml[2 * s] - M) : 0.0f;
     w_s[s] = w;
     den += w * l;
   }
@@ -446,82 +653,85 @@ __global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int 
     __syncthreads();
   }
   const float total = red[0];
-  constexpr int TPR = D / 4;                   // threads per row (float4 each)
-  constexpr int SG = 256 / TPR;                // split groups
-  const int c4 = tid % TPR, sg = tid / TPR;
+
+  const int sl = tid >> 4, d4 = tid & 15;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int s = sg; s < S; s += SG) {
+  // Loads are unconditional so that several are in flight per thread; a split with no visible
+  // cell (weight 0) never wrote its slice, so its contribution is selected away, not multiplied.
+#pragma unroll 8
+  for (int s = sl; s < S; s += 16) {
     const float w = w_s[s];
-    if (w == 0.0f) continue;
-    const float4 v = *reinterpret_cast<const float4*>(base + s * stride + 2 * row_alloc + (size_t)r * D + 4 * c4);
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+    const float4 v = *reinterpret_cast<const float4*>(po + (size_t)s * D + 4 * d4);
+    const bool on = w != 0.0f;
+    acc.x += on ? w * v.x : 0.0f; acc.y += on ? w * v.y : 0.0f;
+    acc.z += on ? w * v.z : 0.0f; acc.w += on ? w * v.w : 0.0f;
   }
-  acc_s[sg * D + 4 * c4 + 0] = acc.x; acc_s[sg * D + 4 * c4 + 1] = acc.y;
-  acc_s[sg * D + 4 * c4 + 2] = acc.z; acc_s[sg * D + 4 * c4 + 3] = acc.w;
+  acc_s[tid] = acc;
   __syncthreads();
-  const float inv = total > 0.0f ? 1.0f / total : 0.0f;
-  for (int d = tid; d < D; d += 256) {
-    float v = 0.0f;
-    for (int g = 0; g < SG; ++g) v += acc_s[g * D + d];
-    acc_s[d] = v * inv;
-  }
-  __syncthreads();
-  if constexpr (ROT) {                         // y <- H y with H = H_256 / 16, spans 1 .. 128
-    for (int h = 1; h < D; h <<= 1) {
-      float nv = 0.0f;
-      const int d = tid;
-      if (d < D) {
-        const float me = acc_s[d], other = acc_s[d ^ h];
-        nv = (d & h) ? (other - me) : (me + other);
-      }
-      __syncthreads();
-      if (d < D) acc_s[d] = nv;
-      __syncthreads();
+  if (tid < 16) {
+    float4 sum = acc_s[tid];
+#pragma unroll
+    for (int g = 1; g < 16; ++g) {
+      const float4 v = acc_s[16 * g + tid];
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
     }
+    const float inv = total > 0.0f ? 1.0f / total : 0.0f;
+    float* out = a.out + (((size_t)b * a.n_q + t) * a.n_q_heads + hq) * D + 64 * c + 4 * tid;
+    *reinterpret_cast<float4*>(out) = make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
   }
-  float* out = a.out + (((size_t)b * a.n_q + t) * a.n_q_heads + hq) * D;
-  for (int d = tid; d < D; d += 256) out[d] = ROT ? acc_s[d] * 0.0625f : acc_s[d];
 }
 
-template <int D, int RT, int VF, int NW>
+template <int D, int RT, int VF, int SH>
 hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+  // two row tiles (verify windows) keep 128 accumulator registers per lane: one wave per SIMD,
+  // four waves per workgroup, one page of prefetch
+  constexpr Shape sh = RT == 1 ? kShapes[SH] : Shape{4, 8, 1, 1};
+  constexpr int PD = sh.pd;
   dim3 grid(plan.n_splits, a.hkv, a.batch);
-  k_decode_split<D, RT, VF, NW><<<grid, dim3(NW * 64), 0, s>>>(a);
+  if (RT == 1 && plan.dup)
+    k_decode_split<D, RT, VF, sh.nw, sh.ppw, PD, sh.occ, true><<<grid, dim3(sh.nw * 64), 0, s>>>(a);
+  else
+    k_decode_split<D, RT, VF, sh.nw, sh.ppw, PD, sh.occ, false><<<grid, dim3(sh.nw * 64), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid(16 * RT, a.hkv, a.batch);
-  k_decode_combine<D, VF == 2><<<cgrid, dim3(256), 0, s>>>(a, 16 * RT);
+  dim3 cgrid((D / 64) * 16 * RT, a.hkv, a.batch);
+  k_decode_combine<D><<<cgrid, dim3(256), 0, s>>>(a, 16 * RT);
   return hipGetLastError();
+}
+
+template <int D, int RT, int VF>
+hipError_t launch_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+  switch (shape_index()) {
+    case 1: return launch_t<D, RT, VF, 1>(plan, a, s);
+    case 2: return launch_t<D, RT, VF, 2>(plan, a, s);
+    default: return launch_t<D, RT, VF, 0>(plan, a, s);
+  }
 }
 
 }  // namespace
 
+int decode_max_splits() { return kMaxSplits; }
+
 DecodePlan plan_decode(int head_dim, int hkv, int batch, int max_pages, int max_rows) {
   DecodePlan p{};
   p.row_tiles = max_rows <= 16 ? 1 : 2;
-  p.waves = 4;
-  const long total = (long)batch * hkv * max_pages;
-  const long target = 2L * device_cu_count();
-  long pps = (total + target - 1) / target;
-  if (const char* env = getenv("KVQ_DECODE_PPS")) pps = atol(env);
-  if (pps < 4) pps = 4;
-  long ns = (max_pages + pps - 1) / pps;
-  if (ns > 1024) { pps = (max_pages + 1023) / 1024; ns = (max_pages + pps - 1) / pps; }
-  if (ns < 1) ns = 1;
-  p.pages_per_split = (int)pps;
-  p.n_splits = (int)ns;
-  p.part_bytes = (size_t)batch * hkv * ns * (16 * p.row_tiles) * (head_dim + 2) * sizeof(float);
+  const Shape sh = p.row_tiles == 1 ? kShapes[shape_index()] : Shape{4, 8, 1, 1};
+  p.dup = max_rows <= 8;
+  p.waves = sh.nw;
+  p.pages_per_split = sh.nw * sh.ppw;
+  p.n_splits = (max_pages + p.pages_per_split - 1) / p.pages_per_split;
+  p.part_bytes = (size_t)batch * hkv * p.n_splits * (16 * p.row_tiles) * (head_dim + 2) * sizeof(float);
   return p;
 }
 
 hipError_t launch_decode(int v_fmt, int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   const bool q4 = v_fmt == KVQ_FMT_Q4_0_H256;
   const int rt = plan.row_tiles;
-  if (q4) return rt == 1 ? launch_t<256, 1, 2, 4>(plan, a, s) : launch_t<256, 2, 2, 4>(plan, a, s);
+  if (q4) return rt == 1 ? launch_shape<256, 1, 2>(plan, a, s) : launch_shape<256, 2, 2>(plan, a, s);
   switch (D) {
-    case 64: return rt == 1 ? launch_t<64, 1, 1, 4>(plan, a, s) : launch_t<64, 2, 1, 4>(plan, a, s);
-    case 128: return rt == 1 ? launch_t<128, 1, 1, 4>(plan, a, s) : launch_t<128, 2, 1, 4>(plan, a, s);
-    case 256: return rt == 1 ? launch_t<256, 1, 1, 4>(plan, a, s) : launch_t<256, 2, 1, 4>(plan, a, s);
+    case 64: return rt == 1 ? launch_shape<64, 1, 1>(plan, a, s) : launch_shape<64, 2, 1>(plan, a, s);
+    case 128: return rt == 1 ? launch_shape<128, 1, 1>(plan, a, s) : launch_shape<128, 2, 1>(plan, a, s);
+    case 256: return rt == 1 ? launch_shape<256, 1, 1>(plan, a, s) : launch_shape<256, 2, 1>(plan, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -39,7 +39,7 @@ __device__ __forceinline__ void store4(void* out, size_t idx, const float v[4], 
 
 // INT8_G64: one thread per 4 consecutive values of a cell.
 __global__ __launch_bounds__(256) void k_gather_int8(GatherArgs g, const uint8_t* __restrict__ codes,
-                                                     const uint16_t* __restrict__ scales, int D, int d_major,
+                                                     const uint16_t* __restrict__ scales, int D, int is_v,
                                                      void* out, int dtype) {
   const int tpc = D / 4;
   const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -54,14 +54,13 @@ __global__ __launch_bounds__(256) void k_gather_int8(GatherArgs g, const uint8_t
   float v[4];
   for (int e = 0; e < 4; ++e) {
     const int d = 4 * part + e;
-    const size_t off = d_major ? tile * KVQ_PAGE_SIZE * D + (size_t)d * KVQ_PAGE_SIZE + slot
-                               : (tile * KVQ_PAGE_SIZE + slot) * D + d;
+    const size_t off = tile * KVQ_PAGE_SIZE * D + (is_v ? v_tile_offset(d, slot) : k_tile_offset(d, slot));
     v[e] = (float)(int8_t)codes[off] * s;
   }
   store4(out, ((size_t)i * g.hkv + head) * D + 4 * part, v, dtype);
 }
 
-// Q4_0_H256 (d-major V): one wave per cell, lane l holds elements 4l .. 4l+3.
+// Q4_0_H256 (V): one wave per cell, lane l holds elements 4l .. 4l+3.
 __global__ __launch_bounds__(256) void k_gather_q4h(GatherArgs g, const uint8_t* __restrict__ codes,
                                                     const uint16_t* __restrict__ scales, void* out, int dtype,
                                                     int unrotate) {
@@ -72,8 +71,8 @@ __global__ __launch_bounds__(256) void k_gather_q4h(GatherArgs g, const uint8_t*
   const int i = (int)(c / g.hkv), head = (int)(c % g.hkv);
   int slot;
   const size_t tile = tile_of(g, i, head, slot);
-  const uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128 + slot;
-  const uint32_t b0 = base[(size_t)(2 * lane) * KVQ_PAGE_SIZE], b1 = base[(size_t)(2 * lane + 1) * KVQ_PAGE_SIZE];
+  const uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128;
+  const uint32_t b0 = base[v_tile_offset(2 * lane, slot)], b1 = base[v_tile_offset(2 * lane + 1, slot)];
   const float d = f16_bits_to_f32(scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)]);
   float y[4] = {(float)((int)(b0 & 15) - 8) * d, (float)((int)(b0 >> 4) - 8) * d, (float)((int)(b1 & 15) - 8) * d,
                 (float)((int)(b1 >> 4) - 8) * d};
@@ -132,14 +131,14 @@ __global__ __launch_bounds__(256) void k_gather_iso3(GatherArgs g, const uint8_t
 
 }  // namespace
 
-hipError_t launch_gather(int fmt, bool d_major, const uint8_t* codes, const uint16_t* scales, int D,
+hipError_t launch_gather(int fmt, bool is_v, const uint8_t* codes, const uint16_t* scales, int D,
                          const float quat[4], const GatherArgs& g, int out_dtype, bool unrotate, void* out,
                          hipStream_t s) {
   const long cells = (long)g.count * g.hkv;
   if (cells == 0) return hipSuccess;
   if (fmt == KVQ_FMT_INT8_G64) {
     const long threads = cells * (D / 4);
-    k_gather_int8<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, d_major ? 1 : 0,
+    k_gather_int8<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, is_v ? 1 : 0,
                                                                                out, out_dtype);
   } else if (fmt == KVQ_FMT_Q4_0_H256) {
     k_gather_q4h<<<dim3((unsigned)((cells + 3) / 4)), dim3(256), 0, s>>>(g, codes, scales, out, out_dtype,

@@ -67,8 +67,6 @@ kvq_status check_pages(const kvq_pages* p) {
   return KVQ_OK;
 }
 
-bool d_major(const kvq_store& s, bool is_v) { return is_v && (s.fmt == KVQ_FMT_INT8_G64 || s.fmt == KVQ_FMT_Q4_0_H256); }
-
 kvq_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return KVQ_OK;
   return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -164,20 +162,12 @@ kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages, const void
   if ((long)n_tok * cache->n_kv_heads > (1L << 31) / 4) return fail(KVQ_ERR_SHAPE, "n_tok %d too large", n_tok);
   AppendArgs a{tok_seq, tok_pos, pages->block_table, n_tok, pages->batch, pages->max_pages, cache->num_pages,
                cache->n_kv_heads, nullptr, nullptr};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (k_new) {
-    hipError_t e = launch_append(cache->k.fmt, false, static_cast<const uint16_t*>(k_new),
-                                 static_cast<uint8_t*>(cache->k.codes), static_cast<uint16_t*>(cache->k.scales),
-                                 cache->head_dim, cache->iso_quat, a, s);
-    if (e != hipSuccess) return hip_status(e, "append K launch");
-  }
-  if (v_new) {
-    hipError_t e = launch_append(cache->v.fmt, d_major(cache->v, true), static_cast<const uint16_t*>(v_new),
-                                 static_cast<uint8_t*>(cache->v.codes), static_cast<uint16_t*>(cache->v.scales),
-                                 cache->head_dim, cache->iso_quat, a, s);
-    if (e != hipSuccess) return hip_status(e, "append V launch");
-  }
-  return KVQ_OK;
+  hipError_t e = launch_append_kv(cache->k.fmt, static_cast<const uint16_t*>(k_new),
+                                  static_cast<uint8_t*>(cache->k.codes), static_cast<uint16_t*>(cache->k.scales),
+                                  cache->v.fmt, static_cast<const uint16_t*>(v_new),
+                                  static_cast<uint8_t*>(cache->v.codes), static_cast<uint16_t*>(cache->v.scales),
+                                  cache->head_dim, cache->iso_quat, a, static_cast<hipStream_t>(stream));
+  return hip_status(e, "append launch");
 }
 
 kvq_status kvq_dequant_gather(const kvq_cache* cache, const kvq_pages* pages, int32_t which, int32_t seq,
@@ -199,7 +189,7 @@ kvq_status kvq_dequant_gather(const kvq_cache* cache, const kvq_pages* pages, in
   if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
   if ((uintptr_t)out & 15) return fail(KVQ_ERR_SHAPE, "out must be 16-byte aligned");
   GatherArgs g{pages->block_table, pages->max_pages, cache->num_pages, cache->n_kv_heads, seq, start, count};
-  hipError_t e = launch_gather(sto.fmt, d_major(sto, which == 1), static_cast<const uint8_t*>(sto.codes),
+  hipError_t e = launch_gather(sto.fmt, which == 1, static_cast<const uint8_t*>(sto.codes),
                                static_cast<const uint16_t*>(sto.scales), cache->head_dim, cache->iso_quat, g,
                                out_dtype, unrotate != 0, out, static_cast<hipStream_t>(stream));
   return hip_status(e, "gather launch");
@@ -228,6 +218,9 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
     return fail(KVQ_ERR_UNSUPPORTED, "n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
                 KVQ_MAX_ROWS_PER_KV_HEAD);
   *plan = plan_decode(D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
+  if (plan->n_splits > decode_max_splits())
+    return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d needs %d context splits; decode supports %d", max_pages,
+                plan->n_splits, decode_max_splits());
   return KVQ_OK;
 }
 
@@ -276,6 +269,10 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const
   a.pages_per_split = plan.pages_per_split;
   a.n_splits = plan.n_splits;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  // the default grouping (explicit maps that coincide with it included) lets kernels skip the lists
+  a.g_uniform = n_q_heads % cache->n_kv_heads == 0 ? n_q_heads / cache->n_kv_heads : 0;
+  for (int h = 0; h < n_q_heads && a.g_uniform; ++h)
+    if (a.head_list[h] != h || (h % a.g_uniform == 0 && a.head_off[h / a.g_uniform] != h)) a.g_uniform = 0;
   return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, static_cast<hipStream_t>(stream)),
                     "decode launch");
 }

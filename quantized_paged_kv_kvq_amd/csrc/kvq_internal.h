@@ -8,6 +8,16 @@
 
 namespace kvq {
 
+// Byte order of code byte c of the cell in slot t inside one (page, KV head) tile (see kvq.h):
+//   INT8_G64 K stores: 16-byte chunks, chunk-major -- a wave reads a contiguous kilobyte per load
+//   INT8_G64 / Q4_0_H256 V stores: 4 consecutive slots of one code byte form a 32-bit word; the
+//     words of code bytes c, c+16, c+32, c+48 (c % 64 < 16) form a 16-byte unit
+//   ISO3 stores: token-major
+__host__ __device__ inline int k_tile_offset(int c, int t) { return ((c >> 4) * 16 + t) * 16 + (c & 15); }
+__host__ __device__ inline int v_tile_offset(int c, int t) {
+  return ((((c >> 6) << 4) | (c & 15)) * 4 + (t >> 2)) * 16 + ((c >> 4) & 3) * 4 + (t & 3);
+}
+
 // Where appended tokens go: the page table of a batch plus the per-token (sequence, position).
 struct AppendArgs {
   const int32_t* tok_seq;   // [n_tok]
@@ -25,8 +35,10 @@ struct AppendArgs {
   const int32_t* seq_lens;  // [batch] (only with cu_new)
 };
 
-hipError_t launch_append(int fmt, bool d_major, const uint16_t* x, uint8_t* codes, uint16_t* scales,
-                         int head_dim, const float quat[4], const AppendArgs& a, hipStream_t s);
+// Encode n_tok tokens into the K store and/or the V store (x == nullptr skips a store), one launch.
+hipError_t launch_append_kv(int fmt_k, const uint16_t* xk, uint8_t* codes_k, uint16_t* scales_k, int fmt_v,
+                            const uint16_t* xv, uint8_t* codes_v, uint16_t* scales_v, int head_dim,
+                            const float quat[4], const AppendArgs& a, hipStream_t s);
 
 struct GatherArgs {
   const int32_t* bt;
@@ -38,7 +50,7 @@ struct GatherArgs {
   int count;
 };
 
-hipError_t launch_gather(int fmt, bool d_major, const uint8_t* codes, const uint16_t* scales,
+hipError_t launch_gather(int fmt, bool is_v, const uint8_t* codes, const uint16_t* scales,
                          int head_dim, const float quat[4], const GatherArgs& g, int out_dtype,
                          bool unrotate, void* out, hipStream_t s);
 
@@ -64,12 +76,14 @@ struct DecodeArgs {
   int pages_per_split;
   int n_splits;
   float scale_log2;         // sm_scale * log2(e)
+  int g_uniform;            // G when query head h reads KV head h / G (the default map), else 0
   int16_t head_off[KVQ_MAX_Q_HEADS + 1];
   int16_t head_list[KVQ_MAX_Q_HEADS];
 };
 
 struct DecodePlan {
   int row_tiles;        // 16-row MFMA column tiles per KV head (1 or 2)
+  bool dup;             // at most 8 rows: hi/lo weight parts share one MFMA (columns 0-7 / 8-15)
   int waves;            // waves per workgroup
   int pages_per_split;
   int n_splits;
@@ -81,5 +95,6 @@ hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const 
                          hipStream_t s);
 
 int device_cu_count();
+int decode_max_splits();
 
 }  // namespace kvq

@@ -75,6 +75,26 @@ def oracle_stores(w: Workload):
     return sk, sv
 
 
+def tile_index(layout: str, cb: int) -> np.ndarray:
+    """idx[t][c] = offset inside a (page, KV head) tile of code byte c of the cell in slot t, for the
+    byte orders documented in include/kvq.h."""
+    t = np.arange(16)[:, None]
+    c = np.arange(cb)[None, :]
+    if layout == "token":
+        return t * cb + c
+    if layout == "k_chunk":
+        return ((c >> 4) * 16 + t) * 16 + (c & 15)
+    if layout == "v_quad":
+        return ((((c >> 6) << 4) | (c & 15)) * 4 + (t >> 2)) * 16 + ((c >> 4) & 3) * 4 + (t & 3)
+    raise ValueError(layout)
+
+
+def store_layout(fmt: str, which: str) -> str:
+    if fmt == "iso3":
+        return "token"
+    return "k_chunk" if which == "k" else "v_quad"
+
+
 def gpu_slabs_token_major(cache, which: str):
     """The device slabs of one store as numpy, codes re-ordered to [page][head][slot][code byte]."""
     codes = (cache.k_codes if which == "k" else cache.v_codes).cpu().numpy()
@@ -82,11 +102,9 @@ def gpu_slabs_token_major(cache, which: str):
     fmt = cache.fmt_k if which == "k" else cache.fmt_v
     npg, hkv, nbytes = codes.shape
     cb = nbytes // 16
-    if which == "v" and fmt in ("int8", "q4h"):          # d-major V tiles: [code byte][slot]
-        codes = codes.reshape(npg, hkv, cb, 16).transpose(0, 1, 3, 2)
-    else:
-        codes = codes.reshape(npg, hkv, 16, cb)
-    return np.ascontiguousarray(codes), scales
+    idx = tile_index(store_layout(fmt, which), cb)
+    assert sorted(idx.ravel().tolist()) == list(range(nbytes)), "tile byte order must be a permutation"
+    return np.ascontiguousarray(codes[:, :, idx]), scales
 
 
 def assert_slabs_equal(cache, sk, sv):
