@@ -173,8 +173,9 @@ kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages,
  *   out      : device fp32 [batch][n_q][n_q_heads][head_dim]; a query with no visible
  *              cell gets zeros.  With a Q4_0_H256 V store the output is rotated back.
  *   workspace: device, >= kvq_decode_workspace_bytes(...) bytes, 256-byte aligned.
- * Requires n_q * (largest number of query heads of one KV head) <= 32, and a K store
- * of format INT8_G64 (the V store may be INT8_G64 or Q4_0_H256). */
+ * Requires n_q * (largest number of query heads of one KV head) <= 32, head_dim 64,
+ * 128 or 256, and a K store of format INT8_G64 (the V store may be INT8_G64 or
+ * Q4_0_H256). */
 kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
                            const void* q, int32_t n_q, int32_t n_q_heads,
                            const int32_t* q_lens, const int32_t* head_map,
@@ -193,10 +194,17 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
  * then advances seq_lens.
  *   q            : device bf16 [n_new][n_q_heads][head_dim]
  *   k_new, v_new : device bf16 [n_new][n_kv_heads][head_dim]
- *   cu_new       : device int32 [batch + 1], offsets of each sequence's new tokens
- *   max_new      : host bound on cu_new[b+1] - cu_new[b] (sizes the grid)
+ *   cu_new       : device int32 [batch + 1], offsets of each sequence's new tokens;
+ *                  cu_new[0] = 0 <= cu_new[1] <= ... <= cu_new[batch] = n_new
+ *   max_new      : host bound, >= cu_new[b+1] - cu_new[b] for every b and <= n_new
+ *                  (sizes the grid; tokens past it are not computed)
+ *   head_map     : as for decode; at most 32 query heads per KV head
  *   out          : device fp32 [n_new][n_q_heads][head_dim]
- * Requires both stores in the same format, ISO3 or INT8_G64. */
+ *   workspace    : unused (may be NULL); kvq_extend_workspace_bytes returns 0
+ * Requires ISO3 K and V stores and head_dim 128.  Prefix attention runs in the
+ * quaternion-rotated basis (the query rotated once, the accumulator rotated back once);
+ * the cells of a chunk's pages must not be written by pack_after of another sequence
+ * in the same call. */
 kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages,
                            const void* q, const void* k_new, const void* v_new,
                            const int32_t* cu_new, int32_t n_new, int32_t max_new,
@@ -204,7 +212,7 @@ kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages,
                            float sm_scale, float* out, int32_t pack_after,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes kvq_extend_attn needs (0 on invalid arguments). */
+/* Workspace bytes kvq_extend_attn needs: 0 (kept for a stable signature). */
 size_t kvq_extend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages,
                                   int32_t n_new, int32_t max_new, int32_t n_q_heads);
 

@@ -29,16 +29,11 @@
 //     unnormalised partial.  A second kernel merges the splits with a log-sum-exp combine,
 //     normalises, applies H to k8v4 outputs and writes fp32 rows.
 #include "kvq_internal.h"
+#include "device_util.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
 // Launch shapes: waves per workgroup, pages per wave per split (a split is NW * PPW pages), pages
 // each wave keeps in flight ahead of the one it processes, and waves per SIMD the registers allow.
 struct Shape { int nw, ppw, pd, occ; };
@@ -57,9 +52,6 @@ int shape_index() {
   return idx;
 }
 
-__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-__device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-__device__ __forceinline__ float h2f(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
 
 // 8 int8 codes (two dwords, code e in byte e) -> 8 exact fp16 values.
 __device__ __forceinline__ f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
@@ -105,35 +97,6 @@ __device__ __forceinline__ void split_bf16(const float x[4], s16x4& hi, s16x4& l
   const uint32_t l1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[2]) |
                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[3]) << 16);
   lo = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
-}
-
-// Values of lanes l ^ 16 and l ^ 32 through the gfx950 VALU lane swaps (no LDS round trip).
-__device__ __forceinline__ float partner16(float x, int lane) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float((lane & 16) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float partner32(float x, int lane) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float((lane & 32) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float max_over_row_lanes(float x) {     // max over lanes l, l^16, l^32, l^48
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_over_row_lanes(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float s1 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s1), __float_as_uint(s1), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// The cache is streamed once per step: non-temporal loads keep it from displacing reusable lines.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 stream_load(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 template <int N>

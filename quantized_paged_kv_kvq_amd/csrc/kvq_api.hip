@@ -277,21 +277,96 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const
                     "decode launch");
 }
 
+static kvq_status extend_setup(const kvq_cache* cache, int32_t batch, int32_t n_new, int32_t max_new,
+                               int32_t n_q_heads, const int32_t* head_map, ExtendArgs* a, int* tiles) {
+  kvq_status st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if ((st = check_store_fmt(cache->k.fmt, cache->head_dim, false)) != KVQ_OK) return st;
+  if ((st = check_store_fmt(cache->v.fmt, cache->head_dim, true)) != KVQ_OK) return st;
+  if (cache->k.fmt != KVQ_FMT_ISO3 || cache->v.fmt != KVQ_FMT_ISO3)
+    return fail(KVQ_ERR_UNSUPPORTED, "extend attention needs ISO3 K and V stores (got formats %d / %d)",
+                cache->k.fmt, cache->v.fmt);
+  if (cache->head_dim != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "extend attention supports head_dim 128 (got %d)", cache->head_dim);
+  if (batch < 1 || batch > 65535) return fail(KVQ_ERR_SHAPE, "batch %d out of range", batch);
+  if (n_new < 0) return fail(KVQ_ERR_SHAPE, "n_new must be >= 0 (got %d)", n_new);
+  if (max_new < 0 || max_new > n_new)
+    return fail(KVQ_ERR_SHAPE, "max_new %d outside [0, n_new = %d]", max_new, n_new);
+  int max_g = 0;
+  if ((st = build_head_lists(n_q_heads, cache->n_kv_heads, head_map, a->head_off, a->head_list, &max_g)) != KVQ_OK)
+    return st;
+  if (max_g > 32)
+    return fail(KVQ_ERR_UNSUPPORTED, "extend supports up to 32 query heads per KV head (got %d)", max_g);
+  int g_pad = 1;
+  while (g_pad < max_g) g_pad <<= 1;
+  a->g_pad = g_pad;
+  const int per_block = extend_tokens_per_block(g_pad);
+  *tiles = (max_new + per_block - 1) / per_block;
+  if ((long)*tiles * cache->n_kv_heads > 0x7fffffffL) return fail(KVQ_ERR_SHAPE, "n_new %d too large", n_new);
+  if ((long)n_new * (n_q_heads > cache->n_kv_heads ? n_q_heads : cache->n_kv_heads) * cache->head_dim > 0x7fffffffL)
+    return fail(KVQ_ERR_SHAPE, "n_new %d too large", n_new);
+  return KVQ_OK;
+}
+
 size_t kvq_extend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages, int32_t n_new,
                                   int32_t max_new, int32_t n_q_heads) {
   (void)cache; (void)batch; (void)max_pages; (void)n_new; (void)max_new; (void)n_q_heads;
-  return 0;
+  return 0;   // extend keeps everything in registers and LDS
 }
 
 kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, const void* k_new,
                            const void* v_new, const int32_t* cu_new, int32_t n_new, int32_t max_new,
                            int32_t n_q_heads, const int32_t* head_map, float sm_scale, float* out,
                            int32_t pack_after, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)pages; (void)q; (void)k_new; (void)v_new; (void)cu_new; (void)n_new; (void)max_new; (void)n_q_heads;
-  (void)head_map; (void)sm_scale; (void)out; (void)pack_after; (void)workspace; (void)workspace_bytes; (void)stream;
+  (void)workspace; (void)workspace_bytes;
   kvq_status st;
-  if ((st = check_cache(cache)) != KVQ_OK) return st;
-  return fail(KVQ_ERR_UNSUPPORTED, "extend attention is not built yet");
+  if ((st = check_pages(pages)) != KVQ_OK) return st;
+  ExtendArgs a;
+  int tiles = 0;
+  if ((st = extend_setup(cache, pages->batch, n_new, max_new, n_q_heads, head_map, &a, &tiles)) != KVQ_OK)
+    return st;
+  if ((st = check_store(cache, cache->k, false)) != KVQ_OK) return st;
+  if ((st = check_store(cache, cache->v, true)) != KVQ_OK) return st;
+  if (!(sm_scale == sm_scale)) return fail(KVQ_ERR_SHAPE, "sm_scale is NaN");
+  if (n_new == 0) return KVQ_OK;
+  if (!q || !k_new || !v_new || !cu_new || !out) return fail(KVQ_ERR_NULL, "q, k_new, v_new, cu_new or out is NULL");
+  if (((uintptr_t)q & 15) || ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15) || ((uintptr_t)out & 15))
+    return fail(KVQ_ERR_SHAPE, "q, k_new, v_new and out must be 16-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  a.k_codes = static_cast<const uint8_t*>(cache->k.codes);
+  a.k_norms = static_cast<const uint16_t*>(cache->k.scales);
+  a.v_codes = static_cast<const uint8_t*>(cache->v.codes);
+  a.v_norms = static_cast<const uint16_t*>(cache->v.scales);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.cu_new = cu_new;
+  a.prefix_lens = pages->seq_lens;
+  a.bt = pages->block_table;
+  a.out = out;
+  a.hkv = cache->n_kv_heads;
+  a.num_pages = cache->num_pages;
+  a.max_pages = pages->max_pages;
+  a.batch = pages->batch;
+  a.n_new = n_new;
+  a.n_q_heads = n_q_heads;
+  for (int i = 0; i < 4; ++i) a.quat[i] = cache->iso_quat[i];
+  a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  a.q_scale = a.scale_log2 / extend_level_scale();
+  a.g_uniform = n_q_heads % cache->n_kv_heads == 0 ? n_q_heads / cache->n_kv_heads : 0;
+  for (int h = 0; h < n_q_heads && a.g_uniform; ++h)
+    if (a.head_list[h] != h || (h % a.g_uniform == 0 && a.head_off[h / a.g_uniform] != h)) a.g_uniform = 0;
+  if (tiles > 0 && (st = hip_status(launch_extend(a, tiles, s), "extend launch")) != KVQ_OK) return st;
+  if (!pack_after) return KVQ_OK;
+  // deferred packing: token i of sequence b goes to cell seq_lens[b] + (i - cu_new[b])
+  AppendArgs ap{nullptr, nullptr, pages->block_table, n_new, pages->batch, pages->max_pages, cache->num_pages,
+                cache->n_kv_heads, cu_new, pages->seq_lens};
+  return hip_status(launch_append_kv(cache->k.fmt, static_cast<const uint16_t*>(k_new),
+                                     static_cast<uint8_t*>(cache->k.codes), static_cast<uint16_t*>(cache->k.scales),
+                                     cache->v.fmt, static_cast<const uint16_t*>(v_new),
+                                     static_cast<uint8_t*>(cache->v.codes), static_cast<uint16_t*>(cache->v.scales),
+                                     cache->head_dim, cache->iso_quat, ap, s),
+                    "extend pack launch");
 }
 
 }  // extern "C"

@@ -94,6 +94,40 @@ DecodePlan plan_decode(int head_dim, int hkv, int batch, int max_pages, int max_
 hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const DecodeArgs& a,
                          hipStream_t s);
 
+// Extend over an ISO3 prefix: one row per (new token, query head); rows of KV head j use the query
+// heads head_list[head_off[j] .. head_off[j+1]).
+struct ExtendArgs {
+  const uint8_t* k_codes;
+  const uint16_t* k_norms;
+  const uint8_t* v_codes;
+  const uint16_t* v_norms;
+  const uint16_t* q;          // bf16 [n_new][n_q_heads][head_dim]
+  const uint16_t* k_new;      // bf16 [n_new][hkv][head_dim]
+  const uint16_t* v_new;
+  const int32_t* cu_new;      // [batch + 1]
+  const int32_t* prefix_lens; // [batch]
+  const int32_t* bt;          // [batch][max_pages]
+  float* out;                 // fp32 [n_new][n_q_heads][head_dim]
+  int hkv;
+  int num_pages;
+  int max_pages;
+  int batch;
+  int n_new;
+  int n_q_heads;
+  int g_pad;                  // power of two >= the largest group; a wave holds 32 / g_pad tokens
+  float quat[4];
+  float q_scale;              // sm_scale * log2(e) / S (rotated prefix phase)
+  float scale_log2;           // sm_scale * log2(e)
+  int g_uniform;
+  int16_t head_off[KVQ_MAX_Q_HEADS + 1];
+  int16_t head_list[KVQ_MAX_Q_HEADS];
+};
+
+// Query tokens of one workgroup for a group width (power of two <= 32).
+inline int extend_tokens_per_block(int g_pad) { return 4 * (32 / g_pad); }
+float extend_level_scale();
+hipError_t launch_extend(const ExtendArgs& a, int tiles_per_seq, hipStream_t s);
+
 int device_cu_count();
 int decode_max_splits();
 

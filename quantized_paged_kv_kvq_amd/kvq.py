@@ -229,14 +229,15 @@ def kvq_extend_attn(cache: PagedKVCache, pages: Pages, q: torch.Tensor, k_new: t
         out = torch.empty((N, Hq, D), dtype=torch.float32, device=q.device)
     if workspace is None:
         nbytes = kvq_extend_workspace_bytes(cache, pages.batch, pages.max_pages, N, max_new, Hq)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     keep, hm = _head_map_arg(head_map)
     _check(lib().kvq_extend_attn(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
                                  _ptr(q, torch.bfloat16, "q"), _ptr(k_new, torch.bfloat16, "k_new"),
                                  _ptr(v_new, torch.bfloat16, "v_new"), _ptr(cu_new, torch.int32, "cu_new"), N,
                                  int(max_new), Hq, hm, float(sm_scale), _ptr(out, torch.float32, "out"),
-                                 1 if pack_after else 0, _ptr(workspace, None, "workspace"),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+                                 1 if pack_after else 0, _ptr(workspace, None, "workspace"), ws_bytes,
+                                 _stream(stream)))
     del keep
     return out
 

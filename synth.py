@@ -92,9 +92,15 @@ class Workload:
     def max_pages(self) -> int:
         return int(self.block_table.shape[1])
 
+    def new_lens(self) -> np.ndarray:
+        """Tokens the step itself writes, per sequence."""
+        if "new" in self.meta:
+            return np.asarray(self.meta["new"], np.int32)
+        return np.full(self.batch, self.n_step, np.int32)
+
     def prefix_lens(self) -> np.ndarray:
         """Cells already in the cache before the step writes."""
-        return (self.seq_lens - self.n_step).astype(np.int32)
+        return (self.seq_lens - self.new_lens()).astype(np.int32)
 
 
 def _page_table(rng, lens, page_size, identity):
@@ -210,3 +216,22 @@ def ragged_decode(fmt_k: str, fmt_v: str, lens, seed: int = 11, n_q: int = 1, n_
     return Workload("ragged_decode", fmt_k, fmt_v, len(lens), n_q_heads, n_kv_heads, head_dim,
                     PAGE_SIZE, lens, table, npages, ks, vs, q, n_q=n_q, n_step=n_step, q_lens=q_lens,
                     quat=quat)
+
+
+def ragged_extend(prefix_lens, new_lens, seed: int = 21, n_q_heads: int = 8, n_kv_heads: int = 2,
+                  head_dim: int = 128, identity: bool = False) -> Workload:
+    """Prefill chunks over ISO3 prefixes of any lengths, for parity tests: sequence b holds
+    ``prefix_lens[b]`` packed cells and ``new_lens[b]`` new bf16 tokens; the q rows of all
+    sequences' new tokens are concatenated in sequence order."""
+    rng = np.random.default_rng(seed)
+    pre = np.asarray(prefix_lens, np.int32)
+    new = np.asarray(new_lens, np.int32)
+    lens = (pre + new).astype(np.int32)
+    table, npages = _page_table(rng, lens, PAGE_SIZE, identity=identity)
+    ks = [normal_bf16(rng, (int(L), n_kv_heads, head_dim)) for L in lens]
+    vs = [normal_bf16(rng, (int(L), n_kv_heads, head_dim)) for L in lens]
+    q = normal_bf16(rng, (int(new.sum()), n_q_heads, head_dim))
+    quat = random_quaternion(seed + 1000)
+    return Workload("ragged_extend", "iso3", "iso3", len(lens), n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
+                    lens, table, npages, ks, vs, q, n_q=int(new.max()) if len(new) else 0, n_step=0, quat=quat,
+                    kind="extend", meta={"new": new})

@@ -118,3 +118,34 @@ def test_append_and_gather_validation_errors():
     assert G(c, p, 0, 0, 0, 1, out=None) == 1
     assert G(c, p, 0, 0, 0, 0) == 0
     assert L.kvq_status_str(3) == b"unsupported format or geometry"
+
+
+def extend(c, p, n_new=64, max_new=64, hq=16, head_map=None, q=FAKE, kn=FAKE, vn=FAKE, cu=FAKE, out=FAKE,
+           scale=0.0625):
+    L = kvq.lib()
+    hm = None
+    if head_map is not None:
+        arr = (ctypes.c_int32 * len(head_map))(*head_map)
+        hm = ctypes.cast(arr, ctypes.c_void_p)
+    return L.kvq_extend_attn(ctypes.byref(c) if c else None, ctypes.byref(p) if p else None, q, kn, vn, cu, n_new,
+                             max_new, hq, hm, scale, out, 1, None, 0, None)
+
+
+def test_extend_validation_errors():
+    L = kvq.lib()
+    iso = lambda **kw: make_cache(fk=3, fv=3, D=128, **kw)
+    assert extend(None, make_pages()) == 1
+    assert extend(iso(), None) == 1
+    assert extend(make_cache(), make_pages()) == 3                      # int8 stores: no extend path
+    assert extend(make_cache(fk=3, fv=3, D=256), make_pages()) == 3     # head_dim 128 only
+    assert extend(iso(), make_pages(), max_new=65) == 2                 # max_new > n_new
+    assert extend(iso(), make_pages(), n_new=-1, max_new=0) == 2
+    assert extend(iso(), make_pages(), hq=15) == 2                      # Hq % Hkv
+    assert extend(iso(hkv=1), make_pages(), hq=33) == 3                 # 33 query heads on one KV head
+    assert extend(iso(), make_pages(), q=None) == 1
+    assert extend(iso(), make_pages(), cu=None) == 1
+    assert extend(iso(), make_pages(), kn=FAKE + 4) == 2                # misaligned
+    assert extend(iso(), make_pages(), scale=float("nan")) == 2
+    assert extend(iso(), make_pages(), n_new=0, max_new=0, q=None) == 0  # empty chunk: no-op
+    c = iso()
+    assert L.kvq_extend_workspace_bytes(ctypes.byref(c), 1, 64, 64, 64, 16) == 0
