@@ -30,8 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0        # dense fp16 / bf16 matrix peak of MI355X
 MALL_BYTES = 256 << 20
 METRIC = "decode-attn µs/step + achieved HBM GB/s vs peak, int8 KV @128K ctx"
+EXTEND_METRIC = "extend-attn µs/step + achieved MFMA TFLOP/s vs dense fp16 peak, ISO3 KV, 30k prefix + 2048 new"
 
 
 def make_workload(name: str):
@@ -46,6 +48,8 @@ def make_workload(name: str):
         return synth.batched_int8_decode()
     if name == "tiny_int8_decode":
         return synth.tiny_int8_decode()
+    if name == "iso3_extend":
+        return synth.iso3_extend()
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -96,6 +100,131 @@ def cpu_baseline(w, budget_s: float = 15.0):
                       f"step's tokens + fp64 attention over all {int(np.sum(w.seq_lens))} cells"}
 
 
+def extend_flops(w):
+    """Algorithmic flops of one extend launch: QK and PV over every (row, visible key) pair."""
+    pre, new = w.prefix_lens(), w.new_lens()
+    keys = sum(int(new[b]) * int(pre[b]) + int(new[b]) * (int(new[b]) + 1) // 2 for b in range(w.batch))
+    return 4.0 * keys * w.n_q_heads * w.head_dim
+
+
+def extend_cpu_baseline(w, budget_s: float = 15.0):
+    """The oracle's extend on a sample of query rows, scaled to the whole chunk, plus its encode of
+    the chunk's tokens (deferred packing); the oracle's prefix is encoded first, outside the timing."""
+    from oracle import attention as oatt
+    from oracle import paged as opaged
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    pre, new = w.prefix_lens(), w.new_lens()
+    P, N = int(pre[0]), int(new[0])
+    sk = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sv = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    opaged.append(sk, w.block_table, np.zeros(P, int), np.arange(P), w.k[0][:P], w.page_size, quat=w.quat)
+    opaged.append(sv, w.block_table, np.zeros(P, int), np.arange(P), w.v[0][:P], w.page_size, quat=w.quat)
+    cu = np.array([0, N], np.int32)
+    rows = np.linspace(0, N - 1, 16).astype(np.int64)
+    t0 = time.perf_counter()
+    n_calls = 0
+    while True:
+        oatt.extend(sk, sv, w.block_table, pre, w.q, w.k[0][P:], w.v[0][P:], cu, w.page_size, w.sm_scale,
+                    quat=w.quat, rows=rows)
+        n_calls += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    t_rows = (time.perf_counter() - t0) / n_calls
+    t1 = time.perf_counter()
+    sk2 = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    opaged.append(sk2, w.block_table, np.zeros(N, int), np.arange(P, P + N), w.k[0][P:], w.page_size, quat=w.quat)
+    opaged.append(sk2, w.block_table, np.zeros(N, int), np.arange(P, P + N), w.v[0][P:], w.page_size, quat=w.quat)
+    t_pack = time.perf_counter() - t1
+    per_step = t_rows * N / len(rows) + t_pack
+    return {"value": per_step * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 attention of {len(rows)} of {N} query tokens (all {w.n_q_heads} heads, "
+                      f"{n_calls} runs) scaled by {N}/{len(rows)}, plus the numpy encode of the {N} new tokens"}
+
+
+def bench_extend(args):
+    import torch
+    import quantized_paged_kv_kvq_amd as kvq
+    from kvq_testutil import dev_bf16, dev_i32
+
+    w = make_workload(args.workload)
+    pre, new = w.prefix_lens(), w.new_lens()
+    P, N = int(pre[0]), int(new[0])
+    cache = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, "iso3", "iso3", quat=w.quat)
+    pages = kvq.Pages(dev_i32(w.block_table), dev_i32(pre))
+    kvq.kvq_append(cache, pages, dev_bf16(w.k[0][:P]), dev_bf16(w.v[0][:P]), dev_i32(np.zeros(P, np.int32)),
+                   dev_i32(np.arange(P, dtype=np.int32)))
+    q, kn, vn = dev_bf16(w.q), dev_bf16(w.k[0][P:]), dev_bf16(w.v[0][P:])
+    cu = dev_i32(np.array([0, N], np.int32))
+    out = torch.empty((N, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(pack, stream):
+        kvq.kvq_extend_attn(cache, pages, q, kn, vn, cu, N, sm_scale=w.sm_scale, out=out, pack_after=pack,
+                            stream=stream)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step(True, stream)
+    torch.cuda.synchronize()
+    mode = "eager"
+    g_step = g_att = None
+    if not args.no_graph:
+        try:
+            g_step, g_att = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_step):
+                step(True, torch.cuda.current_stream())
+            with torch.cuda.graph(g_att):
+                step(False, torch.cuda.current_stream())
+            g_step.replay(); g_att.replay()
+            torch.cuda.synchronize()
+            mode = "hip-graph"
+        except Exception as e:  # noqa: BLE001
+            print(f"[bench] graph capture unavailable ({e}); timing eager launches", file=sys.stderr, flush=True)
+            g_step = g_att = None
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g_step.replay() if g_step else step(True, stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        g_att.replay() if g_att else step(False, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    att_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    flops = extend_flops(w)
+    achieved = flops / (att_us * 1e-6) / 1e12
+    print(f"[bench] {mode}: extend attention {att_us:.1f} us ({achieved:.1f} TFLOP/s), step {ms_per_step * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = extend_cpu_baseline(w)
+    line = {
+        "metric": EXTEND_METRIC, "value": round(ms_per_step * 1e3, 3), "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16/bf16 mfma, iso3 cells",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "prefix": P, "n_new": N, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+                   "k_format": "iso3", "v_format": "iso3",
+                   "step": "extend attention over the packed prefix + causal new tokens, then pack the new tokens",
+                   "launch": mode},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_extend_iso3", "launch_us": round(att_us, 3), "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +247,8 @@ def main():
 
     torch.cuda.set_device(0)
     kvq.lib()
+    if args.workload == "iso3_extend":
+        return bench_extend(args)
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
     w = make_workload(args.workload)
     cb_k, ns_k = kvq.cell_bytes(w.fmt_k, w.head_dim)

@@ -200,7 +200,9 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
  *                  (sizes the grid; tokens past it are not computed)
  *   head_map     : as for decode; at most 32 query heads per KV head
  *   out          : device fp32 [n_new][n_q_heads][head_dim]
- *   workspace    : unused (may be NULL); kvq_extend_workspace_bytes returns 0
+ *   workspace    : device, >= kvq_extend_workspace_bytes(...) bytes, 256-byte aligned:
+ *                  every 64-cell tile of every prefix and chunk is staged there once as
+ *                  the attention kernel's tile image (about 33 KB per tile and KV head)
  * Requires ISO3 K and V stores and head_dim 128.  Prefix attention runs in the
  * quaternion-rotated basis (the query rotated once, the accumulator rotated back once);
  * the cells of a chunk's pages must not be written by pack_after of another sequence
@@ -212,7 +214,8 @@ kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages,
                            float sm_scale, float* out, int32_t pack_after,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes kvq_extend_attn needs: 0 (kept for a stable signature). */
+/* Workspace bytes kvq_extend_attn needs for this geometry (0 on invalid arguments):
+ * batch * n_kv_heads * (ceil(max_pages * page_size / 64) + ceil(max_new / 64)) tiles. */
 size_t kvq_extend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages,
                                   int32_t n_new, int32_t max_new, int32_t n_q_heads);
 

@@ -1,12 +1,22 @@
 // Extend (prefill chunk) attention over an ISO3-packed prefix plus the chunk's own bf16 tokens.
 //
 // FreeToken PR #398, "What": a prefill chunk attends the cached prefix, which is held packed,
-// and its own new tokens, which are packed only after the chunk's attention (deferred packing).
-// Token i of a chunk at position P + i sees the P prefix cells and new tokens 0..i.
+// and its own new tokens, which are packed only after the chunk's attention (deferred packing);
+// prompt-chunk attention dequantises the packed prefix once into a scratch that a tiled kernel
+// then reads.  Token i of a chunk at position P + i sees the P prefix cells and new tokens 0..i.
 //
-// Work decomposition: one workgroup = 4 waves = one (sequence, KV head, 4 * T query tokens) tile;
-// a wave owns 32 query rows (T tokens x G_pad query heads of the KV head) as two 16-column MFMA
-// tiles.  Keys stream through LDS 64 at a time, double-buffered, one barrier per tile.
+// Two kernels:
+//   * k_extend_stage writes, for every 64-key tile of every (sequence, KV head), the image of the
+//     tile as the attention kernel's LDS holds it: K as [key][head_dim] and V as [head_dim][key]
+//     (transposed for the PV contraction), both with rows padded so that the MFMA operand reads
+//     are free of bank conflicts, plus the per-key norms.  Prefix tiles come from the
+//     ISO3 cells (the dequantisation runs once per cell, not once per query tile); chunk tiles from
+//     the bf16 tokens.
+//   * k_extend_attn: one workgroup = 4 waves = one (sequence, KV head, 4 * T query tokens) tile; a
+//     wave owns 32 query rows (T tokens x G_pad query heads), the 32 columns of 32x32x16 MFMA
+//     tiles: lane l holds row l % 32 and, per 32-key block, 16 of its scores.  Tile images stream
+//     into LDS with direct global-to-LDS loads (no registers), double-buffered, one barrier per
+//     tile; two workgroups share a CU so that one's softmax overlaps the other's MFMAs.
 //
 // Prefix phase (rotated basis).  An ISO3 key is k = n * conj(r) (x) c with c the centroid values of
 // its codes, so <q, k> = n * <r (x) q, c>: the query is rotated once, the codes are used as they
@@ -18,7 +28,7 @@
 // rotated query and the weights p * n / S are split into fp16 hi + lo parts (22 significant bits),
 // so each QK and each PV tile takes two MFMAs.
 //
-// New-token phase (original basis, bf16 MFMA).  q and the new K/V are bf16 and enter the bf16 MFMA
+// Chunk phase (original basis, bf16 MFMA).  q and the new K/V are bf16 and enter the bf16 MFMA
 // exactly; the weights are split into bf16 hi + lo parts (16 significant bits).  Causal mask per
 // row; tiles past a wave's last token are skipped.
 //
@@ -32,17 +42,35 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kWaves = 4;
-constexpr int kKeys = 64;                 // keys per tile
-constexpr int kKStride = kD + 8;          // halves per key row of the K tile (272 B)
-constexpr int kVStride = kKeys + 8;       // halves per head_dim row of the V tile (144 B)
-constexpr int kLutEntries = 4096;         // every 12-bit group of 4 codes
-constexpr float kLevelScale = 1.2495174407958984f;   // S: S * c is within 2^-15.9 of fp16 for all 8 levels
+constexpr int kKeys = 64;                                  // keys per tile
+constexpr int kKRow = kD * 2 + 16;                         // K image row: one key, 256 B + 16 B pad
+constexpr int kVRow = kKeys * 2 + 16;                      // V image row: one head_dim, 128 B + 16 B pad
+constexpr int kImgK = kKeys * kKRow;                       // K image bytes: [key][d] fp16/bf16
+constexpr int kImgV = kD * kVRow;                          // V image bytes: [d][key position]
+constexpr int kNormOff = kImgK + kImgV;                    // fp32 K norms [64], then V norms / S [64]
+static_assert(kNormOff + 2 * kKeys * 4 <= kExtendTileBytes, "tile image layout");
+static_assert(kExtendTileBytes % 4096 == 0, "a tile image is 4 waves x whole kilobytes");
+constexpr float kLevelScale = 1.2495174407958984f;         // S: S * c is within 2^-15.9 of fp16 for all 8 levels
 
 constexpr double kSqrt128 = 11.3137084989847603904135327140;
 __constant__ float kLevels[8] = {
     (float)(-2.1520 / kSqrt128), (float)(-1.3440 / kSqrt128), (float)(-0.7560 / kSqrt128),
     (float)(-0.2451 / kSqrt128), (float)(0.2451 / kSqrt128),  (float)(0.7560 / kSqrt128),
     (float)(1.3440 / kSqrt128),  (float)(2.1520 / kSqrt128)};
+
+// Byte offsets inside a tile image: 16-byte chunk c (head_dim 8c .. 8c+7) of key k, and 16-byte
+// chunk c (key positions 8c .. 8c+7) of head_dim row d.  The 16-byte row padding makes the 16 rows
+// that a 16-lane group of an MFMA operand read touches start in 16 different bank quads.
+__device__ __forceinline__ int k_img_off(int key, int c) { return key * kKRow + (c << 4); }
+__device__ __forceinline__ int v_img_off(int d, int c) { return kImgK + d * kVRow + (c << 4); }
+
+// Position order of a tile's keys in a V row: inside each 16-key group, positions 8h .. 8h+7 hold
+// keys 4h .. 4h+3 and 8+4h .. 8+4h+3, the 8 keys that lane half h of a 32x32 MFMA accumulator holds
+// for one 16-key step, so one 16-byte read gives a PV A-operand lane the keys of its B operand.
+__device__ __forceinline__ int key_at(int pos) {
+  const int p16 = pos & 15, e = p16 & 7;
+  return (pos & ~15) + 8 * (e >> 2) + 4 * (p16 >> 3) + (e & 3);
+}
 
 // r (x) u for a quaternion r = (w, x, y, z) and a group u = (u0, u1, u2, u3).
 __device__ __forceinline__ void qmul(float w, float x, float y, float z, const float u[4], float t[4]) {
@@ -52,145 +80,138 @@ __device__ __forceinline__ void qmul(float w, float x, float y, float z, const f
   t[3] = ((w * u[3] + x * u[2]) - y * u[1]) + z * u[0];
 }
 
-// Position of key k of a tile in the V tile rows: inside each 32-key half, the 4 keys of lane
-// group g from the first 16 and the 4 from the second 16 sit side by side, so that one 16-byte LDS
-// read gives a PV A-operand lane the same 8 keys its B operand holds.
-__device__ __forceinline__ int vpos(int k) {
-  const int k32 = k & 31;
-  return (k & 32) + ((k32 & 15) >> 2) * 8 + (k32 >> 4) * 4 + (k & 3);
+__device__ __forceinline__ uint8_t* prefix_image(const ExtendArgs& a, int b, int kvh, int t) {
+  return a.ws + ((size_t)(b * a.hkv + kvh) * a.pt_max + t) * kExtendTileBytes;
+}
+__device__ __forceinline__ uint8_t* chunk_image(const ExtendArgs& a, int b, int kvh, int t) {
+  return a.ws + (size_t)a.batch * a.hkv * a.pt_max * kExtendTileBytes +
+         ((size_t)(b * a.hkv + kvh) * a.nt_max + t) * kExtendTileBytes;
 }
 
-struct Lds {
-  uint2 lut[kLutEntries];                               // 4 codes -> 4 fp16 values S * c
-  uint16_t k[2][kKeys * kKStride];                      // [key][d]
-  uint16_t v[2][kD * kVStride];                         // [d][vpos(key)]
-  float nk[2][kKeys];                                   // K norms
-  float nv[2][kKeys];                                   // V norms / S
+// ============================== staging ==============================
+struct StageLds {
+  uint32_t raw[2][kKeys * 12 + 4];                          // ISO3 codes of the tile's keys (K, V), 48 B each
+  uint16_t level[8];                                         // S * c as fp16
+  __attribute__((aligned(16))) uint8_t img[kExtendTileBytes];
 };
 
-// ---- tile loaders.  Waves 0-1 handle K (thread: one key, 64 head_dim values), waves 2-3 handle V
-// (thread: two adjacent keys, 32 head_dim values), so every role is wave-uniform.
-struct IsoRegs {
-  uint32_t c[6];     // K: 64 codes of one key; V: 32 codes of each of two keys
-  uint32_t norm;     // K: norm (low half); V: norms of the two keys
-};
-
-__device__ __forceinline__ int iso_page_index(int it, int tid) {
-  const int key = tid < 128 ? (tid >> 1) : 2 * (tid & 31);
-  return (it * kKeys + key) >> 4;
+// 3-bit code of head_dim d of key `key` from the staged 48-byte rows (little-endian bit stream).
+__device__ __forceinline__ uint32_t code_at(const uint32_t* raw, int key, int d) {
+  const int bit = 3 * d, w = key * 12 + (bit >> 5);
+  return __builtin_amdgcn_alignbit(raw[w + 1], raw[w], bit & 31) & 7u;
 }
 
-__device__ __forceinline__ void iso_load(const ExtendArgs& a, int it, int page, int kvh, int tid, IsoRegs& r) {
-  const size_t tile = (size_t)page * a.hkv + kvh;
-  if (tid < 128) {
-    const int key = tid >> 1, half = tid & 1;
-    const int slot = (it * kKeys + key) & 15;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k_codes + (tile * 16 + slot) * 48 + 24 * half);
-#pragma unroll
-    for (int i = 0; i < 6; ++i) r.c[i] = src[i];
-    r.norm = half == 0 ? a.k_norms[tile * 16 + slot] : 0u;
-  } else {
-    const int m = tid & 31, chunk = (tid - 128) >> 5;
-    const int slot = (it * kKeys + 2 * m) & 15;
-    const uint32_t* src0 = reinterpret_cast<const uint32_t*>(a.v_codes + (tile * 16 + slot) * 48 + 12 * chunk);
-    const uint32_t* src1 = src0 + 12;                   // next slot: 48 bytes further
-#pragma unroll
-    for (int i = 0; i < 3; ++i) { r.c[i] = src0[i]; r.c[3 + i] = src1[i]; }
-    r.norm = chunk == 0 ? *reinterpret_cast<const uint32_t*>(a.v_norms + tile * 16 + slot) : 0u;
-  }
-}
+__global__ __launch_bounds__(256) void k_extend_stage(const ExtendArgs a) {
+  __shared__ StageLds s;
+  const int tid = threadIdx.x;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int s0 = clampi(a.cu_new[b], 0, a.n_new);
+  const int n_b = clampi(a.cu_new[b + 1], s0, a.n_new) - s0;
+  const int P = clampi(a.prefix_lens[b], 0, a.max_pages * KVQ_PAGE_SIZE);
 
-// 12-bit group g (0..7) of a 96-bit little-endian code stream held in three words.
-__device__ __forceinline__ uint32_t group12(const uint32_t* w, int g) {
-  const int bit = 12 * g, wi = bit >> 5, sh = bit & 31;
-  const uint64_t two = (uint64_t)w[wi] | ((uint64_t)(wi + 1 < 3 ? w[wi + 1] : 0u) << 32);
-  return (uint32_t)(two >> sh) & 0xfffu;
-}
-
-__device__ __forceinline__ void iso_store(Lds& s, int buf, int tid, const IsoRegs& r) {
-  if (tid < 128) {
-    const int key = tid >> 1, half = tid & 1;
-    uint32_t h[32];                                     // 64 fp16 values, two per word
+  if ((int)blockIdx.x < a.pt_max) {
+    const int t = blockIdx.x;
+    if (t * kKeys >= P) return;
+    const int* bt_row = a.bt + (size_t)b * a.max_pages;
+    for (int i = tid; i < kKeys * 12; i += 256) {
+      const int key = i / 12, w = i % 12;
+      const int pos = min(t * kKeys + key, P - 1);
+      const int page = clampi(bt_row[pos >> 4], 0, a.num_pages - 1);
+      const size_t cell = ((size_t)page * a.hkv + kvh) * KVQ_PAGE_SIZE + (pos & 15);
+      s.raw[0][i] = reinterpret_cast<const uint32_t*>(a.k_codes + cell * 48)[w];
+      s.raw[1][i] = reinterpret_cast<const uint32_t*>(a.v_codes + cell * 48)[w];
+    }
+    if (tid < 8) s.level[tid] = __builtin_bit_cast(uint16_t, (_Float16)(kLevelScale * kLevels[tid]));
+    if (tid < 4) { s.raw[0][kKeys * 12 + tid] = 0u; s.raw[1][kKeys * 12 + tid] = 0u; }
+    if (tid < kKeys) {
+      const int pos = t * kKeys + tid;
+      const bool live = pos < P;
+      const int pc = min(pos, P - 1);
+      const int page = clampi(bt_row[pc >> 4], 0, a.num_pages - 1);
+      const size_t cell = ((size_t)page * a.hkv + kvh) * KVQ_PAGE_SIZE + (pc & 15);
+      float* norms = reinterpret_cast<float*>(s.img + kNormOff);
+      norms[tid] = live ? h2f(a.k_norms[cell]) : 0.0f;
+      norms[kKeys + tid] = live ? h2f(a.v_norms[cell]) * (1.0f / kLevelScale) : 0.0f;
+    }
+    __syncthreads();
+    {   // K image: thread = (key, 32 head_dim values)
+      const int key = tid >> 2, q = tid & 3;
 #pragma unroll
-    for (int part = 0; part < 2; ++part)
+      for (int c = 0; c < 4; ++c) {
+        uint32_t w[4];
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const uint2 e = s.lut[group12(r.c + 3 * part, g)];
-        h[part * 16 + 2 * g] = e.x;
-        h[part * 16 + 2 * g + 1] = e.y;
+        for (int e = 0; e < 4; ++e) {
+          const int d = 32 * q + 8 * c + 2 * e;
+          w[e] = (uint32_t)s.level[code_at(s.raw[0], key, d)] |
+                 ((uint32_t)s.level[code_at(s.raw[0], key, d + 1)] << 16);
+        }
+        *reinterpret_cast<uint4*>(s.img + k_img_off(key, 4 * q + c)) = make_uint4(w[0], w[1], w[2], w[3]);
       }
-    uint4* dst = reinterpret_cast<uint4*>(&s.k[buf][key * kKStride + 64 * half]);
+    }
+    {   // V image: thread = (head_dim row, 32 key positions)
+      const int d = tid >> 1, h = tid & 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
-    if (half == 0) s.nk[buf][key] = h2f((uint16_t)(r.norm & 0xffffu));
+      for (int c = 0; c < 4; ++c) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = 32 * h + 8 * c + 2 * e;
+          w[e] = (uint32_t)s.level[code_at(s.raw[1], key_at(p), d)] |
+                 ((uint32_t)s.level[code_at(s.raw[1], key_at(p + 1), d)] << 16);
+        }
+        *reinterpret_cast<uint4*>(s.img + v_img_off(d, 4 * h + c)) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(prefix_image(a, b, kvh, t));
+    const uint4* src = reinterpret_cast<const uint4*>(s.img);
+    for (int i = tid; i < kExtendTileBytes / 16; i += 256) dst[i] = src[i];
   } else {
-    const int m = tid & 31, chunk = (tid - 128) >> 5;
-    uint32_t h0[16], h1[16];                            // 32 fp16 values of each key
+    const int t = blockIdx.x - a.pt_max;
+    if (t * kKeys >= n_b) return;
+    uint8_t* img = chunk_image(a, b, kvh, t);
+    {   // K image straight from the bf16 rows
+      const int key = tid >> 2, q = tid & 3;
+      const int kk = min(t * kKeys + key, n_b - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(a.k_new + ((size_t)(s0 + kk) * a.hkv + kvh) * kD + 32 * q);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const uint2 e0 = s.lut[group12(r.c, g)];
-      const uint2 e1 = s.lut[group12(r.c + 3, g)];
-      h0[2 * g] = e0.x; h0[2 * g + 1] = e0.y;
-      h1[2 * g] = e1.x; h1[2 * g + 1] = e1.y;
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(img + k_img_off(key, 4 * q + c)) = src[c];
     }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&s.v[buf][(32 * chunk) * kVStride + vpos(2 * m)]);
+    {   // V image: transpose through registers
+      const int d = tid >> 1, h = tid & 1;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;   // high or low halves of both keys
-      dst[d * (kVStride / 2)] = __builtin_amdgcn_perm(h1[d >> 1], h0[d >> 1], sel);
-    }
-    if (chunk == 0) {
-      s.nv[buf][2 * m] = h2f((uint16_t)(r.norm & 0xffffu)) / kLevelScale;
-      s.nv[buf][2 * m + 1] = h2f((uint16_t)(r.norm >> 16)) / kLevelScale;
+      for (int c = 0; c < 4; ++c) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = 32 * h + 8 * c + 2 * e;
+          const int k0 = min(t * kKeys + key_at(p), n_b - 1), k1 = min(t * kKeys + key_at(p + 1), n_b - 1);
+          w[e] = (uint32_t)a.v_new[((size_t)(s0 + k0) * a.hkv + kvh) * kD + d] |
+                 ((uint32_t)a.v_new[((size_t)(s0 + k1) * a.hkv + kvh) * kD + d] << 16);
+        }
+        *reinterpret_cast<uint4*>(img + v_img_off(d, 4 * h + c)) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
   }
 }
 
-// ---- new-token tiles: bf16 K/V of the chunk, same roles and LDS layout.
-struct NewRegs {
-  uint4 c[8];        // K: 64 values of one key; V: 32 values of each of two keys
-};
-
-__device__ __forceinline__ void new_load(const ExtendArgs& a, int s0, int kmax, int nt, int kvh, int tid, NewRegs& r) {
-  if (tid < 128) {
-    const int key = min(nt * kKeys + (tid >> 1), kmax - 1), half = tid & 1;
-    const uint4* src = reinterpret_cast<const uint4*>(a.k_new + ((size_t)(s0 + key) * a.hkv + kvh) * kD + 64 * half);
+// ============================== attention ==============================
+// A tile image into LDS: each wave moves a quarter of it with 16-byte direct loads.
+__device__ __forceinline__ void load_tile(const uint8_t* src, uint8_t* dst, int wv, int lane) {
+  constexpr int kPerWave = kExtendTileBytes / 4 / 1024;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.c[i] = src[i];
-  } else {
-    const int m = tid & 31, chunk = (tid - 128) >> 5;
-    const int k0 = min(nt * kKeys + 2 * m, kmax - 1), k1 = min(nt * kKeys + 2 * m + 1, kmax - 1);
-    const uint4* src0 = reinterpret_cast<const uint4*>(a.v_new + ((size_t)(s0 + k0) * a.hkv + kvh) * kD + 32 * chunk);
-    const uint4* src1 = reinterpret_cast<const uint4*>(a.v_new + ((size_t)(s0 + k1) * a.hkv + kvh) * kD + 32 * chunk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { r.c[i] = src0[i]; r.c[4 + i] = src1[i]; }
+  for (int i = 0; i < kPerWave; ++i) {
+    const int off = (wv * kPerWave + i) * 1024;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off + lane * 16),
+                                     (__attribute__((address_space(3))) void*)(dst + off), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ uint32_t word_of4(const uint4* q, int w) {
-  const uint4 t = q[w >> 2];
-  const int k = w & 3;
-  return k == 0 ? t.x : k == 1 ? t.y : k == 2 ? t.z : t.w;
+__device__ __forceinline__ void wait_tile_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): this wave's direct loads landed
+  __syncthreads();
 }
 
-__device__ __forceinline__ void new_store(Lds& s, int buf, int tid, const NewRegs& r) {
-  if (tid < 128) {
-    const int key = tid >> 1, half = tid & 1;
-    uint4* dst = reinterpret_cast<uint4*>(&s.k[buf][key * kKStride + 64 * half]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = r.c[i];
-  } else {
-    const int m = tid & 31, chunk = (tid - 128) >> 5;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&s.v[buf][(32 * chunk) * kVStride + vpos(2 * m)]);
-#pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-      dst[d * (kVStride / 2)] = __builtin_amdgcn_perm(word_of4(r.c + 4, d >> 1), word_of4(r.c, d >> 1), sel);
-    }
-  }
-}
-
-// ---- hi/lo splits of 8 weights into MFMA B operands
 __device__ __forceinline__ void split_f16x8(const float x[8], f16x8& hi, f16x8& lo) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -216,34 +237,164 @@ __device__ __forceinline__ void split_bf16x8(const float x[8], bf16x8& hi, bf16x
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// Online-softmax update of one 16-column tile from its 16 scores per lane (key kb*16 + 4*g4 + j
-// at s[4*kb + j], -inf where masked); returns the weights in p.
-__device__ __forceinline__ void softmax_step(float (&s)[16], float& m_run, float& l_run, f32x4 (&O)[8]) {
-  float mx = s[0];
+// Online-softmax update of one row from u (32 values per lane: key 16*s + 8*(e/4) + 4*h + e%4 of
+// the tile at u[8*s + e], -inf where masked; the other 32 keys sit in lane l ^ 32) with true scores
+// u * rs (rs > 0).  u becomes the weights.
+__device__ __forceinline__ void softmax_step(float (&u)[32], float rs, float& m_run, float& l_run, f32x16 (&O)[4],
+                                             int lane) {
+  float mx = fmaxf(fmaxf(u[0], u[1]), u[2]);
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = max_over_row_lanes(mx);
+  for (int i = 3; i < 31; i += 2) mx = fmaxf(fmaxf(mx, u[i]), u[i + 1]);
+  mx = fmaxf(mx, u[31]);
+  mx = fmaxf(mx, partner32(mx, lane)) * rs;
   const float m_new = fmaxf(m_run, mx);
   const float m_use = m_new == kNegInf ? 0.0f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
   m_run = m_new;
   float sum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-    sum += s[i];
+  for (int i = 0; i < 32; ++i) {
+    u[i] = __builtin_amdgcn_exp2f(fmaf(u[i], rs, -m_use));
+    sum += u[i];
   }
   l_run = l_run * alpha + sum;
   if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) O[t] *= alpha;
+    for (int t = 0; t < 4; ++t) O[t] *= alpha;
   }
 }
 
-__global__ __launch_bounds__(256, 1) void k_extend_iso3(const ExtendArgs a) {
-  __shared__ __attribute__((aligned(16))) Lds s;
+// Scheduling groups (instruction classes of the AMDGPU scheduler): operand reads for the next MFMA
+// step are issued ahead of the current step's MFMAs so that LDS latency hides behind them.
+constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100;
+
+template <typename V8, int NQ>
+struct TileOps;
+template <int NQ>
+struct TileOps<f16x8, NQ> {
+  static __device__ __forceinline__ f32x16 mma(const f16x8& a, const f16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <int NQ>
+struct TileOps<bf16x8, NQ> {
+  static __device__ __forceinline__ f32x16 mma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// S^T for the tile's 64 keys (two 32-key blocks) against this wave's 32 rows; q is given as NQ
+// parts (hi, lo) whose products accumulate.
+template <typename V8, int NQ>
+__device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, const V8 (&q)[NQ][8], f32x16 (&S)[2]) {
+  using Ops = TileOps<V8, NQ>;
+  S[0] = f32x16{};
+  S[1] = f32x16{};
+  V8 ka[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) ka[0][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, h));
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int cb = ks & 1;
+    if (ks + 1 < 8) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        ka[cb ^ 1][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, 2 * (ks + 1) + h));
+    }
+#pragma unroll
+    for (int part = 0; part < NQ; ++part)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) S[kb] = Ops::mma(ka[cb][kb], q[part][ks], S[kb]);
+    if (ks + 1 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NQ, 0);
+  }
+}
+
+// O^T += V^T P^T for the tile: per 16-key step, the weights' hi and lo parts (built by `part` from
+// u[8*st .. 8*st+7]) against the 4 head_dim blocks of V.
+template <typename V8, typename Split>
+__device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, const float (&u)[32], Split split,
+                                        f32x16 (&O)[4]) {
+  using Ops = TileOps<V8, 1>;
+  V8 va[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) va[0][t] = *reinterpret_cast<const V8*>(buf + v_img_off(32 * t + l32, h));
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int cb = st & 1;
+    if (st + 1 < 4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        va[cb ^ 1][t] = *reinterpret_cast<const V8*>(buf + v_img_off(32 * t + l32, 2 * (st + 1) + h));
+    }
+    V8 ph, pl;
+    split(st, ph, pl);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[t] = Ops::mma(va[cb][t], ph, O[t]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[t] = Ops::mma(va[cb][t], pl, O[t]);
+    if (st + 1 < 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
+  }
+}
+
+// One prefix tile: QK (fp16, q hi + lo), softmax, weights * n / S split hi + lo, PV (fp16).
+template <bool TAIL>
+__device__ __forceinline__ void prefix_tile(const uint8_t* buf, int limit, int l32, int h, int lane,
+                                            const f16x8 (&q)[2][8], float rs, float& m_run, float& l_run,
+                                            f32x16 (&O)[4]) {
+  f32x16 S[2];
+  qk_tile<f16x8, 2>(buf, l32, h, q, S);
+  const float* nk = reinterpret_cast<const float*>(buf + kNormOff);
+  const float* nv = nk + kKeys;
+  float u[32];
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const int key = 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h;   // keys key .. key+3
+    const float4 n4 = *reinterpret_cast<const float4*>(nk + key);
+    const float nn[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u[i + j] = S[i >> 4][(i & 15) + j] * nn[j];
+      if (TAIL) u[i + j] = key + j < limit ? u[i + j] : kNegInf;
+    }
+  }
+  softmax_step(u, rs, m_run, l_run, O, lane);
+  pv_tile<f16x8>(buf, l32, h, u,
+                 [&](int st, f16x8& ph, f16x8& pl) {
+                   float x[8];
+#pragma unroll
+                   for (int e4 = 0; e4 < 2; ++e4) {
+                     const float4 n4 = *reinterpret_cast<const float4*>(nv + 16 * st + 8 * e4 + 4 * h);
+                     x[4 * e4 + 0] = u[8 * st + 4 * e4 + 0] * n4.x;
+                     x[4 * e4 + 1] = u[8 * st + 4 * e4 + 1] * n4.y;
+                     x[4 * e4 + 2] = u[8 * st + 4 * e4 + 2] * n4.z;
+                     x[4 * e4 + 3] = u[8 * st + 4 * e4 + 3] * n4.w;
+                   }
+                   split_f16x8(x, ph, pl);
+                 },
+                 O);
+}
+
+// One chunk tile: QK (bf16, exact), causal mask, softmax, weights split hi + lo, PV (bf16).
+__device__ __forceinline__ void chunk_tile(const uint8_t* buf, int key0, int tok, float rs, int l32, int h, int lane,
+                                           const bf16x8 (&qb)[1][8], float& m_run, float& l_run, f32x16 (&O)[4]) {
+  f32x16 S[2];
+  qk_tile<bf16x8, 1>(buf, l32, h, qb, S);
+  float u[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int key = key0 + 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h + (i & 3);
+    u[i] = key <= tok ? S[i >> 4][i & 15] : kNegInf;
+  }
+  softmax_step(u, rs, m_run, l_run, O, lane);
+  pv_tile<bf16x8>(buf, l32, h, u, [&](int st, bf16x8& ph, bf16x8& pl) { split_bf16x8(u + 8 * st, ph, pl); }, O);
+}
+
+__global__ __launch_bounds__(256, 2) void k_extend_attn(const ExtendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kExtendTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, g4 = lane >> 4;
+  const int l32 = lane & 31, h = lane >> 5;
   const int kvh = blockIdx.x % a.hkv, tile = blockIdx.x / a.hkv, b = blockIdx.y;
 
   const int s0 = clampi(a.cu_new[b], 0, a.n_new);
@@ -251,60 +402,37 @@ __global__ __launch_bounds__(256, 1) void k_extend_iso3(const ExtendArgs a) {
   const int tw = 32 / a.g_pad;                              // tokens per wave
   const int tok0 = tile * kWaves * tw;                      // first token of the workgroup
   if (tok0 >= n_b) return;
-  const int cap = a.max_pages * KVQ_PAGE_SIZE;
-  const int P = clampi(a.prefix_lens[b], 0, cap);
-  const int* bt_row = a.bt + (size_t)b * a.max_pages;
+  const int P = clampi(a.prefix_lens[b], 0, a.max_pages * KVQ_PAGE_SIZE);
 
   int G, h0;
   if (a.g_uniform > 0) { G = a.g_uniform; h0 = kvh * G; }
   else { h0 = a.head_off[kvh]; G = a.head_off[kvh + 1] - h0; }
 
-  // ---- rows: row 16*rb + c16 of this wave = (token tw*wv + r / g_pad, head slot r % g_pad)
-  int tok[2], qrow[2];
-  bool valid[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = 16 * rb + c16;
-    tok[rb] = tok0 + wv * tw + r / a.g_pad;
-    const int hs = r % a.g_pad;
-    valid[rb] = tok[rb] < n_b && hs < G;
-    const int hq = valid[rb] ? (a.g_uniform > 0 ? h0 + hs : a.head_list[h0 + hs]) : 0;
-    qrow[rb] = valid[rb] ? (s0 + tok[rb]) * a.n_q_heads + hq : 0;
-  }
+  // ---- this lane's row: (token tw*wv + l32 / g_pad, head slot l32 % g_pad)
+  const int tok = tok0 + wv * tw + l32 / a.g_pad;
+  const int hs = l32 % a.g_pad;
+  const bool valid = tok < n_b && hs < G;
+  const int qrow = valid ? (s0 + tok) * a.n_q_heads + (a.g_uniform > 0 ? h0 + hs : a.head_list[h0 + hs]) : 0;
+  const uint16_t* qp = a.q + (size_t)qrow * kD + 8 * h;     // head_dim 16*ks + 8*h .. +7 for ks = 0..7
 
-  f32x4 O[2][8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) O[0][t] = O[1][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.0f, 0.0f};
+  f32x16 O[4] = {};
+  float m_run = kNegInf, l_run = 0.0f;
 
   // ================= prefix phase (rotated basis, fp16 MFMA) =================
   const int n_pt = (P + kKeys - 1) / kKeys;
   if (n_pt > 0) {
+    load_tile(prefix_image(a, b, kvh, 0), lds[0], wv, lane);
     const float rw = a.quat[0], rx = a.quat[1], ry = a.quat[2], rz = a.quat[3];
-    // LUT of 4-code groups: S * c rounded to fp16
-    for (int e = tid; e < kLutEntries; e += 256) {
-      uint32_t h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        h[i] = __builtin_bit_cast(uint16_t, (_Float16)(kLevelScale * kLevels[(e >> (3 * i)) & 7]));
-      s.lut[e] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    }
-    IsoRegs regs;
-    int pg_next = clampi(bt_row[min(iso_page_index(0, tid), a.max_pages - 1)], 0, a.num_pages - 1);
-    iso_load(a, 0, pg_next, kvh, tid, regs);
-    if (n_pt > 1) pg_next = clampi(bt_row[min(iso_page_index(1, tid), a.max_pages - 1)], 0, a.num_pages - 1);
-
-    // rotated, scaled query as fp16 hi + lo: lane holds head_dim 32*ks + 8*g4 .. +7 of its rows
-    f16x8 qh[2][4], ql[2][4];
-    float rowscale[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float v[4][8];
+    // rotated, scaled query as fp16 hi + lo
+    f16x8 qs[2][8];                                         // [hi, lo][ks]
+    float rs;
+    {
+      float v[8][8];
       float mx = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        uint4 raw = *reinterpret_cast<const uint4*>(a.q + (size_t)qrow[rb] * kD + 32 * ks + 8 * g4);
-        if (!valid[rb]) raw = make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+        if (!valid) raw = make_uint4(0, 0, 0, 0);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int grp = 0; grp < 2; ++grp) {
@@ -319,194 +447,82 @@ __global__ __launch_bounds__(256, 1) void k_extend_iso3(const ExtendArgs a) {
           }
         }
       }
-      mx = max_over_row_lanes(mx);
+      mx = fmaxf(mx, partner32(mx, lane));
       int ex = 0;
       if (mx > 0.0f) { frexpf(mx, &ex); ex = 14 - ex; }      // max * 2^ex in [2^13, 2^14)
-      rowscale[rb] = ldexpf(1.0f, -ex);
+      rs = ldexpf(1.0f, -ex);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 8; ++ks) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = ldexpf(v[ks][e], ex);
-        split_f16x8(x, qh[rb][ks], ql[rb][ks]);
+        split_f16x8(x, qs[0][ks], qs[1][ks]);
       }
     }
-
-    __syncthreads();                                        // LUT ready
-    iso_store(s, 0, tid, regs);
-    __syncthreads();
+    wait_tile_and_sync();
 
     for (int it = 0; it < n_pt; ++it) {
-      const int buf = it & 1;
-      const bool more = it + 1 < n_pt;
-      if (more) {
-        iso_load(a, it + 1, pg_next, kvh, tid, regs);
-        if (it + 2 < n_pt)
-          pg_next = clampi(bt_row[min(iso_page_index(it + 2, tid), a.max_pages - 1)], 0, a.num_pages - 1);
-      }
-      const int limit = P - it * kKeys;                     // keys of this tile inside the prefix
-
-      // QK: S^T[key][row]; A = K tile (16 keys x 32 head_dim), B = q hi, then q lo
-      f32x4 S[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) S[kb][0] = S[kb][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const f16x8 ka = __builtin_bit_cast(
-              f16x8, *reinterpret_cast<const uint4*>(&s.k[buf][(16 * kb + c16) * kKStride + 32 * ks + 8 * g4]));
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            S[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[rb][ks], S[kb][rb], 0, 0, 0);
-            S[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql[rb][ks], S[kb][rb], 0, 0, 0);
-          }
-        }
-      float nk[16], nv[16];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float4 a4 = *reinterpret_cast<const float4*>(&s.nk[buf][16 * kb + 4 * g4]);
-        const float4 b4 = *reinterpret_cast<const float4*>(&s.nv[buf][16 * kb + 4 * g4]);
-        nk[4 * kb] = a4.x; nk[4 * kb + 1] = a4.y; nk[4 * kb + 2] = a4.z; nk[4 * kb + 3] = a4.w;
-        nv[4 * kb] = b4.x; nv[4 * kb + 1] = b4.y; nv[4 * kb + 2] = b4.z; nv[4 * kb + 3] = b4.w;
-      }
-      f16x8 ph[2][2], pl[2][2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 16 * (i >> 2) + 4 * g4 + (i & 3);
-          p[i] = key < limit ? S[i >> 2][rb][i & 3] * nk[i] * rowscale[rb] : kNegInf;
-        }
-        softmax_step(p, m_run[rb], l_run[rb], O[rb]);
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 8 * ks2 + e;                      // key block 2*ks2 + e/4, slot e%4
-            const int key = 16 * (i >> 2) + 4 * g4 + (i & 3);
-            x[e] = key < limit ? p[i] * nv[i] : 0.0f;
-          }
-          split_f16x8(x, ph[rb][ks2], pl[rb][ks2]);
-        }
-      }
-      // PV: O^T[d][row] in the rotated basis; A = V tile (16 head_dim x 32 keys)
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const f16x8 va = __builtin_bit_cast(
-              f16x8, *reinterpret_cast<const uint4*>(&s.v[buf][(16 * t + c16) * kVStride + 32 * ks2 + 8 * g4]));
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            O[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph[rb][ks2], O[rb][t], 0, 0, 0);
-            O[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl[rb][ks2], O[rb][t], 0, 0, 0);
-          }
-        }
-      if (more) iso_store(s, buf ^ 1, tid, regs);
-      __syncthreads();
+      const uint8_t* cur = lds[it & 1];
+      if (it + 1 < n_pt) load_tile(prefix_image(a, b, kvh, it + 1), lds[(it + 1) & 1], wv, lane);
+      const int limit = P - it * kKeys;
+      if (limit >= kKeys) prefix_tile<false>(cur, limit, l32, h, lane, qs, rs, m_run, l_run, O);
+      else prefix_tile<true>(cur, limit, l32, h, lane, qs, rs, m_run, l_run, O);
+      wait_tile_and_sync();
     }
-    // back to the original basis: lane's 4 values of O[rb][t] are head_dim 16t + 4*g4 .. +3, one group
+    // back to the original basis: O[t][4g .. 4g+3] is head_dim 32t + 8g + 4h .. +3, one group
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float u[4] = {O[rb][t][0], O[rb][t][1], O[rb][t][2], O[rb][t][3]};
+      for (int g = 0; g < 4; ++g) {
+        const float u[4] = {O[t][4 * g], O[t][4 * g + 1], O[t][4 * g + 2], O[t][4 * g + 3]};
         float r[4];
         qmul(rw, -rx, -ry, -rz, u, r);
-        O[rb][t] = f32x4{r[0], r[1], r[2], r[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[t][4 * g + e] = r[e];
       }
   }
 
-  // ================= new-token phase (original basis, bf16 MFMA) =================
+  // ================= chunk phase (original basis, bf16 MFMA) =================
   const int kmax = min(n_b, tok0 + kWaves * tw);            // new keys any row of the workgroup sees
   const int n_nt = (kmax + kKeys - 1) / kKeys;
   const int wave_last = tok0 + wv * tw + tw - 1;
-  bf16x8 qb[2][4];
+  load_tile(chunk_image(a, b, kvh, 0), lds[0], wv, lane);
+  bf16x8 qb[1][8];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 raw = *reinterpret_cast<const uint4*>(a.q + (size_t)qrow[rb] * kD + 32 * ks + 8 * g4);
-      if (!valid[rb]) raw = make_uint4(0, 0, 0, 0);
-      qb[rb][ks] = __builtin_bit_cast(bf16x8, raw);
-    }
-  NewRegs nr;
-  new_load(a, s0, kmax, 0, kvh, tid, nr);
-  new_store(s, 0, tid, nr);
-  __syncthreads();
+  for (int ks = 0; ks < 8; ++ks) {
+    uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+    if (!valid) raw = make_uint4(0, 0, 0, 0);
+    qb[0][ks] = __builtin_bit_cast(bf16x8, raw);
+  }
+  wait_tile_and_sync();
   for (int nt = 0; nt < n_nt; ++nt) {
-    const int buf = nt & 1;
-    const bool more = nt + 1 < n_nt;
-    if (more) new_load(a, s0, kmax, nt + 1, kvh, tid, nr);
-    if (nt * kKeys <= wave_last) {
-      f32x4 S[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) S[kb][0] = S[kb][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 ka = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const uint4*>(&s.k[buf][(16 * kb + c16) * kKStride + 32 * ks + 8 * g4]));
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            S[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[rb][ks], S[kb][rb], 0, 0, 0);
-        }
-      bf16x8 ph[2][2], pl[2][2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = nt * kKeys + 16 * (i >> 2) + 4 * g4 + (i & 3);
-          p[i] = key <= tok[rb] ? S[i >> 2][rb][i & 3] * a.scale_log2 : kNegInf;
-        }
-        softmax_step(p, m_run[rb], l_run[rb], O[rb]);
-        split_bf16x8(p, ph[rb][0], pl[rb][0]);
-        split_bf16x8(p + 8, ph[rb][1], pl[rb][1]);
-      }
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const uint4*>(&s.v[buf][(16 * t + c16) * kVStride + 32 * ks2 + 8 * g4]));
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            O[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[rb][ks2], O[rb][t], 0, 0, 0);
-            O[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb][ks2], O[rb][t], 0, 0, 0);
-          }
-        }
-    }
-    if (more) new_store(s, buf ^ 1, tid, nr);
-    __syncthreads();
+    const uint8_t* cur = lds[nt & 1];
+    if (nt + 1 < n_nt) load_tile(chunk_image(a, b, kvh, nt + 1), lds[(nt + 1) & 1], wv, lane);
+    if (nt * kKeys <= wave_last) chunk_tile(cur, nt * kKeys, tok, a.scale_log2, l32, h, lane, qb, m_run, l_run, O);
+    wait_tile_and_sync();
   }
 
-  // ---- normalise and write
+  // ---- normalise and write: lanes l and l ^ 32 hold the two halves of a row's sum
+  const float l = l_run + partner32(l_run, lane);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (valid) {
+    float* o = a.out + (size_t)qrow * kD + 4 * h;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float l = sum_over_row_lanes(l_run[rb]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (valid[rb]) {
-      float* o = a.out + (size_t)qrow[rb] * kD + 4 * g4;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(o + 16 * t) = O[rb][t] * inv;
-    }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(o + 32 * t + 8 * g) =
+            make_float4(O[t][4 * g] * inv, O[t][4 * g + 1] * inv, O[t][4 * g + 2] * inv, O[t][4 * g + 3] * inv);
   }
 }
 
 }  // namespace
-}  // namespace kvq
-
-namespace kvq {
 
 float extend_level_scale() { return kLevelScale; }
 
 hipError_t launch_extend(const ExtendArgs& a, int tiles_per_seq, hipStream_t s) {
-  k_extend_iso3<<<dim3((unsigned)(a.hkv * tiles_per_seq), (unsigned)a.batch), dim3(256), 0, s>>>(a);
+  k_extend_stage<<<dim3((unsigned)(a.pt_max + a.nt_max), (unsigned)a.hkv, (unsigned)a.batch), dim3(256), 0, s>>>(a);
+  k_extend_attn<<<dim3((unsigned)(a.hkv * tiles_per_seq), (unsigned)a.batch), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -277,8 +277,9 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const
                     "decode launch");
 }
 
-static kvq_status extend_setup(const kvq_cache* cache, int32_t batch, int32_t n_new, int32_t max_new,
-                               int32_t n_q_heads, const int32_t* head_map, ExtendArgs* a, int* tiles) {
+static kvq_status extend_setup(const kvq_cache* cache, int32_t batch, int32_t max_pages, int32_t n_new,
+                               int32_t max_new, int32_t n_q_heads, const int32_t* head_map, ExtendArgs* a,
+                               int* tiles) {
   kvq_status st;
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->k.fmt, cache->head_dim, false)) != KVQ_OK) return st;
@@ -289,6 +290,7 @@ static kvq_status extend_setup(const kvq_cache* cache, int32_t batch, int32_t n_
   if (cache->head_dim != 128)
     return fail(KVQ_ERR_UNSUPPORTED, "extend attention supports head_dim 128 (got %d)", cache->head_dim);
   if (batch < 1 || batch > 65535) return fail(KVQ_ERR_SHAPE, "batch %d out of range", batch);
+  if (max_pages < 1) return fail(KVQ_ERR_SHAPE, "max_pages must be >= 1");
   if (n_new < 0) return fail(KVQ_ERR_SHAPE, "n_new must be >= 0 (got %d)", n_new);
   if (max_new < 0 || max_new > n_new)
     return fail(KVQ_ERR_SHAPE, "max_new %d outside [0, n_new = %d]", max_new, n_new);
@@ -305,25 +307,32 @@ static kvq_status extend_setup(const kvq_cache* cache, int32_t batch, int32_t n_
   if ((long)*tiles * cache->n_kv_heads > 0x7fffffffL) return fail(KVQ_ERR_SHAPE, "n_new %d too large", n_new);
   if ((long)n_new * (n_q_heads > cache->n_kv_heads ? n_q_heads : cache->n_kv_heads) * cache->head_dim > 0x7fffffffL)
     return fail(KVQ_ERR_SHAPE, "n_new %d too large", n_new);
+  a->pt_max = (int)(((long)max_pages * KVQ_PAGE_SIZE + 63) / 64);
+  a->nt_max = (max_new + 63) / 64;
+  if ((long)a->pt_max + a->nt_max > 0x7fffffffL) return fail(KVQ_ERR_SHAPE, "too many tiles");
   return KVQ_OK;
 }
 
 size_t kvq_extend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages, int32_t n_new,
                                   int32_t max_new, int32_t n_q_heads) {
-  (void)cache; (void)batch; (void)max_pages; (void)n_new; (void)max_new; (void)n_q_heads;
-  return 0;   // extend keeps everything in registers and LDS
+  (void)n_q_heads;   // the tile images depend on the KV heads only
+  if (check_cache(cache) != KVQ_OK) return 0;
+  if (cache->k.fmt != KVQ_FMT_ISO3 || cache->v.fmt != KVQ_FMT_ISO3 || cache->head_dim != 128) return 0;
+  if (batch < 1 || batch > 65535 || max_pages < 1 || n_new < 0 || max_new < 0 || max_new > n_new) return 0;
+  const int pt_max = (int)(((long)max_pages * KVQ_PAGE_SIZE + 63) / 64), nt_max = (max_new + 63) / 64;
+  return extend_workspace_bytes(batch, cache->n_kv_heads, pt_max, nt_max);
 }
 
 kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, const void* k_new,
                            const void* v_new, const int32_t* cu_new, int32_t n_new, int32_t max_new,
                            int32_t n_q_heads, const int32_t* head_map, float sm_scale, float* out,
                            int32_t pack_after, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   kvq_status st;
   if ((st = check_pages(pages)) != KVQ_OK) return st;
   ExtendArgs a;
   int tiles = 0;
-  if ((st = extend_setup(cache, pages->batch, n_new, max_new, n_q_heads, head_map, &a, &tiles)) != KVQ_OK)
+  if ((st = extend_setup(cache, pages->batch, pages->max_pages, n_new, max_new, n_q_heads, head_map, &a, &tiles)) !=
+      KVQ_OK)
     return st;
   if ((st = check_store(cache, cache->k, false)) != KVQ_OK) return st;
   if ((st = check_store(cache, cache->v, true)) != KVQ_OK) return st;
@@ -332,6 +341,14 @@ kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages, const
   if (!q || !k_new || !v_new || !cu_new || !out) return fail(KVQ_ERR_NULL, "q, k_new, v_new, cu_new or out is NULL");
   if (((uintptr_t)q & 15) || ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15) || ((uintptr_t)out & 15))
     return fail(KVQ_ERR_SHAPE, "q, k_new, v_new and out must be 16-byte aligned");
+  const size_t need = extend_workspace_bytes(pages->batch, cache->n_kv_heads, a.pt_max, a.nt_max);
+  if (tiles > 0) {
+    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if ((uintptr_t)workspace & 255) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, extend needs %zu", workspace_bytes, need);
+  }
+  a.ws = static_cast<uint8_t*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   a.k_codes = static_cast<const uint8_t*>(cache->k.codes);
   a.k_norms = static_cast<const uint16_t*>(cache->k.scales);

@@ -108,6 +108,9 @@ struct ExtendArgs {
   const int32_t* prefix_lens; // [batch]
   const int32_t* bt;          // [batch][max_pages]
   float* out;                 // fp32 [n_new][n_q_heads][head_dim]
+  uint8_t* ws;                // tile images: [batch][hkv][pt_max] prefix tiles, then [batch][hkv][nt_max] chunk tiles
+  int pt_max;                 // prefix tiles per (sequence, KV head): ceil(max_pages * page_size / 64)
+  int nt_max;                 // chunk tiles per (sequence, KV head): ceil(max_new / 64)
   int hkv;
   int num_pages;
   int max_pages;
@@ -125,6 +128,12 @@ struct ExtendArgs {
 
 // Query tokens of one workgroup for a group width (power of two <= 32).
 inline int extend_tokens_per_block(int g_pad) { return 4 * (32 / g_pad); }
+// One 64-key tile image: K [64][128] + V [128][64] 16-bit values (rows padded by 16 bytes), then
+// 64 + 64 fp32 norms, rounded up to whole kilobytes per wave of a 4-wave workgroup.
+constexpr int kExtendTileBytes = 36864;
+inline size_t extend_workspace_bytes(int batch, int hkv, int pt_max, int nt_max) {
+  return (size_t)batch * hkv * ((size_t)pt_max + nt_max) * kExtendTileBytes;
+}
 float extend_level_scale();
 hipError_t launch_extend(const ExtendArgs& a, int tiles_per_seq, hipStream_t s);
 

@@ -148,4 +148,5 @@ def test_extend_validation_errors():
     assert extend(iso(), make_pages(), scale=float("nan")) == 2
     assert extend(iso(), make_pages(), n_new=0, max_new=0, q=None) == 0  # empty chunk: no-op
     c = iso()
-    assert L.kvq_extend_workspace_bytes(ctypes.byref(c), 1, 64, 64, 64, 16) == 0
+    assert L.kvq_extend_workspace_bytes(ctypes.byref(c), 1, 64, 64, 64, 16) == 2 * (16 + 1) * 36864
+    assert L.kvq_extend_workspace_bytes(ctypes.byref(make_cache()), 1, 64, 64, 64, 16) == 0
