@@ -41,7 +41,7 @@ namespace kvq {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
+constexpr int kWaves = kExtendWaves;                       // attention workgroup: two groups of 4 waves
 constexpr int kKeys = 64;                                  // keys per tile
 constexpr int kKRow = kD * 2 + 16;                         // K image row: one key, 256 B + 16 B pad
 constexpr int kVRow = kKeys * 2 + 16;                      // V image row: one head_dim, 128 B + 16 B pad
@@ -49,7 +49,7 @@ constexpr int kImgK = kKeys * kKRow;                       // K image bytes: [ke
 constexpr int kImgV = kD * kVRow;                          // V image bytes: [d][key position]
 constexpr int kNormOff = kImgK + kImgV;                    // fp32 K norms [64], then V norms / S [64]
 static_assert(kNormOff + 2 * kKeys * 4 <= kExtendTileBytes, "tile image layout");
-static_assert(kExtendTileBytes % 4096 == 0, "a tile image is 4 waves x whole kilobytes");
+static_assert(kExtendTileBytes % 1024 == 0, "a tile image is whole kilobytes");
 constexpr float kLevelScale = 1.2495174407958984f;         // S: S * c is within 2^-15.9 of fp16 for all 8 levels
 
 constexpr double kSqrt128 = 11.3137084989847603904135327140;
@@ -196,22 +196,6 @@ __global__ __launch_bounds__(256) void k_extend_stage(const ExtendArgs a) {
 }
 
 // ============================== attention ==============================
-// A tile image into LDS: each wave moves a quarter of it with 16-byte direct loads.
-__device__ __forceinline__ void load_tile(const uint8_t* src, uint8_t* dst, int wv, int lane) {
-  constexpr int kPerWave = kExtendTileBytes / 4 / 1024;
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int off = (wv * kPerWave + i) * 1024;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off + lane * 16),
-                                     (__attribute__((address_space(3))) void*)(dst + off), 16, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void wait_tile_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): this wave's direct loads landed
-  __syncthreads();
-}
-
 __device__ __forceinline__ void split_f16x8(const float x[8], f16x8& hi, f16x8& lo) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -310,11 +294,10 @@ __device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, cons
   }
 }
 
-// O^T += V^T P^T for the tile: per 16-key step, the weights' hi and lo parts (built by `part` from
-// u[8*st .. 8*st+7]) against the 4 head_dim blocks of V.
-template <typename V8, typename Split>
-__device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, const float (&u)[32], Split split,
-                                        f32x16 (&O)[4]) {
+// O^T += V^T P^T for the tile: per 16-key step st, the weights' hi and lo parts P[st][0..1] (as MFMA
+// B operands) against the 4 head_dim blocks of V.
+template <typename V8>
+__device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, const u32x4 (&P)[4][2], f32x16 (&O)[4]) {
   using Ops = TileOps<V8, 1>;
   V8 va[2][4];
 #pragma unroll
@@ -327,8 +310,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, cons
       for (int t = 0; t < 4; ++t)
         va[cb ^ 1][t] = *reinterpret_cast<const V8*>(buf + v_img_off(32 * t + l32, 2 * (st + 1) + h));
     }
-    V8 ph, pl;
-    split(st, ph, pl);
+    const V8 ph = __builtin_bit_cast(V8, P[st][0]), pl = __builtin_bit_cast(V8, P[st][1]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) O[t] = Ops::mma(va[cb][t], ph, O[t]);
 #pragma unroll
@@ -338,62 +320,167 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, cons
   }
 }
 
-// One prefix tile: QK (fp16, q hi + lo), softmax, weights * n / S split hi + lo, PV (fp16).
-template <bool TAIL>
-__device__ __forceinline__ void prefix_tile(const uint8_t* buf, int limit, int l32, int h, int lane,
-                                            const f16x8 (&q)[2][8], float rs, float& m_run, float& l_run,
-                                            f32x16 (&O)[4]) {
-  f32x16 S[2];
-  qk_tile<f16x8, 2>(buf, l32, h, q, S);
-  const float* nk = reinterpret_cast<const float*>(buf + kNormOff);
-  const float* nv = nk + kKeys;
-  float u[32];
+// Prefix tiles: rotated basis, fp16 MFMAs, per-key norms.
+struct PrefixTiles {
+  const ExtendArgs& a;
+  int b, kvh, P;
+  const f16x8 (&q)[2][8];
+  float rs;
+  __device__ __forceinline__ const uint8_t* image(int t) const { return prefix_image(a, b, kvh, t); }
+  __device__ __forceinline__ bool active(int) const { return true; }
+  __device__ __forceinline__ void qk(const uint8_t* buf, int l32, int h, f32x16 (&S)[2]) const {
+    qk_tile<f16x8, 2>(buf, l32, h, q, S);
+  }
+  // scores / rs of tile t into u (masked past the prefix), returns rs
+  __device__ __forceinline__ float scores(const uint8_t* buf, int t, int h, const f32x16 (&S)[2], float (&u)[32]) const {
+    const float* nk = reinterpret_cast<const float*>(buf + kNormOff);
+    const int limit = P - t * kKeys;
 #pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    const int key = 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h;   // keys key .. key+3
-    const float4 n4 = *reinterpret_cast<const float4*>(nk + key);
-    const float nn[4] = {n4.x, n4.y, n4.z, n4.w};
+    for (int i = 0; i < 32; i += 4) {
+      const int key = 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h;   // keys key .. key+3
+      const float4 n4 = *reinterpret_cast<const float4*>(nk + key);
+      const float nn[4] = {n4.x, n4.y, n4.z, n4.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u[i + j] = S[i >> 4][(i & 15) + j] * nn[j];
-      if (TAIL) u[i + j] = key + j < limit ? u[i + j] : kNegInf;
+      for (int j = 0; j < 4; ++j) u[i + j] = S[i >> 4][(i & 15) + j] * nn[j];
+    }
+    if (limit < kKeys) {                                     // the prefix ends inside this tile
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h + (i & 3) >= limit) u[i] = kNegInf;
+    }
+    return rs;
+  }
+  __device__ __forceinline__ void weights(const uint8_t* buf, int h, const float (&u)[32], u32x4 (&Pw)[4][2]) const {
+    const float* nv = reinterpret_cast<const float*>(buf + kNormOff) + kKeys;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float x[8];
+#pragma unroll
+      for (int e4 = 0; e4 < 2; ++e4) {
+        const float4 n4 = *reinterpret_cast<const float4*>(nv + 16 * st + 8 * e4 + 4 * h);
+        x[4 * e4 + 0] = u[8 * st + 4 * e4 + 0] * n4.x;
+        x[4 * e4 + 1] = u[8 * st + 4 * e4 + 1] * n4.y;
+        x[4 * e4 + 2] = u[8 * st + 4 * e4 + 2] * n4.z;
+        x[4 * e4 + 3] = u[8 * st + 4 * e4 + 3] * n4.w;
+      }
+      f16x8 ph, pl;
+      split_f16x8(x, ph, pl);
+      Pw[st][0] = __builtin_bit_cast(u32x4, ph);
+      Pw[st][1] = __builtin_bit_cast(u32x4, pl);
     }
   }
-  softmax_step(u, rs, m_run, l_run, O, lane);
-  pv_tile<f16x8>(buf, l32, h, u,
-                 [&](int st, f16x8& ph, f16x8& pl) {
-                   float x[8];
-#pragma unroll
-                   for (int e4 = 0; e4 < 2; ++e4) {
-                     const float4 n4 = *reinterpret_cast<const float4*>(nv + 16 * st + 8 * e4 + 4 * h);
-                     x[4 * e4 + 0] = u[8 * st + 4 * e4 + 0] * n4.x;
-                     x[4 * e4 + 1] = u[8 * st + 4 * e4 + 1] * n4.y;
-                     x[4 * e4 + 2] = u[8 * st + 4 * e4 + 2] * n4.z;
-                     x[4 * e4 + 3] = u[8 * st + 4 * e4 + 3] * n4.w;
-                   }
-                   split_f16x8(x, ph, pl);
-                 },
-                 O);
-}
-
-// One chunk tile: QK (bf16, exact), causal mask, softmax, weights split hi + lo, PV (bf16).
-__device__ __forceinline__ void chunk_tile(const uint8_t* buf, int key0, int tok, float rs, int l32, int h, int lane,
-                                           const bf16x8 (&qb)[1][8], float& m_run, float& l_run, f32x16 (&O)[4]) {
-  f32x16 S[2];
-  qk_tile<bf16x8, 1>(buf, l32, h, qb, S);
-  float u[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int key = key0 + 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h + (i & 3);
-    u[i] = key <= tok ? S[i >> 4][i & 15] : kNegInf;
+  __device__ __forceinline__ void pv(const uint8_t* buf, int l32, int h, const u32x4 (&Pw)[4][2], f32x16 (&O)[4]) const {
+    pv_tile<f16x8>(buf, l32, h, Pw, O);
   }
-  softmax_step(u, rs, m_run, l_run, O, lane);
-  pv_tile<bf16x8>(buf, l32, h, u, [&](int st, bf16x8& ph, bf16x8& pl) { split_bf16x8(u + 8 * st, ph, pl); }, O);
+};
+
+// Chunk tiles: original basis, bf16 MFMAs, causal mask; tiles past a wave's last token are skipped.
+struct ChunkTiles {
+  const ExtendArgs& a;
+  int b, kvh, tok, wave_first, wave_last;
+  const bf16x8 (&q)[1][8];
+  __device__ __forceinline__ const uint8_t* image(int t) const { return chunk_image(a, b, kvh, t); }
+  __device__ __forceinline__ bool active(int t) const { return t * kKeys <= wave_last; }
+  __device__ __forceinline__ void qk(const uint8_t* buf, int l32, int h, f32x16 (&S)[2]) const {
+    qk_tile<bf16x8, 1>(buf, l32, h, q, S);
+  }
+  __device__ __forceinline__ float scores(const uint8_t*, int t, int h, const f32x16 (&S)[2], float (&u)[32]) const {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) u[i] = S[i >> 4][i & 15];
+    if ((t + 1) * kKeys > wave_first) {                      // the tile reaches this wave's diagonal
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (t * kKeys + 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h + (i & 3) > tok) u[i] = kNegInf;
+    }
+    return a.scale_log2;
+  }
+  __device__ __forceinline__ void weights(const uint8_t*, int, const float (&u)[32], u32x4 (&Pw)[4][2]) const {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 ph, pl;
+      split_bf16x8(u + 8 * st, ph, pl);
+      Pw[st][0] = __builtin_bit_cast(u32x4, ph);
+      Pw[st][1] = __builtin_bit_cast(u32x4, pl);
+    }
+  }
+  __device__ __forceinline__ void pv(const uint8_t* buf, int l32, int h, const u32x4 (&Pw)[4][2], f32x16 (&O)[4]) const {
+    pv_tile<bf16x8>(buf, l32, h, Pw, O);
+  }
+};
+
+// A tile image into LDS: 36 one-kilobyte direct loads shared by the 8 waves.
+__device__ __forceinline__ void issue_tile(const uint8_t* src, uint8_t* dst, int wv, int lane) {
+  for (int i = wv; i < kExtendTileBytes / 1024; i += kWaves) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + i * 1024 + lane * 16),
+                                     (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+  }
 }
 
-__global__ __launch_bounds__(256, 2) void k_extend_attn(const ExtendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kExtendTileBytes];
+// Register values that must exist at this point of the instruction stream.
+__device__ __forceinline__ void pin(u32x4 (&P)[4][2], f32x16 (&O)[4]) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) asm volatile("" : "+v"(P[st][0]), "+v"(P[st][1]));
+  asm volatile("" : "+v"(O[0]), "+v"(O[1]), "+v"(O[2]), "+v"(O[3]));
+}
+__device__ __forceinline__ void pin(f32x16 (&S)[2], f32x16 (&O)[4]) {
+  asm volatile("" : "+v"(S[0]), "+v"(S[1]));
+  asm volatile("" : "+v"(O[0]), "+v"(O[1]), "+v"(O[2]), "+v"(O[3]));
+}
+
+// Barrier; with `loads` it first waits until this wave's direct-to-LDS tile loads have landed.
+__device__ __forceinline__ void sync_tiles(bool loads) {
+  if (loads) __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+  __syncthreads();
+}
+
+// Ping-pong over n tiles.  The two 4-wave groups alternate between an MFMA cluster (QK of tile
+// it+1, PV of tile it) and a VALU cluster (softmax of tile it's scores, the weights' split); group
+// B runs one barrier phase behind group A, so one group's MFMAs overlap the other's softmax.
+// Tiles live in a ring of three LDS buffers; tile it+2 is loaded during barrier phase 2*it+1 (by
+// group A in its MFMA cluster, group B in its VALU cluster), after the last read of tile it-1
+// (group B's PV in phase 2*it); each wave waits for its loads at the end of the following phase,
+// before the tile's first read in phase 2*it+3.
+template <typename Tiles>
+__device__ __forceinline__ void run_tiles(const Tiles& k, int n, uint8_t* ring, bool group_b, int wv, int lane, int l32,
+                                          int h, float& m_run, float& l_run, f32x16 (&O)[4]) {
+  if (n <= 0) return;
+  auto buf = [&](int t) { return ring + (t % 3) * kExtendTileBytes; };
+  issue_tile(k.image(0), buf(0), wv, lane);
+  if (n > 1) issue_tile(k.image(1), buf(1), wv, lane);
+  sync_tiles(true);
+  if (group_b) sync_tiles(false);
+  f32x16 S[2];
+  if (k.active(0)) k.qk(buf(0), l32, h, S);
+  sync_tiles(false);
+  u32x4 Pw[4][2];
+  for (int it = 0; it < n; ++it) {
+    // ---- VALU cluster: softmax of tile it
+    if (group_b && it + 2 < n) issue_tile(k.image(it + 2), buf(it + 2), wv, lane);
+    const bool act = k.active(it);
+    if (act) {
+      float u[32];
+      const float rs = k.scores(buf(it), it, h, S, u);
+      softmax_step(u, rs, m_run, l_run, O, lane);
+      k.weights(buf(it), h, u, Pw);
+    }
+    // keep each cluster's work on its side of the barrier (the compiler would otherwise sink the
+    // weights and the rescale into the MFMA cluster, next to their uses)
+    pin(Pw, O);
+    sync_tiles(!group_b);            // group A: tile it+1's loads, issued one phase ago, have landed
+    // ---- MFMA cluster: QK of tile it+1, PV of tile it
+    if (!group_b && it + 2 < n) issue_tile(k.image(it + 2), buf(it + 2), wv, lane);
+    if (it + 1 < n && k.active(it + 1)) k.qk(buf(it + 1), l32, h, S);
+    if (act) k.pv(buf(it), l32, h, Pw, O);
+    pin(S, O);
+    sync_tiles(group_b);             // group B: tile it+2's loads, issued one phase ago, have landed
+  }
+  if (!group_b) sync_tiles(true);
+}
+
+__global__ __launch_bounds__(kWaves * 64, 1) void k_extend_attn(const ExtendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * kExtendTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_b = wv >= kWaves / 2;
   const int l32 = lane & 31, h = lane >> 5;
   const int kvh = blockIdx.x % a.hkv, tile = blockIdx.x / a.hkv, b = blockIdx.y;
 
@@ -421,7 +508,6 @@ __global__ __launch_bounds__(256, 2) void k_extend_attn(const ExtendArgs a) {
   // ================= prefix phase (rotated basis, fp16 MFMA) =================
   const int n_pt = (P + kKeys - 1) / kKeys;
   if (n_pt > 0) {
-    load_tile(prefix_image(a, b, kvh, 0), lds[0], wv, lane);
     const float rw = a.quat[0], rx = a.quat[1], ry = a.quat[2], rz = a.quat[3];
     // rotated, scaled query as fp16 hi + lo
     f16x8 qs[2][8];                                         // [hi, lo][ks]
@@ -459,16 +545,8 @@ __global__ __launch_bounds__(256, 2) void k_extend_attn(const ExtendArgs a) {
         split_f16x8(x, qs[0][ks], qs[1][ks]);
       }
     }
-    wait_tile_and_sync();
-
-    for (int it = 0; it < n_pt; ++it) {
-      const uint8_t* cur = lds[it & 1];
-      if (it + 1 < n_pt) load_tile(prefix_image(a, b, kvh, it + 1), lds[(it + 1) & 1], wv, lane);
-      const int limit = P - it * kKeys;
-      if (limit >= kKeys) prefix_tile<false>(cur, limit, l32, h, lane, qs, rs, m_run, l_run, O);
-      else prefix_tile<true>(cur, limit, l32, h, lane, qs, rs, m_run, l_run, O);
-      wait_tile_and_sync();
-    }
+    const PrefixTiles pk{a, b, kvh, P, qs, rs};
+    run_tiles(pk, n_pt, ring, group_b, wv, lane, l32, h, m_run, l_run, O);
     // back to the original basis: O[t][4g .. 4g+3] is head_dim 32t + 8g + 4h .. +3, one group
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -483,23 +561,18 @@ __global__ __launch_bounds__(256, 2) void k_extend_attn(const ExtendArgs a) {
   }
 
   // ================= chunk phase (original basis, bf16 MFMA) =================
-  const int kmax = min(n_b, tok0 + kWaves * tw);            // new keys any row of the workgroup sees
-  const int n_nt = (kmax + kKeys - 1) / kKeys;
-  const int wave_last = tok0 + wv * tw + tw - 1;
-  load_tile(chunk_image(a, b, kvh, 0), lds[0], wv, lane);
-  bf16x8 qb[1][8];
+  {
+    const int kmax = min(n_b, tok0 + kWaves * tw);          // new keys any row of the workgroup sees
+    const int n_nt = (kmax + kKeys - 1) / kKeys;
+    bf16x8 qb[1][8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * ks);
-    if (!valid) raw = make_uint4(0, 0, 0, 0);
-    qb[0][ks] = __builtin_bit_cast(bf16x8, raw);
-  }
-  wait_tile_and_sync();
-  for (int nt = 0; nt < n_nt; ++nt) {
-    const uint8_t* cur = lds[nt & 1];
-    if (nt + 1 < n_nt) load_tile(chunk_image(a, b, kvh, nt + 1), lds[(nt + 1) & 1], wv, lane);
-    if (nt * kKeys <= wave_last) chunk_tile(cur, nt * kKeys, tok, a.scale_log2, l32, h, lane, qb, m_run, l_run, O);
-    wait_tile_and_sync();
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+      if (!valid) raw = make_uint4(0, 0, 0, 0);
+      qb[0][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+    const ChunkTiles ck{a, b, kvh, tok, tok0 + wv * tw, tok0 + wv * tw + tw - 1, qb};
+    run_tiles(ck, n_nt, ring, group_b, wv, lane, l32, h, m_run, l_run, O);
   }
 
   // ---- normalise and write: lanes l and l ^ 32 hold the two halves of a row's sum
@@ -522,7 +595,7 @@ float extend_level_scale() { return kLevelScale; }
 
 hipError_t launch_extend(const ExtendArgs& a, int tiles_per_seq, hipStream_t s) {
   k_extend_stage<<<dim3((unsigned)(a.pt_max + a.nt_max), (unsigned)a.hkv, (unsigned)a.batch), dim3(256), 0, s>>>(a);
-  k_extend_attn<<<dim3((unsigned)(a.hkv * tiles_per_seq), (unsigned)a.batch), dim3(256), 0, s>>>(a);
+  k_extend_attn<<<dim3((unsigned)(a.hkv * tiles_per_seq), (unsigned)a.batch), dim3(kWaves * 64), 0, s>>>(a);
   return hipGetLastError();
 }
 

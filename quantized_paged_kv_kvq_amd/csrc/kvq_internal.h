@@ -126,10 +126,11 @@ struct ExtendArgs {
   int16_t head_list[KVQ_MAX_Q_HEADS];
 };
 
-// Query tokens of one workgroup for a group width (power of two <= 32).
-inline int extend_tokens_per_block(int g_pad) { return 4 * (32 / g_pad); }
+// Extend attention workgroups have 8 waves of 32 query rows; a row is (token, query head slot).
+constexpr int kExtendWaves = 8;
+inline int extend_tokens_per_block(int g_pad) { return kExtendWaves * (32 / g_pad); }
 // One 64-key tile image: K [64][128] + V [128][64] 16-bit values (rows padded by 16 bytes), then
-// 64 + 64 fp32 norms, rounded up to whole kilobytes per wave of a 4-wave workgroup.
+// 64 + 64 fp32 norms, rounded up to whole kilobytes.
 constexpr int kExtendTileBytes = 36864;
 inline size_t extend_workspace_bytes(int batch, int hkv, int pt_max, int nt_max) {
   return (size_t)batch * hkv * ((size_t)pt_max + nt_max) * kExtendTileBytes;
