@@ -550,87 +550,106 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   for (int rt = 0; rt < RT; ++rt) {
     const int r = 16 * rt + i16;
     if (r >= R || (DUP && i16 >= 8)) continue;
+    float* row = part_o + ((row0 + r) * a.n_splits + split) * D;
+    auto put4 = [&](float* p, float x0, float x1, float x2, float x3) {
+      *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+    };
     if (j4 == 0) {
       float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
       ml[0] = m_run[rt]; ml[1] = l_run[rt];
     }
-    float* row = part_o + ((row0 + r) * a.n_splits + split) * D;
     if constexpr (VF == 1) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)   // lane holds d = 16t + 4*j4 + k
-        *reinterpret_cast<float4*>(row + 16 * t + 4 * j4) = make_float4(O[rt][t][0], O[rt][t][1], O[rt][t][2], O[rt][t][3]);
+        put4(row + 16 * t + 4 * j4, O[rt][t][0], O[rt][t][1], O[rt][t][2], O[rt][t][3]);
     } else {
 #pragma unroll
       for (int g = 0; g < NVG; ++g) {  // tiles 2g (even d) / 2g+1 (odd d): d = 32g + 8*j4 + 2k (+1)
         const f32x4 e = O[rt][2 * g], o = O[rt][2 * g + 1];
-        *reinterpret_cast<float4*>(row + 32 * g + 8 * j4) = make_float4(e[0], o[0], e[1], o[1]);
-        *reinterpret_cast<float4*>(row + 32 * g + 8 * j4 + 4) = make_float4(e[2], o[2], e[3], o[3]);
+        put4(row + 32 * g + 8 * j4, e[0], o[0], e[1], o[1]);
+        put4(row + 32 * g + 8 * j4 + 4, e[2], o[2], e[3], o[3]);
       }
     }
   }
 }
 
-// Log-sum-exp combine of the split partials.  One workgroup per (64 head_dim values, row, KV head,
-// sequence): the split weights 2^(m_s - M) are computed once into LDS, then 16 groups of 16 lanes
-// stream the splits' 64-value slices and a final LDS reduction normalises.
+// Log-sum-exp combine of the split partials of one (64 head_dim values, row, KV head, sequence)
+// slice by one workgroup of 256 threads: M = max of the split maxima, then 16 groups of 16 lanes
+// stream the splits' 64-value slices weighted by 2^(m_s - M) and an LDS reduction normalises.
 constexpr int kMaxSplits = 8192;
 
 template <int D>
-__global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int row_alloc) {
-  __shared__ float w_s[kMaxSplits];
+__device__ __forceinline__ void combine_slice(const DecodeArgs& a, int row_alloc, int b, int kvh, int r, int c) {
   __shared__ float red[256];
   __shared__ float4 acc_s[256];
-  constexpr int NC = D / 64;
-  const int c = blockIdx.x % NC, r = blockIdx.x / NC, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int tid = threadIdx.x;
+  const bool act = tid < 256;                               // a split workgroup may have more threads
   const int h0 = a.g_uniform > 0 ? kvh * a.g_uniform : a.head_off[kvh];
   const int G = a.g_uniform > 0 ? a.g_uniform : a.head_off[kvh + 1] - h0;
-  if (r >= a.n_q * G) return;
   const int t = r / G, hq = a.g_uniform > 0 ? h0 + r % G : a.head_list[h0 + r % G];
   const int S = a.n_splits;
   const size_t row = (size_t)(b * a.hkv + kvh) * row_alloc + r;
   const float* ml = a.part + row * S * 2;
-  const float* po = a.part + (size_t)a.batch * a.hkv * row_alloc * S * 2 + row * S * D + 64 * c;
+  const float* po = a.part + (size_t)a.batch * a.hkv * row_alloc * S * 2 + row * S * D;   // row's [S][D]
+  // (m, l) of split s; 4 values of split s at head_dim d
+  auto ml_of = [&](int s) -> float2 { return *reinterpret_cast<const float2*>(ml + 2 * s); };
+  auto o_of = [&](int s, int d) -> float4 { return *reinterpret_cast<const float4*>(po + (size_t)s * D + d); };
 
-  float mx = kNegInf;
-  for (int s = tid; s < S; s += 256)
-    if (ml[2 * s + 1] > 0.0f) mx = fmaxf(mx, ml[2 * s]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = 128; o >= 1; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float den = 0.0f;
-  for (int s = tid; s < S; s += 256) {
-    const float l = ml[2 * s + 1];
-    const float w = l > 0.0f ? __builtin_amdgcn_exp2f(ml[2 * s] - M) : 0.0f;
-    w_s[s] = w;
-    den += w * l;
-  }
-  red[tid] = den;
-  __syncthreads();
-  for (int o = 128; o >= 1; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float total = red[0];
-
-  const int sl = tid >> 4, d4 = tid & 15;
+  // Each thread reads the (m, l) and 4 output values of its splits s = sl, sl + 16, ... up front
+  // (all loads in flight together), then the row max and the sum of weights come from LDS
+  // reductions over the 16 split lanes that share a head_dim group.
+  constexpr int kPer = 8;                                   // splits per thread held in registers
+  const int sl = tid >> 4, d = 64 * c + 4 * (tid & 15);
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  // Loads are unconditional so that several are in flight per thread; a split with no visible
-  // cell (weight 0) never wrote its slice, so its contribution is selected away, not multiplied.
-#pragma unroll 8
-  for (int s = sl; s < S; s += 16) {
-    const float w = w_s[s];
-    const float4 v = *reinterpret_cast<const float4*>(po + (size_t)s * D + 4 * d4);
-    const bool on = w != 0.0f;
-    acc.x += on ? w * v.x : 0.0f; acc.y += on ? w * v.y : 0.0f;
-    acc.z += on ? w * v.z : 0.0f; acc.w += on ? w * v.w : 0.0f;
+  float mx = kNegInf, den = 0.0f;                           // acc and den are relative to 2^mx
+  for (int s0 = 0; s0 < S; s0 += 16 * kPer) {
+    float2 mlv[kPer];
+    float4 ov[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = min(s0 + sl + 16 * k, S - 1);
+      mlv[k] = act ? ml_of(s) : make_float2(kNegInf, 0.0f);
+      ov[k] = act ? o_of(s, d) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (s0 + sl + 16 * k >= S) mlv[k].y = 0.0f;           // past the last split: weight 0
+    }
+    // running rescale: acc is kept relative to mx
+    float m_new = mx;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) m_new = mlv[k].y > 0.0f ? fmaxf(m_new, mlv[k].x) : m_new;
+    const float mu = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = mx == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mx - mu);
+    acc.x *= alpha; acc.y *= alpha; acc.z *= alpha; acc.w *= alpha;
+    den *= alpha;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool on = mlv[k].y > 0.0f;
+      const float w = on ? __builtin_amdgcn_exp2f(mlv[k].x - mu) : 0.0f;
+      acc.x += on ? w * ov[k].x : 0.0f; acc.y += on ? w * ov[k].y : 0.0f;
+      acc.z += on ? w * ov[k].z : 0.0f; acc.w += on ? w * ov[k].w : 0.0f;
+      den += on ? w * mlv[k].y : 0.0f;
+    }
+    mx = m_new;
   }
-  acc_s[tid] = acc;
+  // merge the 16 split lanes: common max, rescale, sum
+  if (act) red[tid] = mx;
   __syncthreads();
+  float M = kNegInf;
+  if (act) {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) M = fmaxf(M, red[16 * g + (tid & 15)]);
+  }
+  const float Mu = M == kNegInf ? 0.0f : M;
+  const float scale = mx == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mx - Mu);
+  __syncthreads();
+  if (act) {
+    acc.x *= scale; acc.y *= scale; acc.z *= scale; acc.w *= scale;
+    acc_s[tid] = acc;
+    red[tid] = den * scale;
+  }
+  __syncthreads();
+  float total = 0.0f;                                       // one den per split lane group
+#pragma unroll
+  for (int g = 0; g < 16; ++g) total += red[16 * g];
   if (tid < 16) {
     float4 sum = acc_s[tid];
 #pragma unroll
@@ -642,19 +661,29 @@ __global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int 
     float* out = a.out + (((size_t)b * a.n_q + t) * a.n_q_heads + hq) * D + 64 * c + 4 * tid;
     *reinterpret_cast<float4*>(out) = make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
   }
+  __syncthreads();                                          // red / acc_s are reused by the next slice
 }
+
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int row_alloc) {
+  constexpr int NC = D / 64;
+  const int c = blockIdx.x % NC, r = blockIdx.x / NC, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.g_uniform > 0 ? a.g_uniform : a.head_off[kvh + 1] - a.head_off[kvh];
+  if (r >= a.n_q * G) return;
+  combine_slice<D>(a, row_alloc, b, kvh, r, c);
+}
+
 
 template <int D, int RT, int VF, int SH>
 hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   // two row tiles (verify windows) keep 128 accumulator registers per lane: one wave per SIMD,
   // four waves per workgroup, one page of prefetch
   constexpr Shape sh = RT == 1 ? kShapes[SH] : Shape{4, 8, 1, 1};
-  constexpr int PD = sh.pd;
-  dim3 grid(plan.n_splits, a.hkv, a.batch);
+  const dim3 grid(plan.n_splits, a.hkv, a.batch), block(sh.nw * 64);
   if (RT == 1 && plan.dup)
-    k_decode_split<D, RT, VF, sh.nw, sh.ppw, PD, sh.occ, true><<<grid, dim3(sh.nw * 64), 0, s>>>(a);
+    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true><<<grid, block, 0, s>>>(a);
   else
-    k_decode_split<D, RT, VF, sh.nw, sh.ppw, PD, sh.occ, false><<<grid, dim3(sh.nw * 64), 0, s>>>(a);
+    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, false><<<grid, block, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid((D / 64) * 16 * RT, a.hkv, a.batch);
