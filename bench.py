@@ -64,6 +64,24 @@ def algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v):
     return cells * per_cell + pages * 4 + q + out
 
 
+def recorded_traffic(workload: str):
+    """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE profile of this workload,
+    or None when there is none or the decode kernel source has changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "decode_int8_moe_131072.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"traffic-record: workload=(\S+) source=(\S+) source_sha256_16=([0-9a-f]+) traffic_bytes=(\d+)",
+                  open(path).read())
+    if not m or m.group(1) != workload:
+        return None
+    src = os.path.join(ROOT, m.group(2))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != m.group(3):
+        return None
+    return int(m.group(4))
+
+
 def cpu_baseline(w, budget_s: float = 15.0):
     """Time the oracle's step (encode the step's tokens, then fp64 attention over the dequantised
     cache) on the host cores; the oracle's cache is filled first, outside the timing."""
@@ -225,6 +243,19 @@ def bench_extend(args):
     print(json.dumps(line))
 
 
+def copy_probe(nbytes: int):
+    """A plain copy of a known number of bytes (torch's elementwise copy kernel), five times: the
+    per-dispatch FETCH_SIZE / WRITE_SIZE counters of this kernel calibrate those of the others."""
+    import torch
+    n = nbytes // 16 * 16
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +265,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--replicas", type=int, default=0, help="cache copies to rotate (0 = enough to exceed the MALL)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="run only a plain device copy of BYTES (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
@@ -246,6 +279,8 @@ def main():
     from kvq_testutil import dev_bf16, dev_i32, token_lists
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
     kvq.lib()
     if args.workload == "iso3_extend":
         return bench_extend(args)
@@ -254,7 +289,8 @@ def main():
     cb_k, ns_k = kvq.cell_bytes(w.fmt_k, w.head_dim)
     cb_v, ns_v = kvq.cell_bytes(w.fmt_v, w.head_dim)
     cache_bytes = w.num_pages * w.n_kv_heads * 16 * ((cb_k + 2 * ns_k) + (cb_v + 2 * ns_v))
-    R = args.replicas or max(2, int(np.ceil(3 * MALL_BYTES / cache_bytes)) + 1)
+    # enough copies to exceed three times the Infinity Cache (capped: a tiny cache stays latency-bound)
+    R = args.replicas or min(64, max(2, int(np.ceil(3 * MALL_BYTES / cache_bytes)) + 1))
 
     pre = token_lists(w, "prefix")
     step = token_lists(w, "step")
@@ -371,7 +407,7 @@ def main():
                    "step": "append new K/V token(s) + decode attention", "cache_replicas": R,
                    "launch": mode},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
                      "kernel": "decode attention launch (split-K kernel + log-sum-exp combine kernel)",
                      "launch_us": round(dec_avg, 3), "algorithmic_bytes": int(algo)},
         "cpu_baseline": cpu,
