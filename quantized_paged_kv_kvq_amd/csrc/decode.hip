@@ -38,15 +38,16 @@ namespace {
 // each wave keeps in flight ahead of the one it processes, and waves per SIMD the registers allow.
 struct Shape { int nw, ppw, pd, occ; };
 constexpr Shape kShapes[] = {{4, 16, 2, 2}, {4, 8, 1, 2}, {8, 8, 1, 2}};
-constexpr int kDefaultShape = 0;
+constexpr int kNumShapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
 
-int shape_index() {
-  static int idx = -1;
-  if (idx < 0) {
-    idx = kDefaultShape;
+// KVQ_DECODE_SHAPE overrides the choice (for tuning); -1 when unset
+int shape_override() {
+  static int idx = -2;
+  if (idx == -2) {
+    idx = -1;
     if (const char* e = getenv("KVQ_DECODE_SHAPE")) {
       const int v = atoi(e);
-      if (v >= 0 && v < (int)(sizeof(kShapes) / sizeof(kShapes[0]))) idx = v;
+      if (v >= 0 && v < kNumShapes) idx = v;
     }
   }
   return idx;
@@ -97,6 +98,14 @@ __device__ __forceinline__ void split_bf16(const float x[4], s16x4& hi, s16x4& l
   const uint32_t l1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[2]) |
                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[3]) << 16);
   lo = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
+}
+
+// Cache loads: non-temporal when each page is read by one workgroup (streamed once), plain when the
+// row groups of a split read it in turn (the later ones then find it in L2).
+template <bool NT>
+__device__ __forceinline__ uint4 page_load(const void* p) {
+  if constexpr (NT) return stream_load(p);
+  else return *reinterpret_cast<const uint4*>(p);
 }
 
 template <int N>
@@ -152,7 +161,7 @@ struct PageBuf {
   }
 };
 
-template <int D, int VF>
+template <int D, int VF, bool NT>
 __device__ __forceinline__ void load_page(PageBuf<D, VF>& pb, const DecodeArgs& a, int page, int kvh, int lane) {
   constexpr int NG = PageBuf<D, VF>::NG, NVG = PageBuf<D, VF>::NVG;
   const int i16 = lane & 15, j4 = lane >> 4;
@@ -160,12 +169,12 @@ __device__ __forceinline__ void load_page(PageBuf<D, VF>& pb, const DecodeArgs& 
   // K tile: 16-byte chunk c of slot t at (c * 16 + t) * 16; this lane's chunk for group g is 4g + j4
   const uint4* kb = reinterpret_cast<const uint4*>(a.k_codes + tile * (16 * D)) + lane;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) pb.k[g] = stream_load(kb + 64 * g);
+  for (int g = 0; g < NG; ++g) pb.k[g] = page_load<NT>(kb + 64 * g);
   load_words<2 * NG>(pb.ks, reinterpret_cast<const uint32_t*>(a.k_scales + (tile * 16 + 4 * j4) * NG));
   // V tile: 16-byte unit (64*G + 4*i16 + j4) holds tiles 4G..4G+3 (one word each) of row i16
   const uint4* vb = reinterpret_cast<const uint4*>(a.v_codes + tile * (16 * (VF == 1 ? D : D / 2))) + 4 * i16 + j4;
 #pragma unroll
-  for (int G = 0; G < PageBuf<D, VF>::NVQ; ++G) pb.v[G] = stream_load(vb + 64 * G);
+  for (int G = 0; G < PageBuf<D, VF>::NVQ; ++G) pb.v[G] = page_load<NT>(vb + 64 * G);
   load_words<2 * NVG>(pb.vs, reinterpret_cast<const uint32_t*>(a.v_scales + (tile * 16 + 4 * j4) * NVG));
 }
 
@@ -329,19 +338,25 @@ __device__ __forceinline__ void hadamard_rows(f32x4 (&O)[RT][16], int lane) {
   }
 }
 
-template <int D, int RT, int VF, int NW, int PPW, int PD, int OCC, bool DUP>
+template <int D, int RT, int VF, int NW, int PPW, int PD, int OCC, bool DUP, bool NTL>
 __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs a) {
   constexpr int NG = D / 64;
   constexpr int NVG = VF == 1 ? D / 64 : D / 32;
   constexpr int NT = D / 16;                                // PV tiles of 16 head_dim rows
-  constexpr int RA = 16 * RT;                               // allocated rows
   constexpr float kOff = VF == 1 ? 128.0f : 136.0f;         // bias carried by the V A-operand
+  const int RA = a.row_alloc;                               // allocated rows per (sequence, KV head)
 
   // wave-uniform wave index: page ids then come through scalar loads, which do not wait on the
   // vector-memory counter that tracks the prefetched page
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, j4 = lane >> 4;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // blockIdx.x -> (split, row group) so that the row groups of a split share blockIdx.x % 8, i.e.
+  // run on the same XCD (workgroups are dealt to the 8 XCDs round robin) and share its L2
+  const int n_rg = a.row_groups;
+  const int xg = blockIdx.x, rem = xg % (8 * n_rg);
+  const int rg = rem >> 3, split = (xg / (8 * n_rg)) * 8 + (rem & 7);
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  if (split >= a.n_splits) return;                          // the grid is rounded up to 8 splits
 
   // ---- rows of this KV head.  With the default grouping (query head h reads KV head h / G) the
   // q addresses are arithmetic on kernel arguments; an explicit head map goes through the lists.
@@ -362,7 +377,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   const int seq_len = clampi(a.seq_lens[b], 0, cap);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = DUP ? (i16 & 7) : 16 * rt + i16;
+    const int r = DUP ? 8 * rg + (i16 & 7) : 16 * rt + i16;
     valid[rt] = r < R;
     const int t = valid[rt] ? r / G : 0;
     const int i = valid[rt] ? r % G : 0;
@@ -391,7 +406,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   PageBuf<D, VF> buf[PD + 1];
 #pragma unroll
   for (int i = 0; i < PD && i < PPW; ++i)
-    load_page<D, VF>(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, lane);
+    load_page<D, VF, NTL>(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, lane);
 
   int Lmax = 0;
   for (int t = 0; t < a.n_q; ++t)
@@ -404,8 +419,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   if (R == 0) return;
   if (p_begin >= p_end) {                                   // nothing visible in this split
-    if (threadIdx.x < RA) {
-      float* ml = part_ml + ((row0 + threadIdx.x) * a.n_splits + split) * 2;
+    const int r = DUP ? 8 * rg + (int)threadIdx.x : (int)threadIdx.x;
+    if ((int)threadIdx.x < (DUP ? 8 : RA) && r < RA) {
+      float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
       ml[0] = kNegInf; ml[1] = 0.0f;
     }
     return;
@@ -473,8 +489,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     for (int i = 0; i < PPW; ++i) {
       const int pc = p0 + i * NW;
       if (i + PD < PPW)
-        load_page<D, VF>(buf[(i + PD) % (PD + 1)], a, clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1),
-                         kvh, lane);
+        load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a,
+                              clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1), kvh, lane);
       page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qf, qmul, m_run, l_run, ls, O);
       if (i + 1 >= n_mine) break;
     }
@@ -548,7 +564,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   // ---- write the workgroup's partial for rows r < R
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + i16;
+    const int r = DUP ? 8 * rg + i16 : 16 * rt + i16;
     if (r >= R || (DUP && i16 >= 8)) continue;
     float* row = part_o + ((row0 + r) * a.n_splits + split) * D;
     auto put4 = [&](float* p, float x0, float x1, float x2, float x3) {
@@ -676,24 +692,24 @@ __global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int 
 
 template <int D, int RT, int VF, int SH>
 hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
-  // two row tiles (verify windows) keep 128 accumulator registers per lane: one wave per SIMD,
-  // four waves per workgroup, one page of prefetch
-  constexpr Shape sh = RT == 1 ? kShapes[SH] : Shape{4, 8, 1, 1};
-  const dim3 grid(plan.n_splits, a.hkv, a.batch), block(sh.nw * 64);
-  if (RT == 1 && plan.dup)
-    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true><<<grid, block, 0, s>>>(a);
+  constexpr Shape sh = kShapes[SH];
+  // with several row groups the splits are padded to a multiple of 8 (see the blockIdx mapping)
+  const int gx = plan.row_groups == 1 ? plan.n_splits : (plan.n_splits + 7) / 8 * 8 * plan.row_groups;
+  const dim3 grid((unsigned)gx, a.hkv, a.batch), block(sh.nw * 64);
+  if (plan.row_groups == 1)
+    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, true><<<grid, block, 0, s>>>(a);
   else
-    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, false><<<grid, block, 0, s>>>(a);
+    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, false><<<grid, block, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid((D / 64) * 16 * RT, a.hkv, a.batch);
-  k_decode_combine<D><<<cgrid, dim3(256), 0, s>>>(a, 16 * RT);
+  dim3 cgrid((D / 64) * plan.rows, a.hkv, a.batch);
+  k_decode_combine<D><<<cgrid, dim3(256), 0, s>>>(a, a.row_alloc);
   return hipGetLastError();
 }
 
 template <int D, int RT, int VF>
 hipError_t launch_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
-  switch (shape_index()) {
+  switch (plan.shape) {
     case 1: return launch_t<D, RT, VF, 1>(plan, a, s);
     case 2: return launch_t<D, RT, VF, 2>(plan, a, s);
     default: return launch_t<D, RT, VF, 0>(plan, a, s);
@@ -706,24 +722,32 @@ int decode_max_splits() { return kMaxSplits; }
 
 DecodePlan plan_decode(int head_dim, int hkv, int batch, int max_pages, int max_rows) {
   DecodePlan p{};
-  p.row_tiles = max_rows <= 16 ? 1 : 2;
-  const Shape sh = p.row_tiles == 1 ? kShapes[shape_index()] : Shape{4, 8, 1, 1};
-  p.dup = max_rows <= 8;
+  // up to 8 query rows per KV head share one MFMA (weights' hi parts in columns 0-7, lo parts in
+  // 8-15); more rows take one workgroup per group of 8 rows
+  p.rows = max_rows;
+  p.row_groups = max(1, (max_rows + 7) / 8);
+  // 64-page splits (16 pages per wave, two in flight) unless that leaves CUs without a workgroup;
+  // then 32-page splits
+  auto splits_of = [&](int sh) { return (max_pages + kShapes[sh].nw * kShapes[sh].ppw - 1) / (kShapes[sh].nw * kShapes[sh].ppw); };
+  p.shape = shape_override();
+  if (p.shape < 0) {
+    p.shape = 0;
+    if ((long)splits_of(0) * hkv * batch * p.row_groups < device_cu_count()) p.shape = 1;
+  }
+  const Shape sh = kShapes[p.shape];
   p.waves = sh.nw;
   p.pages_per_split = sh.nw * sh.ppw;
-  p.n_splits = (max_pages + p.pages_per_split - 1) / p.pages_per_split;
-  p.part_bytes = (size_t)batch * hkv * p.n_splits * (16 * p.row_tiles) * (head_dim + 2) * sizeof(float);
+  p.n_splits = splits_of(p.shape);
+  p.part_bytes = (size_t)batch * hkv * p.n_splits * (8 * p.row_groups) * (head_dim + 2) * sizeof(float);
   return p;
 }
 
 hipError_t launch_decode(int v_fmt, int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
-  const bool q4 = v_fmt == KVQ_FMT_Q4_0_H256;
-  const int rt = plan.row_tiles;
-  if (q4) return rt == 1 ? launch_shape<256, 1, 2>(plan, a, s) : launch_shape<256, 2, 2>(plan, a, s);
+  if (v_fmt == KVQ_FMT_Q4_0_H256) return launch_shape<256, 1, 2>(plan, a, s);
   switch (D) {
-    case 64: return rt == 1 ? launch_shape<64, 1, 1>(plan, a, s) : launch_shape<64, 2, 1>(plan, a, s);
-    case 128: return rt == 1 ? launch_shape<128, 1, 1>(plan, a, s) : launch_shape<128, 2, 1>(plan, a, s);
-    case 256: return rt == 1 ? launch_shape<256, 1, 1>(plan, a, s) : launch_shape<256, 2, 1>(plan, a, s);
+    case 64: return launch_shape<64, 1, 1>(plan, a, s);
+    case 128: return launch_shape<128, 1, 1>(plan, a, s);
+    case 256: return launch_shape<256, 1, 1>(plan, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -268,6 +268,8 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const
   a.n_q_heads = n_q_heads;
   a.pages_per_split = plan.pages_per_split;
   a.n_splits = plan.n_splits;
+  a.row_groups = plan.row_groups;
+  a.row_alloc = 8 * plan.row_groups;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
   // the default grouping (explicit maps that coincide with it included) lets kernels skip the lists
   a.g_uniform = n_q_heads % cache->n_kv_heads == 0 ? n_q_heads / cache->n_kv_heads : 0;

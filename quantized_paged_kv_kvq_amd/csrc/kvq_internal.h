@@ -77,13 +77,16 @@ struct DecodeArgs {
   int n_splits;
   float scale_log2;         // sm_scale * log2(e)
   int g_uniform;            // G when query head h reads KV head h / G (the default map), else 0
+  int row_groups;           // workgroups per split: each takes 8 query rows of the KV head
+  int row_alloc;            // rows of the partials per (sequence, KV head): 8 * row_groups
   int16_t head_off[KVQ_MAX_Q_HEADS + 1];
   int16_t head_list[KVQ_MAX_Q_HEADS];
 };
 
 struct DecodePlan {
-  int row_tiles;        // 16-row MFMA column tiles per KV head (1 or 2)
-  bool dup;             // at most 8 rows: hi/lo weight parts share one MFMA (columns 0-7 / 8-15)
+  int shape;            // launch shape (waves, pages per wave, prefetch depth)
+  int rows;             // query rows of the widest KV head
+  int row_groups;       // groups of 8 query rows per KV head, one workgroup each per split
   int waves;            // waves per workgroup
   int pages_per_split;
   int n_splits;

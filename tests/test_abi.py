@@ -94,7 +94,7 @@ def test_decode_workspace_size_formula():
     L = kvq.lib()
     c = make_cache()
     n = L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 1, 16, None)
-    assert n == 2 * 128 * 16 * (256 + 2) * 4          # 2 KV heads x 128 splits x 16 rows x (D + m, l) fp32
+    assert n == 2 * 128 * 8 * (256 + 2) * 4           # 2 KV heads x 128 splits x 8 rows x (D + m, l) fp32
     assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 5, 16, None) == 0
 
 
