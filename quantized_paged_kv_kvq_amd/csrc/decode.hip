@@ -25,8 +25,8 @@
 //     (code + 128) -- 4-bit q4_0 code, value code - 8 -- with the offset removed at the end from
 //     the per-group sums of the weights.  Every MFMA tile of 16 head_dim rows lies inside one
 //     scale group, so one weight vector per group serves all its tiles.
-//   * The NW waves of a workgroup merge (m, l, O) through LDS; the workgroup writes one
-//     unnormalised partial.  A second kernel merges the splits with a log-sum-exp combine,
+//   * The NW waves of a workgroup merge (m, l, O) through LDS in one round (each wave merges and
+//     writes a share of the head_dim tiles); the workgroup writes one unnormalised partial.  A second kernel merges the splits with a log-sum-exp combine,
 //     normalises, applies H to k8v4 outputs and writes fp32 rows.
 #include "kvq_internal.h"
 #include "device_util.h"
@@ -178,12 +178,19 @@ __device__ __forceinline__ void load_page(PageBuf<D, VF>& pb, const DecodeArgs& 
   load_words<2 * NVG>(pb.vs, reinterpret_cast<const uint32_t*>(a.v_scales + (tile * 16 + 4 * j4) * NVG));
 }
 
+// q fragments (B operand of QK) in LDS, 64 lanes apart
+template <int NG>
+struct QLds {
+  const f16x8* p;
+  __device__ __forceinline__ f16x8 operator()(int rt, int g, int h) const { return p[((rt * NG + g) * 2 + h) * 64]; }
+};
+
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
 // DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the bf16 hi part of
 // the softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both.
-template <int D, int RT, int VF, bool DUP>
+template <int D, int RT, int VF, bool DUP, class QF>
 __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j4, bool lo_col, const int (&Lrow)[RT],
-                                          const f16x8* __restrict__ qf, const float (&qmul)[RT],
+                                          const QF& qf, const float (&qmul)[RT],
                                           float (&m_run)[RT], float (&l_run)[RT],
                                           float (&ls)[RT][VF == 1 ? D / 64 : D / 32], f32x4 (&O)[RT][D / 16]) {
   constexpr int NG = D / 64;
@@ -198,7 +205,7 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
     const f16x8 a1 = codes_to_f16(pb.k[g].z, pb.k[g].w);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const f16x8 b0 = qf[((rt * NG + g) * 2 + 0) * 64], b1 = qf[((rt * NG + g) * 2 + 1) * 64];
+      const f16x8 b0 = qf(rt, g, 0), b1 = qf(rt, g, 1);
       acc[rt][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
       acc[rt][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[rt][g], 0, 0, 0);
     }
@@ -389,6 +396,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   // order, so everything the prologue needs is issued before the page stream; the pages depend
   // only on page-table entries of this split (clamped to the table), not on lengths or rows, and a
   // page past the sequence's end is loaded but never processed.
+  const int* bt_row = a.bt + (size_t)b * a.max_pages;
+  const int p_begin = split * a.pages_per_split;
+  const int p0 = p_begin + wv;
+  const int p_cap = min(p_begin + a.pages_per_split, a.max_pages) - 1;
   uint4 raw[RT][NG][2];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -399,10 +410,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
       raw[rt][g][1] = *reinterpret_cast<const uint4*>(qp + 64 * g + 8);
     }
   }
-  const int* bt_row = a.bt + (size_t)b * a.max_pages;
-  const int p_begin = split * a.pages_per_split;
-  const int p0 = p_begin + wv;
-  const int p_cap = min(p_begin + a.pages_per_split, a.max_pages) - 1;
+  // LDS: q fragments (one copy for the workgroup: every wave holds the same rows), then the wave
+  // merge buffers
+  constexpr int kQBytes = RT * NG * 2 * 64 * 16;
+  constexpr int kMergeBytes = NW * RT * (NT * 64 * 16 + 2 * 64 * 4);
+  __shared__ __align__(16) uint8_t smem[kQBytes + kMergeBytes];
   PageBuf<D, VF> buf[PD + 1];
 #pragma unroll
   for (int i = 0; i < PD && i < PPW; ++i)
@@ -427,9 +439,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     return;
   }
 
-  // q fragments of this lane (B operand of QK) live in LDS: [wave][rt][g][half][lane] x 16 bytes
-  __shared__ f16x8 lds_q[NW * RT * NG * 2 * 64];
-  f16x8* qf = lds_q + wv * (RT * NG * 2 * 64) + lane;
+  // q fragments of this lane (B operand of QK) live in LDS: [rt][g][half][lane] x 16 bytes,
+  // written by wave 0
+  const QLds<NG> qlds{reinterpret_cast<const f16x8*>(smem) + lane};
   float qmul[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -458,7 +470,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
           f[2 * e] = (_Float16)ldexpf(bf16f(w[e] & 0xffffu), ex);
           f[2 * e + 1] = (_Float16)ldexpf(bf16f(w[e] >> 16), ex);
         }
-        qf[((rt * NG + g) * 2 + h) * 64] = f;
+        if (wv == 0) const_cast<f16x8*>(qlds.p)[((rt * NG + g) * 2 + h) * 64] = f;
       }
     qmul[rt] = ldexpf(a.scale_log2, -ex);
   }
@@ -482,6 +494,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   // exits only: every wait on the vector memory counter then covers exactly the page about to be
   // processed.  Prefetches past the wave's last page re-read that page (an L2 hit), so no branch
   // guards a load.
+  __syncthreads();                                          // q fragments written by wave 0
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;          // pages of this wave, >= 1
     const int p_last = p0 + (n_mine - 1) * NW;
@@ -491,7 +504,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
       if (i + PD < PPW)
         load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a,
                               clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1), kvh, lane);
-      page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qf, qmul, m_run, l_run, ls, O);
+      page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
       if (i + 1 >= n_mine) break;
     }
   }
@@ -509,54 +522,63 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     }
   }
 
-  // ---- merge the NW waves through LDS (halving rounds)
+  // ---- merge the NW waves.  Every wave stores (m, l, O) in LDS, then wave w merges and writes
+  // tiles w, w + NW, ... of all waves (int8 V); k8v4 needs whole rows for its Hadamard, so there
+  // wave 0 merges everything.
+  float* lds_o = reinterpret_cast<float*>(smem + kQBytes);           // [wave][rt][t][lane] x f32x4
+  float* lds_ml = lds_o + NW * RT * NT * 64 * 4;                      // [wave][rt][m | l][lane]
   if constexpr (NW > 1) {
-    __shared__ float lds_o[(NW / 2) * RT * NT * 4 * 64];
-    __shared__ float lds_ml[(NW / 2) * RT * 2 * 64];
 #pragma unroll
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-      if (wv >= half && wv < 2 * half) {
-        const int slot = wv - half;
+    for (int rt = 0; rt < RT; ++rt) {
+      if (VF == 1 || wv != 0) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) lds_o[(((slot * RT + rt) * NT + t) * 4 + k) * 64 + lane] = O[rt][t][k];
-          lds_ml[((slot * RT + rt) * 2 + 0) * 64 + lane] = m_run[rt];
-          lds_ml[((slot * RT + rt) * 2 + 1) * 64 + lane] = l_run[rt];
-        }
+        for (int t = 0; t < NT; ++t)
+          *reinterpret_cast<f32x4*>(lds_o + (((wv * RT + rt) * NT + t) * 64 + lane) * 4) = O[rt][t];
       }
-      __syncthreads();
-      if (wv < half) {
+      lds_ml[((wv * RT + rt) * 2 + 0) * 64 + lane] = m_run[rt];
+      lds_ml[((wv * RT + rt) * 2 + 1) * 64 + lane] = l_run[rt];
+    }
+    __syncthreads();
+    if (VF == 2 && wv != 0) return;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const float mo = lds_ml[((wv * RT + rt) * 2 + 0) * 64 + lane];
-          const float lo = lds_ml[((wv * RT + rt) * 2 + 1) * 64 + lane];
-          const float M = fmaxf(m_run[rt], mo);
-          const float Mu = M == kNegInf ? 0.0f : M;
-          const float c1 = __builtin_amdgcn_exp2f(m_run[rt] - Mu), c2 = __builtin_amdgcn_exp2f(mo - Mu);
-          m_run[rt] = M;
-          l_run[rt] = l_run[rt] * c1 + lo * c2;
+    for (int rt = 0; rt < RT; ++rt) {
+      float mv[NW], cv[NW];
+      float M = kNegInf;
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              O[rt][t][k] = O[rt][t][k] * c1 + lds_o[(((wv * RT + rt) * NT + t) * 4 + k) * 64 + lane] * c2;
-        }
+      for (int v = 0; v < NW; ++v) {
+        mv[v] = lds_ml[((v * RT + rt) * 2 + 0) * 64 + lane];
+        M = fmaxf(M, mv[v]);
       }
-      __syncthreads();
+      const float Mu = M == kNegInf ? 0.0f : M;
+      float l = 0.0f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        cv[v] = __builtin_amdgcn_exp2f(mv[v] - Mu);
+        l += cv[v] * lds_ml[((v * RT + rt) * 2 + 1) * 64 + lane];
+      }
+      m_run[rt] = M;
+      l_run[rt] = l;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (VF == 1 && t % NW != wv) continue;
+        f32x4 acc = VF == 1 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : O[rt][t] * cv[0];
+#pragma unroll
+        for (int v = (VF == 1 ? 0 : 1); v < NW; ++v)
+          acc += cv[v] * *reinterpret_cast<const f32x4*>(lds_o + (((v * RT + rt) * NT + t) * 64 + lane) * 4);
+        O[rt][t] = acc;
+      }
     }
   }
-  if (wv != 0) return;
   if constexpr (DUP) {            // column r + 8 holds the lo-part sums of row r: add them in
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
+      if (VF == 1 && NW > 1 && t % NW != wv) continue;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float x = O[0][t][k];
         O[0][t][k] = x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
       }
+    }
   }
   // k8v4: rotate the (unnormalised) partial back now; the combine is linear, so H commutes with it
   if constexpr (VF == 2) hadamard_rows<RT>(O, lane);
@@ -570,14 +592,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     auto put4 = [&](float* p, float x0, float x1, float x2, float x3) {
       *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
     };
-    if (j4 == 0) {
+    if (j4 == 0 && wv == 0) {
       float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
       ml[0] = m_run[rt]; ml[1] = l_run[rt];
     }
     if constexpr (VF == 1) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)   // lane holds d = 16t + 4*j4 + k
-        put4(row + 16 * t + 4 * j4, O[rt][t][0], O[rt][t][1], O[rt][t][2], O[rt][t][3]);
+        if (NW == 1 || t % NW == wv) put4(row + 16 * t + 4 * j4, O[rt][t][0], O[rt][t][1], O[rt][t][2], O[rt][t][3]);
     } else {
 #pragma unroll
       for (int g = 0; g < NVG; ++g) {  // tiles 2g (even d) / 2g+1 (odd d): d = 32g + 8*j4 + 2k (+1)
