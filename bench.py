@@ -3,7 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one pass of the hot path over the workload: quantize-on-write of the step's new K/V
-tokens into the paged cache, then decode (or MTP-verify) attention over the whole context.
+tokens into the paged cache and decode (or MTP-verify) attention over the whole context -- one
+fused launch sequence for int8 K and V (the decode kernel encodes the step's cells), otherwise an
+append launch followed by the decode (--unfused forces the latter).
 Default workload: one full-attention layer of a Qwen3.5-MoE-style model with int8 group-64 K and
 V at 131,072 tokens of context (GQA 16:2, head_dim 256, page size 16, seeded random page
 table).  Inputs are resident in HBM before the timed region.  The cache is replicated so that
@@ -11,10 +13,10 @@ consecutive steps read different copies whose total exceeds the 256 MB last-leve
 cache: every step streams its codes and scales from HBM.
 
 Prints ONE JSON line.  `value` is microseconds per step (lower is better); `roofline` reports
-the decode attention launch (split-K kernel + log-sum-exp combine, timed with HIP events on the
-stream it runs on, around batches of back-to-back launches) against the 8 TB/s HBM peak on its
-algorithmic bytes; `cpu_baseline` times
-the CPU oracle on a bounded sample of the same step.
+the decode attention launch (fused or plain split-K kernel + log-sum-exp combine, timed with HIP
+events on the stream it runs on, around batches of back-to-back launches) against the 8 TB/s HBM
+peak on its algorithmic bytes; `cpu_baseline` times the CPU oracle on a bounded sample of the
+same step.
 """
 from __future__ import annotations
 
@@ -53,15 +55,22 @@ def make_workload(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v):
+def algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v, fused=False):
     """Bytes one decode launch must move: every visible cell's codes and scales, the page-table
-    entries it walks, q in, out."""
+    entries it walks, q in, out; fused with quantize-on-write also the step's bf16 K/V in and its
+    cells' codes and scales out."""
     cells = int(np.sum(np.maximum(w.seq_lens, 0)))
     per_cell = w.n_kv_heads * ((cb_k + 2 * ns_k) + (cb_v + 2 * ns_v))
     pages = int(np.sum((w.seq_lens + w.page_size - 1) // w.page_size))
     q = w.batch * w.n_q * w.n_q_heads * w.head_dim * 2
     out = w.batch * w.n_q * w.n_q_heads * w.head_dim * 4
-    return cells * per_cell + pages * 4 + q + out
+    new = w.batch * w.n_step * (2 * w.n_kv_heads * w.head_dim * 2 + per_cell) if fused else 0
+    return cells * per_cell + pages * 4 + q + out + new
+
+
+def fusable(w):
+    """The step can run as one fused quantize-on-write + decode launch sequence."""
+    return w.fmt_k == "int8" and w.fmt_v == "int8" and w.n_step == w.n_q and 1 <= w.n_q <= 4
 
 
 def recorded_traffic(workload: str):
@@ -264,6 +273,8 @@ def main():
     ap.add_argument("--workload", default="moe_int8_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run quantize-on-write and decode as separate launches even where they can be fused")
     ap.add_argument("--replicas", type=int, default=0, help="cache copies to rotate (0 = enough to exceed the MALL)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run only a plain device copy of BYTES (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -313,15 +324,28 @@ def main():
     print(f"[bench] {R} cache replicas of {cache_bytes / 1e6:.1f} MB; warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
 
+    # int8 K and V: the step is one fused launch sequence (the step's cells are encoded inside the
+    # decode kernel); otherwise quantize-on-write, then decode.  The step's tokens are ordered by
+    # sequence, then position, which is the fused call's [batch][n_q] order.
+    fused = fusable(w) and not args.unfused
+
     def one_step(i, stream):
         c = caches[i % R]
+        if fused:
+            kvq.kvq_decode_attn_append(c, pages, s_k, s_v, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out,
+                                       workspace=ws, stream=stream)
+            return
         kvq.kvq_append(c, pages, s_k, s_v, s_seq, s_pos, stream=stream)
         kvq.kvq_decode_attn(c, pages, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out, workspace=ws, stream=stream)
 
     def decode_batch(stream):
         for i in range(R):
-            kvq.kvq_decode_attn(caches[i], pages, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out, workspace=ws,
-                                stream=stream)
+            if fused:
+                kvq.kvq_decode_attn_append(caches[i], pages, s_k, s_v, q, q_lens=q_lens, sm_scale=w.sm_scale,
+                                           out=out, workspace=ws, stream=stream)
+            else:
+                kvq.kvq_decode_attn(caches[i], pages, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out,
+                                    workspace=ws, stream=stream)
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -378,7 +402,7 @@ def main():
     torch.cuda.synchronize()
     dec_us = [a.elapsed_time(b) * 1e3 / per_batch for a, b in evs]
     dec_avg = float(np.mean(dec_us))
-    algo = algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v)
+    algo = algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v, fused)
     achieved = algo / (dec_avg * 1e-6) / 1e9
     print(f"[bench] {mode}: decode launch avg {dec_avg:.2f} us over {n_batches} x {per_batch} launches, step "
           f"{ms_per_step * 1e3:.2f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
@@ -404,11 +428,14 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "context": int(w.seq_lens.max()), "n_q": w.n_q,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "k_format": w.fmt_k, "v_format": w.fmt_v,
-                   "step": "append new K/V token(s) + decode attention", "cache_replicas": R,
+                   "step": ("quantize-on-write of the new K/V token(s) fused into decode attention" if fused
+                            else "append new K/V token(s), then decode attention"), "cache_replicas": R,
                    "launch": mode},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
-                     "kernel": "decode attention launch (split-K kernel + log-sum-exp combine kernel)",
+                     "kernel": ("fused quantize-on-write + decode attention launch (split-K kernel encoding "
+                                "the step's cells + log-sum-exp combine kernel)" if fused else
+                                "decode attention launch (split-K kernel + log-sum-exp combine kernel)"),
                      "launch_us": round(dec_avg, 3), "algorithmic_bytes": int(algo)},
         "cpu_baseline": cpu,
     }

@@ -182,6 +182,26 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
                            float sm_scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* A decode step in one launch: quantize-on-write of the step's tokens ([FT398] "What":
+ * decode tokens are quantised as they are written) and decode attention over the cache that
+ * includes them ([ST2698] "What it does").  Same result as kvq_append of the n_q new tokens
+ * of every sequence into cells seq_lens[b] - n_q .. seq_lens[b] - 1 followed by
+ * kvq_decode_attn with the same arguments: the cells are encoded exactly as kvq_append
+ * encodes them, written to the cache, and the attention reads them as stored.
+ *   k_new, v_new : device bf16 [batch][n_q][n_kv_heads][head_dim], 16-byte aligned; token t
+ *                  of sequence b goes to position seq_lens[b] - n_q + t
+ *   seq_lens     : already counts the new tokens (seq_lens[b] >= n_q)
+ * Other arguments, workspace and limits as for kvq_decode_attn (same workspace size).
+ * Requires INT8_G64 K and V stores and 1 <= n_q <= 4.  A page holding new cells must not
+ * be read by another sequence of the batch in the same call (pages written by a step are
+ * owned by their sequence). */
+kvq_status kvq_decode_attn_append(const kvq_cache* cache, const kvq_pages* pages,
+                                  const void* k_new, const void* v_new,
+                                  const void* q, int32_t n_q, int32_t n_q_heads,
+                                  const int32_t* q_lens, const int32_t* head_map,
+                                  float sm_scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes kvq_decode_attn needs for this geometry (0 on invalid arguments). */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages,
                                   int32_t n_q, int32_t n_q_heads, const int32_t* head_map);

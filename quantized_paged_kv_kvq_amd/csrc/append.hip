@@ -12,6 +12,7 @@
 //   ISO3       FreeToken PR #398, "What" (per 128 values: L2-normalise, rotate each 4-group by a
 //              unit quaternion, nearest 3-bit Lloyd-Max centroid, corrected norm).
 #include "kvq_internal.h"
+#include "int8_cell.h"
 
 namespace kvq {
 namespace {
@@ -47,8 +48,8 @@ __device__ __forceinline__ void locate(const AppendArgs& a, int tok, int& page, 
 }
 
 // ---------------------------------------------------------------------------------------------
-// INT8_G64.  One thread encodes 4 consecutive values; the 16 threads of a 64-group are 16
-// consecutive lanes, so the group max-abs is a 4-step xor-shuffle reduction (max is exact).
+// INT8_G64.  One thread encodes 4 consecutive values (int8_encode_x4); the 16 threads of a
+// 64-group are 16 consecutive lanes.
 __device__ __forceinline__ void append_int8(const AppendArgs& a, const uint16_t* __restrict__ x,
                                             uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int D,
                                             bool is_v, int block) {
@@ -65,20 +66,8 @@ __device__ __forceinline__ void append_int8(const AppendArgs& a, const uint16_t*
   const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * D + 4 * part);
   float v[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
                 bf16_to_f32(raw.y >> 16)};
-  float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  am = fmaxf(am, __shfl_xor(am, 8));
-  am = fmaxf(am, __shfl_xor(am, 4));
-  am = fmaxf(am, __shfl_xor(am, 2));
-  am = fmaxf(am, __shfl_xor(am, 1));
-  const float s = am / 127.0f;                     // binary32 scale; fp16 is only its storage
-
-  uint32_t packed = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    int q = 0;
-    if (am > 0.0f) q = (int)fminf(fmaxf(rintf(v[e] / s), -127.0f), 127.0f);
-    packed |= (uint32_t)(q & 0xff) << (8 * e);
-  }
+  const Int8x4 enc = int8_encode_x4(v);
+  const uint32_t packed = enc.packed;
   if (!active) return;
   int page, slot;
   locate(a, tok, page, slot);
@@ -91,7 +80,7 @@ __device__ __forceinline__ void append_int8(const AppendArgs& a, const uint16_t*
     for (int e = 0; e < 4; ++e) base[v_tile_offset(4 * part + e, slot)] = (uint8_t)(packed >> (8 * e));
   }
   if ((part & 15) == 0)
-    scales[(tile * KVQ_PAGE_SIZE + slot) * (D / 64) + (part >> 4)] = f32_to_f16_bits(am > 0.0f ? s : 0.0f);
+    scales[(tile * KVQ_PAGE_SIZE + slot) * (D / 64) + (part >> 4)] = enc.scale_bits;
 }
 
 // ---------------------------------------------------------------------------------------------

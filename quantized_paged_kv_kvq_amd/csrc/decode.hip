@@ -30,6 +30,7 @@
 //     normalises, applies H to k8v4 outputs and writes fp32 rows.
 #include "kvq_internal.h"
 #include "device_util.h"
+#include "int8_cell.h"
 
 namespace kvq {
 namespace {
@@ -184,6 +185,45 @@ struct QLds {
   const f16x8* p;
   __device__ __forceinline__ f16x8 operator()(int rt, int g, int h) const { return p[((rt * NG + g) * 2 + h) * 64]; }
 };
+
+// Device-scope loads of a page (int8 V): they miss the CU's L1 and read L2, so a page this wave
+// loaded, then wrote cells into (and waited for), comes back with them.
+__device__ __forceinline__ uint4 load_dev16(const void* base, uint32_t off) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0x10 /* sc1: device scope */);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int D>
+__device__ __forceinline__ void load_page_dev(PageBuf<D, 1>& pb, const DecodeArgs& a, int page, int kvh, int lane) {
+  constexpr int NG = D / 64;
+  const int i16 = lane & 15, j4 = lane >> 4;
+  const size_t tile = (size_t)page * a.hkv + kvh;
+  const uint8_t* kb = a.k_codes + tile * (16 * D);
+  const uint8_t* vb = a.v_codes + tile * (16 * D);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) pb.k[g] = load_dev16(kb, 16 * (64 * g + lane));
+#pragma unroll
+  for (int g = 0; g < NG; ++g) pb.v[g] = load_dev16(vb, 16 * (64 * g + 4 * i16 + j4));
+  const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scales + (tile * 16 + 4 * j4) * NG);
+  const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_scales + (tile * 16 + 4 * j4) * NG);
+#pragma unroll
+  for (int c = 0; c < 2 * NG; c += 4) {
+    if constexpr (NG >= 2) {
+      const uint4 k4 = load_dev16(ks, 4 * c), v4 = load_dev16(vs, 4 * c);
+      pb.ks[c] = k4.x; pb.ks[c + 1] = k4.y; pb.ks[c + 2] = k4.z; pb.ks[c + 3] = k4.w;
+      pb.vs[c] = v4.x; pb.vs[c + 1] = v4.y; pb.vs[c + 2] = v4.z; pb.vs[c + 3] = v4.w;
+    }
+  }
+  if constexpr (NG == 1) {
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ks), (short)0, 0x7fffffff, 0x00020000);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vs), (short)0, 0x7fffffff, 0x00020000);
+    pb.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, 0, 0, 0x10);
+    pb.ks[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4, 0, 0x10);
+    pb.vs[0] = __builtin_amdgcn_raw_buffer_load_b32(rv, 0, 0, 0x10);
+    pb.vs[1] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4, 0, 0x10);
+  }
+}
 
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
 // DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the bf16 hi part of
@@ -400,6 +440,37 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   const int p_begin = split * a.pages_per_split;
   const int p0 = p_begin + wv;
   const int p_cap = min(p_begin + a.pages_per_split, a.max_pages) - 1;
+  // the page ids of this wave in one vector load, lane i: page p0 + i * NW (clamped to the split
+  // and the table); the loads below take them with lane reads.  (Scalar loads of the table could
+  // not be used once the kernel also stores into the cache: the compiler cannot rule out that the
+  // stores change the table.)
+  const int my_ids = clampi(bt_row[min(p0 + min(lane, PPW - 1) * NW, p_cap)], 0, a.num_pages - 1);
+  // Fused quantize-on-write (int8 V only): new token t of this sequence goes to position
+  // seq_len - n_q + t.  The wave whose page list holds that cell loads the token now, encodes and
+  // stores it before the page loop and waits for the stores, so the loop's load of that page
+  // returns the cell; a page the prologue already loaded is loaded again (device scope, past the
+  // CU's L1).  Every row-group workgroup of the split stores the cell itself: the bytes are
+  // identical, and each reads back after its own store.
+  int fz_idx[kDecodeMaxFused], fz_slot[kDecodeMaxFused];   // page index in this wave's list (-1: not ours)
+  uint2 fz_x[kDecodeMaxFused][2];
+  int fz_mask = 0;                                          // bit i: page i of this wave has new cells
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxFused; ++t) {
+    fz_idx[t] = -1;
+    fz_slot[t] = 0;
+    if (VF == 1 && a.k_new && t < a.n_q) {
+      const int pos = clampi(seq_len - a.n_q + t, 0, cap - 1);
+      const int pl = pos / KVQ_PAGE_SIZE - p_begin;
+      if (pl >= 0 && pl < a.pages_per_split && pl % NW == wv) {
+        fz_idx[t] = pl / NW;
+        fz_slot[t] = pos % KVQ_PAGE_SIZE;
+        fz_mask |= 1 << fz_idx[t];
+        const size_t off = ((size_t)(b * a.n_q + t) * a.hkv + kvh) * D + 4 * min(lane, D / 4 - 1);
+        fz_x[t][0] = *reinterpret_cast<const uint2*>(a.k_new + off);
+        fz_x[t][1] = *reinterpret_cast<const uint2*>(a.v_new + off);
+      }
+    }
+  }
   uint4 raw[RT][NG][2];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -418,7 +489,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   PageBuf<D, VF> buf[PD + 1];
 #pragma unroll
   for (int i = 0; i < PD && i < PPW; ++i)
-    load_page<D, VF, NTL>(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, lane);
+    load_page<D, VF, NTL>(buf[i], a, __builtin_amdgcn_readlane(my_ids, i), kvh, lane);
 
   int Lmax = 0;
   for (int t = 0; t < a.n_q; ++t)
@@ -429,6 +500,41 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   const size_t row0 = (size_t)(b * a.hkv + kvh) * RA;
   float* part_ml = a.part;
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
+  // ---- encode this wave's new cells into the cache; pages of the prologue that hold one are
+  // loaded again once the stores have completed
+  if (fz_mask) {
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxFused; ++t) {
+      if (fz_idx[t] < 0) continue;
+      const size_t tile = (size_t)__builtin_amdgcn_readlane(my_ids, fz_idx[t]) * a.hkv + kvh;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const float x[4] = {bf16f(fz_x[t][kv].x & 0xffffu), bf16f(fz_x[t][kv].x >> 16),
+                            bf16f(fz_x[t][kv].y & 0xffffu), bf16f(fz_x[t][kv].y >> 16)};
+        const Int8x4 e = int8_encode_x4(x);
+        if (lane < D / 4) {
+          uint8_t* codes = const_cast<uint8_t*>(kv ? a.v_codes : a.k_codes) + tile * (KVQ_PAGE_SIZE * D);
+          uint16_t* scales = const_cast<uint16_t*>(kv ? a.v_scales : a.k_scales);
+          if (kv == 0) {
+            *reinterpret_cast<uint32_t*>(codes + k_tile_offset(4 * lane, fz_slot[t])) = e.packed;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) codes[v_tile_offset(4 * lane + q, fz_slot[t])] = (uint8_t)(e.packed >> (8 * q));
+          }
+          if ((lane & 15) == 0) scales[(tile * KVQ_PAGE_SIZE + fz_slot[t]) * NG + (lane >> 4)] = e.scale_bits;
+        }
+      }
+    }
+    // the stores complete before any later load of this wave (the page loop's loads of these pages)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (VF == 1) {
+#pragma unroll
+      for (int i = 0; i < PD && i < PPW; ++i)
+        if ((fz_mask >> i) & 1)
+          load_page_dev<D>(buf[i], a, __builtin_amdgcn_readlane(my_ids, i), kvh, lane);
+    }
+  }
+
   if (R == 0) return;
   if (p_begin >= p_end) {                                   // nothing visible in this split
     const int r = DUP ? 8 * rg + (int)threadIdx.x : (int)threadIdx.x;
@@ -497,13 +603,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   __syncthreads();                                          // q fragments written by wave 0
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;          // pages of this wave, >= 1
-    const int p_last = p0 + (n_mine - 1) * NW;
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       const int pc = p0 + i * NW;
       if (i + PD < PPW)
-        load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a,
-                              clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1), kvh, lane);
+        load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, __builtin_amdgcn_readlane(my_ids, min(i + PD, n_mine - 1)),
+                              kvh, lane);
       page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
       if (i + 1 >= n_mine) break;
     }

@@ -232,9 +232,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
   return plan.part_bytes;
 }
 
-kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, int32_t n_q,
-                           int32_t n_q_heads, const int32_t* q_lens, const int32_t* head_map, float sm_scale,
-                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, const void* k_new, const void* v_new,
+                              const void* q, int32_t n_q, int32_t n_q_heads, const int32_t* q_lens,
+                              const int32_t* head_map, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   kvq_status st;
   if ((st = check_pages(pages)) != KVQ_OK) return st;
   DecodeArgs a;
@@ -255,6 +256,8 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const
   a.v_codes = static_cast<const uint8_t*>(cache->v.codes);
   a.v_scales = static_cast<const uint16_t*>(cache->v.scales);
   a.q = static_cast<const uint16_t*>(q);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
   a.q_lens = q_lens;
   a.seq_lens = pages->seq_lens;
   a.bt = pages->block_table;
@@ -277,6 +280,32 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const
     if (a.head_list[h] != h || (h % a.g_uniform == 0 && a.head_off[h / a.g_uniform] != h)) a.g_uniform = 0;
   return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, static_cast<hipStream_t>(stream)),
                     "decode launch");
+}
+
+kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, int32_t n_q,
+                           int32_t n_q_heads, const int32_t* q_lens, const int32_t* head_map, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(cache, pages, nullptr, nullptr, q, n_q, n_q_heads, q_lens, head_map, sm_scale, out, workspace,
+                     workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attn_append(const kvq_cache* cache, const kvq_pages* pages, const void* k_new,
+                                  const void* v_new, const void* q, int32_t n_q, int32_t n_q_heads,
+                                  const int32_t* q_lens, const int32_t* head_map, float sm_scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  kvq_status st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if (cache->k.fmt != KVQ_FMT_INT8_G64 || cache->v.fmt != KVQ_FMT_INT8_G64)
+    return fail(KVQ_ERR_UNSUPPORTED, "fused append + decode needs INT8_G64 K and V stores (got formats %d / %d)",
+                cache->k.fmt, cache->v.fmt);
+  if (n_q < 1 || n_q > kDecodeMaxFused)
+    return fail(KVQ_ERR_UNSUPPORTED, "fused append + decode takes 1..%d new tokens per sequence (got %d)",
+                kDecodeMaxFused, n_q);
+  if (!k_new || !v_new) return fail(KVQ_ERR_NULL, "k_new or v_new is NULL");
+  if (((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15))
+    return fail(KVQ_ERR_SHAPE, "k_new and v_new must be 16-byte aligned");
+  return decode_impl(cache, pages, k_new, v_new, q, n_q, n_q_heads, q_lens, head_map, sm_scale, out, workspace,
+                     workspace_bytes, stream);
 }
 
 static kvq_status extend_setup(const kvq_cache* cache, int32_t batch, int32_t max_pages, int32_t n_new,

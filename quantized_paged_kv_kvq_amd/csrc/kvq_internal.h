@@ -81,7 +81,13 @@ struct DecodeArgs {
   int row_alloc;            // rows of the partials per (sequence, KV head): 8 * row_groups
   int16_t head_off[KVQ_MAX_Q_HEADS + 1];
   int16_t head_list[KVQ_MAX_Q_HEADS];
+  // fused quantize-on-write (INT8_G64 K and V): new token t of sequence b, bf16
+  // [batch][n_q][hkv][head_dim], is encoded into position seq_lens[b] - n_q + t before the
+  // attention reads it; nullptr: plain decode
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
+constexpr int kDecodeMaxFused = 4;     // new tokens per sequence of a fused decode
 
 struct DecodePlan {
   int shape;            // launch shape (waves, pages per wave, prefetch depth)

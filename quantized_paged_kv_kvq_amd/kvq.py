@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_append.argtypes = [cp, ip, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
         L.kvq_decode_attn.argtypes = [cp, ip, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_float, c_void_p,
                                       c_void_p, c_size_t, c_void_p]
+        L.kvq_decode_attn_append.argtypes = [cp, ip, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                             c_void_p, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
         L.kvq_decode_workspace_bytes.argtypes = [cp, c_int32, c_int32, c_int32, c_int32, c_void_p]
         L.kvq_decode_workspace_bytes.restype = c_size_t
         L.kvq_extend_attn.argtypes = [cp, ip, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
@@ -71,7 +73,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = c_int32
-        for name in ("kvq_append", "kvq_decode_attn", "kvq_extend_attn", "kvq_dequant_gather"):
+        for name in ("kvq_append", "kvq_decode_attn", "kvq_decode_attn_append", "kvq_extend_attn",
+                     "kvq_dequant_gather"):
             getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -207,6 +210,31 @@ def kvq_decode_attn(cache: PagedKVCache, pages: Pages, q: torch.Tensor, q_lens: 
                                  _ptr(q, torch.bfloat16, "q"), n_q, Hq, _ptr(q_lens, torch.int32, "q_lens"), hm,
                                  float(sm_scale), _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    del keep
+    return out
+
+
+def kvq_decode_attn_append(cache: PagedKVCache, pages: Pages, k_new: torch.Tensor, v_new: torch.Tensor,
+                           q: torch.Tensor, q_lens: Optional[torch.Tensor] = None, head_map=None,
+                           sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode step in one launch: k/v_new bf16 [batch][n_q][n_kv_heads][head_dim] go to positions
+    seq_lens[b] - n_q .. seq_lens[b] - 1, then attention as kvq_decode_attn."""
+    B, n_q, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = kvq_decode_workspace_bytes(cache, pages.batch, pages.max_pages, n_q, Hq, head_map)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    keep, hm = _head_map_arg(head_map)
+    _check(lib().kvq_decode_attn_append(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
+                                        _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+                                        _ptr(q, torch.bfloat16, "q"), n_q, Hq, _ptr(q_lens, torch.int32, "q_lens"),
+                                        hm, float(sm_scale), _ptr(out, torch.float32, "out"),
+                                        _ptr(workspace, None, "workspace"),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
     del keep
     return out
 

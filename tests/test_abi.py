@@ -23,7 +23,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = kvq.lib()
     names = declared_functions()
-    assert {"kvq_append", "kvq_decode_attn", "kvq_extend_attn", "kvq_dequant_gather"} <= set(names)
+    assert {"kvq_append", "kvq_decode_attn", "kvq_decode_attn_append", "kvq_extend_attn",
+            "kvq_dequant_gather"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     ver = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
@@ -88,6 +89,26 @@ def test_decode_validation_errors():
     c = make_cache()
     c.v = kvq.KvqStore(1, None, FAKE)
     assert decode(c, make_pages()) == 1
+
+
+def decode_append(c, p, n_q=1, hq=16, k=FAKE, v=FAKE, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    L = kvq.lib()
+    return L.kvq_decode_attn_append(ctypes.byref(c) if c else None, ctypes.byref(p) if p else None, k, v, q, n_q, hq,
+                                    None, None, 0.0625, out, ws, ws_bytes, None)
+
+
+def test_decode_append_validation_errors():
+    assert decode_append(None, make_pages()) == 1
+    assert decode_append(make_cache(fv=2), make_pages()) == 3           # fused path: int8 V only
+    assert decode_append(make_cache(fk=3, fv=3, D=128), make_pages()) == 3
+    assert decode_append(make_cache(), make_pages(), n_q=5, hq=4) == 3  # at most 4 new tokens per sequence
+    assert decode_append(make_cache(), make_pages(), n_q=0) == 3
+    assert decode_append(make_cache(), make_pages(), k=None) == 1
+    assert decode_append(make_cache(), make_pages(), v=None) == 1
+    assert decode_append(make_cache(), make_pages(), k=FAKE + 8) == 2   # misaligned
+    assert decode_append(make_cache(), make_pages(), q=None) == 1       # then the decode checks
+    assert decode_append(make_cache(), make_pages(), ws_bytes=16) == 4
+    assert decode_append(make_cache(), None) == 1
 
 
 def test_decode_workspace_size_formula():
