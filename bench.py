@@ -354,7 +354,10 @@ def main():
 
     # The launches of a step are captured in HIP graphs (one per cache copy) and replayed, so the
     # timed loop measures the GPU rather than the Python launch path; eager launches if capture fails.
-    graphs, dec_graph, mode = None, None, "eager"
+    # Steps are captured R to a graph, one per cache copy in order (as a model's decode graph holds
+    # its layers' attention launches back to back, with no host round trip between them), plus one
+    # graph per single step for a remainder of the K timed steps.
+    graphs, round_graph, dec_graph, mode = None, None, None, "eager"
     if not args.no_graph:
         try:
             graphs = []
@@ -363,25 +366,33 @@ def main():
                 with torch.cuda.graph(g):
                     one_step(r, torch.cuda.current_stream())
                 graphs.append(g)
+            round_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(round_graph):
+                for r in range(R):
+                    one_step(r, torch.cuda.current_stream())
             dec_graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(dec_graph):
                 decode_batch(torch.cuda.current_stream())
             for g in graphs:
                 g.replay()
+            round_graph.replay()
             dec_graph.replay()
             torch.cuda.synchronize()
             mode = "hip-graph"
         except Exception as e:  # noqa: BLE001
             print(f"[bench] graph capture unavailable ({e}); timing eager launches", file=sys.stderr, flush=True)
-            graphs, dec_graph = None, None
+            graphs, round_graph, dec_graph = None, None, None
     stream = torch.cuda.current_stream()
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % R].replay()
-        else:
+    if graphs:
+        for _ in range(args.steps // R):
+            round_graph.replay()
+        for i in range(args.steps % R):
+            graphs[i].replay()
+    else:
+        for i in range(args.steps):
             one_step(i, stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -430,7 +441,7 @@ def main():
                    "page_size": w.page_size, "k_format": w.fmt_k, "v_format": w.fmt_v,
                    "step": ("quantize-on-write of the new K/V token(s) fused into decode attention" if fused
                             else "append new K/V token(s), then decode attention"), "cache_replicas": R,
-                   "launch": mode},
+                   "launch": mode, "steps_per_graph": R if graphs else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
                      "kernel": ("fused quantize-on-write + decode attention launch (split-K kernel encoding "
