@@ -440,11 +440,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   const int p_begin = split * a.pages_per_split;
   const int p0 = p_begin + wv;
   const int p_cap = min(p_begin + a.pages_per_split, a.max_pages) - 1;
-  // the page ids of this wave in one vector load, lane i: page p0 + i * NW (clamped to the split
-  // and the table); the loads below take them with lane reads.  (Scalar loads of the table could
-  // not be used once the kernel also stores into the cache: the compiler cannot rule out that the
-  // stores change the table.)
-  const int my_ids = clampi(bt_row[min(p0 + min(lane, PPW - 1) * NW, p_cap)], 0, a.num_pages - 1);
+  // Page id of this wave's i-th page (clamped to the split and the table).  The int8 kernel,
+  // which may store new cells, reads the ids of all its pages in one vector load at entry and
+  // takes them with lane reads: once a kernel stores to global memory the compiler can no longer
+  // prove the table unchanged, and scalar loads of it would become vector loads each waited for
+  // with vmcnt(0).  The k8v4 kernel stores nothing and loads each id with a scalar load.
+  int my_ids = 0;
+  if constexpr (VF == 1) my_ids = clampi(bt_row[min(p0 + min(lane, PPW - 1) * NW, p_cap)], 0, a.num_pages - 1);
+  auto page_id = [&](int i) -> int {          // i: index in this wave's page list, uniform
+    if constexpr (VF == 1) return __builtin_amdgcn_readlane(my_ids, i);
+    else return clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1);
+  };
   // Fused quantize-on-write (int8 V only): new token t of this sequence goes to position
   // seq_len - n_q + t.  The wave whose page list holds that cell loads the token now, encodes and
   // stores it before the page loop and waits for the stores, so the loop's load of that page
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   PageBuf<D, VF> buf[PD + 1];
 #pragma unroll
   for (int i = 0; i < PD && i < PPW; ++i)
-    load_page<D, VF, NTL>(buf[i], a, __builtin_amdgcn_readlane(my_ids, i), kvh, lane);
+    load_page<D, VF, NTL>(buf[i], a, page_id(i), kvh, lane);
 
   int Lmax = 0;
   for (int t = 0; t < a.n_q; ++t)
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   // ---- encode this wave's new cells into the cache; pages of the prologue that hold one are
   // loaded again once the stores have completed
-  if (fz_mask) {
+  if (VF == 1 && fz_mask) {
 #pragma unroll
     for (int t = 0; t < kDecodeMaxFused; ++t) {
       if (fz_idx[t] < 0) continue;
@@ -603,12 +609,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   __syncthreads();                                          // q fragments written by wave 0
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;          // pages of this wave, >= 1
+    const int p_last = p0 + (n_mine - 1) * NW;
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       const int pc = p0 + i * NW;
-      if (i + PD < PPW)
-        load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, __builtin_amdgcn_readlane(my_ids, min(i + PD, n_mine - 1)),
-                              kvh, lane);
+      if (i + PD < PPW) {
+        int page;
+        if constexpr (VF == 1) page = page_id(min(i + PD, n_mine - 1));
+        else page = clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1);
+        load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page, kvh, lane);
+      }
       page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
       if (i + 1 >= n_mine) break;
     }
