@@ -28,7 +28,7 @@ UNITS = {
     "kvq_api.hip": [],
     "append.hip": ["-ffp-contract=off"],
     "gather.hip": ["-ffp-contract=off"],
-    "decode.hip": [],
+    "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
     "extend.hip": [],
 }
 

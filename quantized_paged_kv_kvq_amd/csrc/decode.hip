@@ -225,6 +225,8 @@ __device__ __forceinline__ void load_page_dev(PageBuf<D, 1>& pb, const DecodeArg
   }
 }
 
+constexpr float kLazyLog2 = 8.0f;     // weights stay below 2^8 between rescalings
+
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
 // DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the bf16 hi part of
 // the softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both.
@@ -236,6 +238,14 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
   constexpr int NG = D / 64;
   constexpr int NVG = VF == 1 ? D / 64 : D / 32;
   constexpr int NT = D / 16;
+  // k8v4 with more than 8 rows (verify windows; 16 rows per row tile, no duplicated columns):
+  // V enters the MFMA as the exact product (code - 8) x scale in two bf16 parts (a 4-bit code
+  // times an fp16 scale has at most 15 significant bits; the hi part keeps 8, the lo part the
+  // remaining 7), built once per page for all row tiles, and the softmax weights are split into
+  // hi / lo once per row tile instead of once per 32-value scale group.  The lo x lo product
+  // (below 2^-16 of the term) is left out.
+  constexpr bool Q4A = VF == 2 && !DUP;
+  s16x4 bqh[RT], bql[RT];
 
   // ---- QK: S^T[token 4*j4 + k][row] per 64-group
   f32x4 acc[RT][NG];
@@ -262,20 +272,33 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
       for (int g = 1; g < NG; ++g) v = fmaf(acc[rt][g][k], pb.kscale(k, g), v);
       s[k] = (tok0 + k < Lrow[rt]) ? v * qmul[rt] : kNegInf;
     }
+    // Lazy rescaling: the exponentials are taken against a reference max m_run that moves only
+    // when a score exceeds it by more than kLazyLog2 (so every weight stays below 2^kLazyLog2),
+    // not on every increase of the running max; O and l are rescaled only then, and not at all
+    // while they are still zero.  The partial's (m, l, O) all refer to m_run, which is all the
+    // log-sum-exp combine needs.
     const float mx = max_over_row_lanes(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-    const float m_new = fmaxf(m_run[rt], mx);
+    const bool move = mx > m_run[rt] + kLazyLog2;
+    const float m_new = move ? mx : m_run[rt];
     const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
+    const bool rescale = move && m_run[rt] != kNegInf;
+    const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run[rt] - m_use) : 1.0f;
     m_run[rt] = m_new;
     float pk[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_use);
     l_run[rt] = l_run[rt] * alpha + ((pk[0] + pk[1]) + (pk[2] + pk[3]));
-    if (__any(alpha != 1.0f)) {
+    if (__any(rescale)) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) O[rt][t] *= alpha;
+      if constexpr (!Q4A) {
 #pragma unroll
-      for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
+        for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
+      }
+    }
+    if constexpr (Q4A) {
+      split_bf16(pk, bqh[rt], bql[rt]);
+      continue;
     }
 
     // ---- PV per V scale group
@@ -325,6 +348,47 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
         O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, O[rt][2 * g], 0, 0, 0);
         O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bhi, O[rt][2 * g + 1], 0, 0, 0);
         O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, O[rt][2 * g + 1], 0, 0, 0);
+      }
+    }
+  }
+  if constexpr (Q4A) {
+#pragma unroll
+    for (int g = 0; g < NVG; ++g) {
+      // byte k of the word: token 4*j4 + k; its low / high nibble: head_dim 32g + 2*i16 (+1)
+      const uint32_t w = word_of(pb.v[g >> 2], g & 3);
+      float sc[4], off[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sc[k] = pb.vscale(k, g);
+        off[k] = -8.0f * sc[k];
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = fmaf((float)((nib >> (8 * k)) & 0xffu), sc[k], off[k]);   // exact
+          hb[k] = __float_as_uint(x) & 0xffff0000u;
+          lb[k] = __float_as_uint(x - __uint_as_float(hb[k]));                    // exact, low half 0
+        }
+        const s16x4 ahi = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                                                               __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)));
+        const s16x4 alo = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                                                               __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)));
+        // the three products as two K = 32 MFMAs: lane k-block j4 carries tokens 4*j4 .. +3 twice,
+        // [V hi | V lo] x [w hi | w hi], then [V hi | V hi] x [w lo | 0]
+        const uint2 hu = __builtin_bit_cast(uint2, ahi), lu = __builtin_bit_cast(uint2, alo);
+        const bf16x8 a2 = __builtin_bit_cast(bf16x8, u32x4{hu.x, hu.y, lu.x, lu.y});
+        const bf16x8 a3 = __builtin_bit_cast(bf16x8, u32x4{hu.x, hu.y, hu.x, hu.y});
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint2 bu = __builtin_bit_cast(uint2, bqh[rt]), bl = __builtin_bit_cast(uint2, bql[rt]);
+          const bf16x8 b2 = __builtin_bit_cast(bf16x8, u32x4{bu.x, bu.y, bu.x, bu.y});
+          const bf16x8 b3 = __builtin_bit_cast(bf16x8, u32x4{bl.x, bl.y, 0u, 0u});
+          O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, O[rt][2 * g + e], 0, 0, 0);
+          O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, b3, O[rt][2 * g + e], 0, 0, 0);
+        }
       }
     }
   }
@@ -393,13 +457,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   constexpr float kOff = VF == 1 ? 128.0f : 136.0f;         // bias carried by the V A-operand
   const int RA = a.row_alloc;                               // allocated rows per (sequence, KV head)
 
-  // wave-uniform wave index: page ids then come through scalar loads, which do not wait on the
-  // vector-memory counter that tracks the prefetched page
+  // wave-uniform wave index: page addresses are scalar arithmetic
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, j4 = lane >> 4;
   // blockIdx.x -> (split, row group) so that the row groups of a split share blockIdx.x % 8, i.e.
-  // run on the same XCD (workgroups are dealt to the 8 XCDs round robin) and share its L2
-  const int n_rg = a.row_groups;
+  // run on the same XCD (workgroups are dealt to the 8 XCDs round robin) and share its L2.
+  // Without duplicated columns one workgroup holds all rows (RT row tiles of 16).
+  const int n_rg = DUP ? a.row_groups : 1;
   const int xg = blockIdx.x, rem = xg % (8 * n_rg);
   const int rg = rem >> 3, split = (xg / (8 * n_rg)) * 8 + (rem & 7);
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -424,7 +488,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   const int seq_len = clampi(a.seq_lens[b], 0, cap);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = DUP ? 8 * rg + (i16 & 7) : 16 * rt + i16;
+    const int r = DUP ? 8 * (rg + rt) + (i16 & 7) : 16 * rt + i16;
     valid[rt] = r < R;
     const int t = valid[rt] ? r / G : 0;
     const int i = valid[rt] ? r % G : 0;
@@ -490,7 +554,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   // LDS: q fragments (one copy for the workgroup: every wave holds the same rows), then the wave
   // merge buffers
   constexpr int kQBytes = RT * NG * 2 * 64 * 16;
-  constexpr int kMergeBytes = NW * RT * (NT * 64 * 16 + 2 * 64 * 4);
+  constexpr int kMergeBytes = NW * (NT * 64 * 16 + 2 * 64 * 4);   // one row tile at a time
   __shared__ __align__(16) uint8_t smem[kQBytes + kMergeBytes];
   PageBuf<D, VF> buf[PD + 1];
 #pragma unroll
@@ -544,7 +608,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   if (R == 0) return;
   if (p_begin >= p_end) {                                   // nothing visible in this split
     const int r = DUP ? 8 * rg + (int)threadIdx.x : (int)threadIdx.x;
-    if ((int)threadIdx.x < (DUP ? 8 : RA) && r < RA) {
+    if ((int)threadIdx.x < (DUP ? 8 * RT : RA) && r < RA) {
       float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
       ml[0] = kNegInf; ml[1] = 0.0f;
     }
@@ -624,44 +688,45 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     }
   }
 
-  // ---- per-wave totals: row sums over the 4 lane groups; remove the V operand bias
+  // ---- per-wave totals: row sums over the 4 lane groups; remove the V operand bias (the exact
+  // code x scale operand of k8v4 with several row tiles carries none)
+  constexpr bool Q4A = VF == 2 && !DUP;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     l_run[rt] = sum_over_row_lanes(l_run[rt]);
+    if constexpr (!Q4A) {
 #pragma unroll
-    for (int g = 0; g < NVG; ++g) ls[rt][g] = sum_over_row_lanes(ls[rt][g]);
+      for (int g = 0; g < NVG; ++g) ls[rt][g] = sum_over_row_lanes(ls[rt][g]);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int g = VF == 1 ? t / 4 : t / 2;
-      O[rt][t] -= kOff * ls[rt][g];
+      for (int t = 0; t < NT; ++t) {
+        const int g = VF == 1 ? t / 4 : t / 2;
+        O[rt][t] -= kOff * ls[rt][g];
+      }
     }
   }
 
-  // ---- merge the NW waves.  Every wave stores (m, l, O) in LDS, then wave w merges and writes
-  // tiles w, w + NW, ... of all waves (int8 V); k8v4 needs whole rows for its Hadamard, so there
-  // wave 0 merges everything.
-  float* lds_o = reinterpret_cast<float*>(smem + kQBytes);           // [wave][rt][t][lane] x f32x4
-  float* lds_ml = lds_o + NW * RT * NT * 64 * 4;                      // [wave][rt][m | l][lane]
+  // ---- merge the NW waves, one row tile at a time.  Every wave stores (m, l, O) in LDS, then
+  // wave w merges tiles w, w + NW, ... of all waves (int8 V); k8v4 needs whole rows for its
+  // Hadamard, so there wave 0 merges everything.
+  float* lds_o = reinterpret_cast<float*>(smem + kQBytes);           // [wave][t][lane] x f32x4
+  float* lds_ml = lds_o + NW * NT * 64 * 4;                           // [wave][m | l][lane]
   if constexpr (NW > 1) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+      if (rt > 0) __syncthreads();                          // the previous row tile is merged
       if (VF == 1 || wv != 0) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          *reinterpret_cast<f32x4*>(lds_o + (((wv * RT + rt) * NT + t) * 64 + lane) * 4) = O[rt][t];
+        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(lds_o + ((wv * NT + t) * 64 + lane) * 4) = O[rt][t];
       }
-      lds_ml[((wv * RT + rt) * 2 + 0) * 64 + lane] = m_run[rt];
-      lds_ml[((wv * RT + rt) * 2 + 1) * 64 + lane] = l_run[rt];
-    }
-    __syncthreads();
-    if (VF == 2 && wv != 0) return;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+      lds_ml[(wv * 2 + 0) * 64 + lane] = m_run[rt];
+      lds_ml[(wv * 2 + 1) * 64 + lane] = l_run[rt];
+      __syncthreads();
+      if (VF == 2 && wv != 0) continue;
       float mv[NW], cv[NW];
       float M = kNegInf;
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
-        mv[v] = lds_ml[((v * RT + rt) * 2 + 0) * 64 + lane];
+        mv[v] = lds_ml[(v * 2 + 0) * 64 + lane];
         M = fmaxf(M, mv[v]);
       }
       const float Mu = M == kNegInf ? 0.0f : M;
@@ -669,7 +734,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
         cv[v] = __builtin_amdgcn_exp2f(mv[v] - Mu);
-        l += cv[v] * lds_ml[((v * RT + rt) * 2 + 1) * 64 + lane];
+        l += cv[v] * lds_ml[(v * 2 + 1) * 64 + lane];
       }
       m_run[rt] = M;
       l_run[rt] = l;
@@ -679,21 +744,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
         f32x4 acc = VF == 1 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : O[rt][t] * cv[0];
 #pragma unroll
         for (int v = (VF == 1 ? 0 : 1); v < NW; ++v)
-          acc += cv[v] * *reinterpret_cast<const f32x4*>(lds_o + (((v * RT + rt) * NT + t) * 64 + lane) * 4);
+          acc += cv[v] * *reinterpret_cast<const f32x4*>(lds_o + ((v * NT + t) * 64 + lane) * 4);
         O[rt][t] = acc;
       }
     }
+    if (VF == 2 && wv != 0) return;
   }
   if constexpr (DUP) {            // column r + 8 holds the lo-part sums of row r: add them in
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (VF == 1 && NW > 1 && t % NW != wv) continue;
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x = O[0][t][k];
-        O[0][t][k] = x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+      for (int t = 0; t < NT; ++t) {
+        if (VF == 1 && NW > 1 && t % NW != wv) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = O[rt][t][k];
+          O[rt][t][k] = x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+        }
       }
-    }
   }
   // k8v4: rotate the (unnormalised) partial back now; the combine is linear, so H commutes with it
   if constexpr (VF == 2) hadamard_rows<RT>(O, lane);
@@ -701,7 +769,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   // ---- write the workgroup's partial for rows r < R
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = DUP ? 8 * rg + i16 : 16 * rt + i16;
+    const int r = DUP ? 8 * (rg + rt) + i16 : 16 * rt + i16;
     if (r >= R || (DUP && i16 >= 8)) continue;
     float* row = part_o + ((row0 + r) * a.n_splits + split) * D;
     auto put4 = [&](float* p, float x0, float x1, float x2, float x3) {
@@ -830,13 +898,22 @@ __global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int 
 template <int D, int RT, int VF, int SH>
 hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   constexpr Shape sh = kShapes[SH];
-  // with several row groups the splits are padded to a multiple of 8 (see the blockIdx mapping)
-  const int gx = plan.row_groups == 1 ? plan.n_splits : (plan.n_splits + 7) / 8 * 8 * plan.row_groups;
+  // with several row-group workgroups per split (duplicated columns, 8 rows each) the splits are
+  // padded to a multiple of 8 (see the blockIdx mapping); a workgroup holding all rows in row
+  // tiles of 16 needs one wave per SIMD's registers
+  const bool groups = plan.row_tiles == 0 && plan.row_groups > 1;
+  const int gx = groups ? (plan.n_splits + 7) / 8 * 8 * plan.row_groups : plan.n_splits;
   const dim3 grid((unsigned)gx, a.hkv, a.batch), block(sh.nw * 64);
-  if (plan.row_groups == 1)
-    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, true><<<grid, block, 0, s>>>(a);
-  else
-    k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, false><<<grid, block, 0, s>>>(a);
+  if (plan.row_tiles > 0) {
+    if constexpr (VF == 2)
+      k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, 1, false, true><<<grid, block, 0, s>>>(a);
+    else
+      return hipErrorInvalidValue;
+  } else if (!groups) {
+    k_decode_split<D, 1, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, true><<<grid, block, 0, s>>>(a);
+  } else {
+    k_decode_split<D, 1, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, false><<<grid, block, 0, s>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid((D / 64) * plan.rows, a.hkv, a.batch);
@@ -848,7 +925,9 @@ template <int D, int RT, int VF>
 hipError_t launch_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   switch (plan.shape) {
     case 1: return launch_t<D, RT, VF, 1>(plan, a, s);
-    case 2: return launch_t<D, RT, VF, 2>(plan, a, s);
+    case 2:                                   // 8 waves: not with several row tiles (LDS)
+      if constexpr (RT == 1) return launch_t<D, RT, VF, 2>(plan, a, s);
+      else return launch_t<D, RT, VF, 0>(plan, a, s);
     default: return launch_t<D, RT, VF, 0>(plan, a, s);
   }
 }
@@ -857,19 +936,24 @@ hipError_t launch_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t
 
 int decode_max_splits() { return kMaxSplits; }
 
-DecodePlan plan_decode(int head_dim, int hkv, int batch, int max_pages, int max_rows) {
+DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_pages, int max_rows) {
   DecodePlan p{};
   // up to 8 query rows per KV head share one MFMA (weights' hi parts in columns 0-7, lo parts in
-  // 8-15); more rows take one workgroup per group of 8 rows
+  // 8-15); more rows take one workgroup per group of 8 rows, except with a k8v4 V store, where
+  // one workgroup holds up to 4 row groups (its V operand is built once per page for all rows)
   p.rows = max_rows;
   p.row_groups = max(1, (max_rows + 7) / 8);
-  // 64-page splits (16 pages per wave, two in flight) unless that leaves CUs without a workgroup;
-  // then 32-page splits
+  p.row_tiles = (v_fmt == KVQ_FMT_Q4_0_H256 && max_rows > 8) ? (max_rows + 15) / 16 : 0;
+  // 64-page splits (16 pages per wave, two in flight) unless they fill at most about half of the
+  // CUs; then 32-page splits (twice the workgroups, one page in flight).  Measured: 64-page splits
+  // win at 90% of the CUs (232 workgroups, 31.5 vs 33.5 us), 32-page splits at 50% (128, 22.7 vs
+  // 28.7 us).
   auto splits_of = [&](int sh) { return (max_pages + kShapes[sh].nw * kShapes[sh].ppw - 1) / (kShapes[sh].nw * kShapes[sh].ppw); };
   p.shape = shape_override();
   if (p.shape < 0) {
     p.shape = 0;
-    if ((long)splits_of(0) * hkv * batch * p.row_groups < device_cu_count()) p.shape = 1;
+    if ((long)splits_of(0) * hkv * batch * (p.row_tiles ? 1 : p.row_groups) * 20 <= (long)device_cu_count() * 11)
+      p.shape = 1;
   }
   const Shape sh = kShapes[p.shape];
   p.waves = sh.nw;
@@ -880,7 +964,8 @@ DecodePlan plan_decode(int head_dim, int hkv, int batch, int max_pages, int max_
 }
 
 hipError_t launch_decode(int v_fmt, int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
-  if (v_fmt == KVQ_FMT_Q4_0_H256) return launch_shape<256, 1, 2>(plan, a, s);
+  if (v_fmt == KVQ_FMT_Q4_0_H256)
+    return plan.row_tiles == 2 ? launch_shape<256, 2, 2>(plan, a, s) : launch_shape<256, 1, 2>(plan, a, s);
   switch (D) {
     case 64: return launch_shape<64, 1, 1>(plan, a, s);
     case 128: return launch_shape<128, 1, 1>(plan, a, s);

@@ -217,7 +217,7 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if ((long)n_q * max_g > KVQ_MAX_ROWS_PER_KV_HEAD)
     return fail(KVQ_ERR_UNSUPPORTED, "n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
                 KVQ_MAX_ROWS_PER_KV_HEAD);
-  *plan = plan_decode(D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
+  *plan = plan_decode(cache->v.fmt, D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
   if (plan->n_splits > decode_max_splits())
     return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d needs %d context splits; decode supports %d", max_pages,
                 plan->n_splits, decode_max_splits());

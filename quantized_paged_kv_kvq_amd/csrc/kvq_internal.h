@@ -92,14 +92,16 @@ constexpr int kDecodeMaxFused = 4;     // new tokens per sequence of a fused dec
 struct DecodePlan {
   int shape;            // launch shape (waves, pages per wave, prefetch depth)
   int rows;             // query rows of the widest KV head
-  int row_groups;       // groups of 8 query rows per KV head, one workgroup each per split
+  int row_groups;       // groups of 8 query rows per KV head
+  int row_tiles;        // 0: one workgroup per row group of 8 (duplicated columns); else one
+                        // workgroup per split holds all rows in this many row tiles of 16
   int waves;            // waves per workgroup
   int pages_per_split;
   int n_splits;
   size_t part_bytes;
 };
 
-DecodePlan plan_decode(int head_dim, int hkv, int batch, int max_pages, int max_rows);
+DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const DecodeArgs& a,
                          hipStream_t s);
 

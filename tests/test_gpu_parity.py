@@ -154,6 +154,16 @@ def test_verify_k8v4_scaled():
     check_decode(synth.k8v4_verify(ctx=2500, seed=36))
 
 
+@pytest.mark.parametrize("n_q,hq,hkv", [(2, 16, 2), (3, 8, 2), (4, 16, 2), (1, 12, 1)])
+def test_verify_k8v4_row_tiles(n_q, hq, hkv):
+    """k8v4 with more than 8 rows per KV head: one workgroup per split holds all rows in row tiles
+    of 16 (16, 12, 32 and 12 rows), V entering the MFMA as code x scale in two bf16 parts."""
+    back = list(range(n_q - 1, -1, -1))
+    w = synth.ragged_decode("int8", "q4h", [700, 33, 4000], seed=60 + n_q + hq, n_q=n_q, q_len_back=back,
+                            n_q_heads=hq, n_kv_heads=hkv, head_dim=256)
+    check_decode(w)
+
+
 def test_decode_k8v4_single_query():
     check_decode(synth.ragged_decode("int8", "q4h", [1000, 33], seed=37, n_q_heads=16, n_kv_heads=2, head_dim=256))
 
