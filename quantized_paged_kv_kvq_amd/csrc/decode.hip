@@ -364,7 +364,8 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
+        uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
+        asm volatile("" : "+v"(nib));         // keep the 4 codes as bytes: one byte-to-float each
         uint32_t hb[4], lb[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
