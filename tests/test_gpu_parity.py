@@ -178,6 +178,24 @@ def test_decode_outlier_peaked_attention():
     check_decode(w)
 
 
+@pytest.mark.parametrize("fmt_v,n_q", [("int8", 1), ("q4h", 3)])
+def test_decode_rising_scores_move_the_reference_max(fmt_v, n_q):
+    """Scores that rise along the context (steadily, and with jumps of more than 2^8 in weight
+    inside a page) make the softmax reference max move many times: exercises the rescaling of O
+    and l that is skipped while scores stay within 2^8 of the reference."""
+    L = 3000
+    w = synth.ragged_decode("int8", fmt_v, [L], seed=40 + n_q, n_q=n_q, n_q_heads=16, n_kv_heads=2, head_dim=256)
+    k = bf16_to_f32(w.k[0]).copy()
+    q = bf16_to_f32(w.q)
+    qdir = q[0, :, :8].mean(axis=(0, 1))                     # direction of KV head 0's queries
+    qdir /= np.linalg.norm(qdir)
+    ramp = np.linspace(0.0, 120.0, L, dtype=np.float32)
+    ramp[1500:] += 80.0                                      # a jump inside page 93
+    k[:, 0, :] += ramp[:, None] * qdir[None, :]
+    w.k[0] = synth.bf16_bits(k)
+    check_decode(w)
+
+
 def test_decode_deterministic():
     w = synth.moe_int8_decode(ctx=5000, seed=39)
     _, _, a = run_decode(w)
