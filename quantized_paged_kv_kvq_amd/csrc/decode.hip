@@ -37,8 +37,11 @@ namespace {
 
 // Launch shapes: waves per workgroup, pages per wave per split (a split is NW * PPW pages), pages
 // each wave keeps in flight ahead of the one it processes, and waves per SIMD the registers allow.
+// The last shape serves only the k8v4 row-tile kernel (one wave per SIMD), whose long page step
+// hides the load of the next page without a second one in flight.
 struct Shape { int nw, ppw, pd, occ; };
-constexpr Shape kShapes[] = {{4, 16, 2, 2}, {4, 8, 1, 2}, {8, 8, 1, 2}};
+constexpr Shape kShapes[] = {{4, 16, 2, 2}, {4, 8, 1, 2}, {8, 8, 1, 2}, {4, 16, 1, 2}};
+constexpr int kRowTileShape = 3;
 constexpr int kNumShapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
 
 // KVQ_DECODE_SHAPE overrides the choice (for tuning); -1 when unset
@@ -929,6 +932,9 @@ hipError_t launch_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t
     case 2:                                   // 8 waves: not with several row tiles (LDS)
       if constexpr (RT == 1) return launch_t<D, RT, VF, 2>(plan, a, s);
       else return launch_t<D, RT, VF, 0>(plan, a, s);
+    case kRowTileShape:
+      if constexpr (VF == 2) return launch_t<D, RT, VF, kRowTileShape>(plan, a, s);
+      else return launch_t<D, RT, VF, 0>(plan, a, s);
     default: return launch_t<D, RT, VF, 0>(plan, a, s);
   }
 }
@@ -948,14 +954,18 @@ DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_page
   // 64-page splits (16 pages per wave, two in flight) unless they fill at most about half of the
   // CUs; then 32-page splits (twice the workgroups, one page in flight).  Measured: 64-page splits
   // win at 90% of the CUs (232 workgroups, 31.5 vs 33.5 us), 32-page splits at 50% (128, 22.7 vs
-  // 28.7 us).
+  // 28.7 us).  The row-tile kernel takes its 64-page splits with one page in flight (66 vs 68 us
+  // for 3 query tokens x 8 query heads per KV head over 118750 cached tokens).
   auto splits_of = [&](int sh) { return (max_pages + kShapes[sh].nw * kShapes[sh].ppw - 1) / (kShapes[sh].nw * kShapes[sh].ppw); };
   p.shape = shape_override();
   if (p.shape < 0) {
     p.shape = 0;
     if ((long)splits_of(0) * hkv * batch * (p.row_tiles ? 1 : p.row_groups) * 20 <= (long)device_cu_count() * 11)
       p.shape = 1;
+    else if (p.row_tiles)
+      p.shape = kRowTileShape;
   }
+  if (p.shape == kRowTileShape && !p.row_tiles) p.shape = 0;
   const Shape sh = kShapes[p.shape];
   p.waves = sh.nw;
   p.pages_per_split = sh.nw * sh.ppw;

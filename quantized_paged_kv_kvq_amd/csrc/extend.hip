@@ -12,11 +12,12 @@
 //     are free of bank conflicts, plus the per-key norms.  Prefix tiles come from the
 //     ISO3 cells (the dequantisation runs once per cell, not once per query tile); chunk tiles from
 //     the bf16 tokens.
-//   * k_extend_attn: one workgroup = 4 waves = one (sequence, KV head, 4 * T query tokens) tile; a
+//   * k_extend_attn: one workgroup = 8 waves = one (sequence, KV head, 8 * T query tokens) tile; a
 //     wave owns 32 query rows (T tokens x G_pad query heads), the 32 columns of 32x32x16 MFMA
 //     tiles: lane l holds row l % 32 and, per 32-key block, 16 of its scores.  Tile images stream
-//     into LDS with direct global-to-LDS loads (no registers), double-buffered, one barrier per
-//     tile; two workgroups share a CU so that one's softmax overlaps the other's MFMAs.
+//     into LDS with direct global-to-LDS loads (no registers) through a ring of three buffers.
+//     The waves form two groups of 4 that run one barrier phase apart, so that one group's
+//     softmax overlaps the other group's MFMAs (one workgroup per CU).
 //
 // Prefix phase (rotated basis).  An ISO3 key is k = n * conj(r) (x) c with c the centroid values of
 // its codes, so <q, k> = n * <r (x) q, c>: the query is rotated once, the codes are used as they
