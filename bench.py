@@ -52,6 +52,10 @@ def make_workload(name: str):
         return synth.tiny_int8_decode()
     if name == "iso3_extend":
         return synth.iso3_extend()
+    if name == "batched_iso3_decode":
+        return synth.batched_iso3_decode()
+    if name == "moe_iso3_decode":
+        return synth.moe_iso3_decode(ctx=131072)
     raise SystemExit(f"unknown workload {name}")
 
 

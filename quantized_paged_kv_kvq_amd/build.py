@@ -29,6 +29,7 @@ UNITS = {
     "append.hip": ["-ffp-contract=off"],
     "gather.hip": ["-ffp-contract=off"],
     "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+    "decode_iso3.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
     "extend.hip": [],
 }
 

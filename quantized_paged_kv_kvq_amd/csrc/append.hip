@@ -12,6 +12,7 @@
 //   ISO3       FreeToken PR #398, "What" (per 128 values: L2-normalise, rotate each 4-group by a
 //              unit quaternion, nearest 3-bit Lloyd-Max centroid, corrected norm).
 #include "kvq_internal.h"
+#include "iso3_levels.h"
 #include "int8_cell.h"
 
 namespace kvq {
@@ -152,11 +153,6 @@ __device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* 
 // ISO3.  One wave per 128-value block; lane l holds elements l and l + 64, so the pairwise
 // halving sum (upper half onto lower half: spans 64, 32, ..., 1) is an in-lane add followed by
 // xor-shuffles 32 .. 1.
-constexpr double kSqrt128 = 11.3137084989847603904135327140;
-__constant__ float kCentroid[8] = {
-    (float)(-2.1520 / kSqrt128), (float)(-1.3440 / kSqrt128), (float)(-0.7560 / kSqrt128),
-    (float)(-0.2451 / kSqrt128), (float)(0.2451 / kSqrt128),  (float)(0.7560 / kSqrt128),
-    (float)(1.3440 / kSqrt128),  (float)(2.1520 / kSqrt128)};
 
 __device__ __forceinline__ float halving_sum128(float lo, float hi) {
   float s = lo + hi;
@@ -177,10 +173,10 @@ __device__ __forceinline__ float hamilton(int comp, float w, float x, float y, f
 
 __device__ __forceinline__ int nearest_centroid(float r) {
   int best = 0;
-  float bd = fabsf(r - kCentroid[0]);
+  float bd = fabsf(r - kIsoLevels[0]);
 #pragma unroll
   for (int k = 1; k < 8; ++k) {
-    const float dk = fabsf(r - kCentroid[k]);
+    const float dk = fabsf(r - kIsoLevels[k]);
     if (dk < bd) { bd = dk; best = k; }
   }
   return best;
@@ -214,7 +210,7 @@ __device__ __forceinline__ void append_iso3(const AppendArgs& a, const uint16_t*
   const float r0 = rotate_component(u0, lane, qw, qx, qy, qz);
   const float r1 = rotate_component(u1, lane, qw, qx, qy, qz);
   const int c0 = nearest_centroid(r0), c1 = nearest_centroid(r1);
-  const float k0 = kCentroid[c0], k1 = kCentroid[c1];
+  const float k0 = kIsoLevels[c0], k1 = kIsoLevels[c1];
   const float cn = sqrtf(halving_sum128(k0 * k0, k1 * k1));
   const float norm = n / cn;
 

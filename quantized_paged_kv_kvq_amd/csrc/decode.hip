@@ -899,6 +899,13 @@ __global__ __launch_bounds__(256) void k_decode_combine(const DecodeArgs a, int 
 }
 
 
+template <int D>
+hipError_t launch_combine_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+  dim3 cgrid((D / 64) * plan.rows, a.hkv, a.batch);
+  k_decode_combine<D><<<cgrid, dim3(256), 0, s>>>(a, a.row_alloc);
+  return hipGetLastError();
+}
+
 template <int D, int RT, int VF, int SH>
 hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   constexpr Shape sh = kShapes[SH];
@@ -920,9 +927,7 @@ hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid((D / 64) * plan.rows, a.hkv, a.batch);
-  k_decode_combine<D><<<cgrid, dim3(256), 0, s>>>(a, a.row_alloc);
-  return hipGetLastError();
+  return launch_combine_t<D>(plan, a, s);
 }
 
 template <int D, int RT, int VF>
@@ -972,6 +977,15 @@ DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_page
   p.n_splits = splits_of(p.shape);
   p.part_bytes = (size_t)batch * hkv * p.n_splits * (8 * p.row_groups) * (head_dim + 2) * sizeof(float);
   return p;
+}
+
+hipError_t launch_decode_combine(int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_combine_t<64>(plan, a, s);
+    case 128: return launch_combine_t<128>(plan, a, s);
+    case 256: return launch_combine_t<256>(plan, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode(int v_fmt, int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {

@@ -36,6 +36,7 @@
 // Online softmax in base 2 per row across both phases; the row max is shared by the 4 lanes that
 // hold a row's keys, the running sums stay per lane until the end.
 #include "kvq_internal.h"
+#include "iso3_levels.h"
 #include "device_util.h"
 
 namespace kvq {
@@ -51,13 +52,6 @@ constexpr int kImgV = kD * kVRow;                          // V image bytes: [d]
 constexpr int kNormOff = kImgK + kImgV;                    // fp32 K norms [64], then V norms / S [64]
 static_assert(kNormOff + 2 * kKeys * 4 <= kExtendTileBytes, "tile image layout");
 static_assert(kExtendTileBytes % 1024 == 0, "a tile image is whole kilobytes");
-constexpr float kLevelScale = 1.2495174407958984f;         // S: S * c is within 2^-15.9 of fp16 for all 8 levels
-
-constexpr double kSqrt128 = 11.3137084989847603904135327140;
-__constant__ float kLevels[8] = {
-    (float)(-2.1520 / kSqrt128), (float)(-1.3440 / kSqrt128), (float)(-0.7560 / kSqrt128),
-    (float)(-0.2451 / kSqrt128), (float)(0.2451 / kSqrt128),  (float)(0.7560 / kSqrt128),
-    (float)(1.3440 / kSqrt128),  (float)(2.1520 / kSqrt128)};
 
 // Byte offsets inside a tile image: 16-byte chunk c (head_dim 8c .. 8c+7) of key k, and 16-byte
 // chunk c (key positions 8c .. 8c+7) of head_dim row d.  The 16-byte row padding makes the 16 rows
@@ -122,7 +116,7 @@ __global__ __launch_bounds__(256) void k_extend_stage(const ExtendArgs a) {
       s.raw[0][i] = reinterpret_cast<const uint32_t*>(a.k_codes + cell * 48)[w];
       s.raw[1][i] = reinterpret_cast<const uint32_t*>(a.v_codes + cell * 48)[w];
     }
-    if (tid < 8) s.level[tid] = __builtin_bit_cast(uint16_t, (_Float16)(kLevelScale * kLevels[tid]));
+    if (tid < 8) s.level[tid] = __builtin_bit_cast(uint16_t, (_Float16)(kIsoLevelScale * kIsoLevels[tid]));
     if (tid < 4) { s.raw[0][kKeys * 12 + tid] = 0u; s.raw[1][kKeys * 12 + tid] = 0u; }
     if (tid < kKeys) {
       const int pos = t * kKeys + tid;
@@ -132,7 +126,7 @@ __global__ __launch_bounds__(256) void k_extend_stage(const ExtendArgs a) {
       const size_t cell = ((size_t)page * a.hkv + kvh) * KVQ_PAGE_SIZE + (pc & 15);
       float* norms = reinterpret_cast<float*>(s.img + kNormOff);
       norms[tid] = live ? h2f(a.k_norms[cell]) : 0.0f;
-      norms[kKeys + tid] = live ? h2f(a.v_norms[cell]) * (1.0f / kLevelScale) : 0.0f;
+      norms[kKeys + tid] = live ? h2f(a.v_norms[cell]) * (1.0f / kIsoLevelScale) : 0.0f;
     }
     __syncthreads();
     {   // K image: thread = (key, 32 head_dim values)
@@ -592,7 +586,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_extend_attn(const ExtendArgs
 
 }  // namespace
 
-float extend_level_scale() { return kLevelScale; }
+float extend_level_scale() { return kIsoLevelScale; }
 
 hipError_t launch_extend(const ExtendArgs& a, int tiles_per_seq, hipStream_t s) {
   k_extend_stage<<<dim3((unsigned)(a.pt_max + a.nt_max), (unsigned)a.hkv, (unsigned)a.batch), dim3(256), 0, s>>>(a);

@@ -9,6 +9,7 @@
 //              binary32 butterflies of spans 1..128 and a final x 1/16
 //   ISO3       conj(q) * centroid group (left to right), then times the norm
 #include "kvq_internal.h"
+#include "iso3_levels.h"
 
 namespace kvq {
 namespace {
@@ -91,11 +92,6 @@ __global__ __launch_bounds__(256) void k_gather_q4h(GatherArgs g, const uint8_t*
   if (active) store4(out, ((size_t)i * g.hkv + head) * 256 + 4 * lane, y, dtype);
 }
 
-constexpr double kSqrt128 = 11.3137084989847603904135327140;
-__constant__ float kCentroidG[8] = {
-    (float)(-2.1520 / kSqrt128), (float)(-1.3440 / kSqrt128), (float)(-0.7560 / kSqrt128),
-    (float)(-0.2451 / kSqrt128), (float)(0.2451 / kSqrt128),  (float)(0.7560 / kSqrt128),
-    (float)(1.3440 / kSqrt128),  (float)(2.1520 / kSqrt128)};
 
 // ISO3: one thread per 4-value group; the group's 12 code bits start at bit 12*g of its block.
 __global__ __launch_bounds__(256) void k_gather_iso3(GatherArgs g, const uint8_t* __restrict__ codes,
@@ -116,8 +112,8 @@ __global__ __launch_bounds__(256) void k_gather_iso3(GatherArgs g, const uint8_t
   const int bit = 12 * gi;
   const uint32_t w16 = (uint32_t)cb[bit >> 3] | ((uint32_t)cb[(bit >> 3) + 1] << 8);
   const uint32_t bits = w16 >> (bit & 7);
-  const float a = kCentroidG[bits & 7], b = kCentroidG[(bits >> 3) & 7], c = kCentroidG[(bits >> 6) & 7],
-              d = kCentroidG[(bits >> 9) & 7];
+  const float a = kIsoLevels[bits & 7], b = kIsoLevels[(bits >> 3) & 7], c = kIsoLevels[(bits >> 6) & 7],
+              d = kIsoLevels[(bits >> 9) & 7];
   // conjugate quaternion (w, -x, -y, -z), same evaluation order as the encoder's product
   const float w = qw, x = -qx, y = -qy, z = -qz;
   const float r0 = ((w * a - x * b) - y * c) - z * d;

@@ -96,6 +96,9 @@ kvq_status build_head_lists(int hq, int hkv, const int32_t* head_map, int16_t* o
     if (g > *max_g) *max_g = g;
   }
   off[hkv] = (int16_t)pos;
+  // entries past the list are read (never used) for KV heads that serve no query head: keep them a
+  // valid head index
+  for (int i = pos; i < KVQ_MAX_Q_HEADS; ++i) list[i] = 0;
   return KVQ_OK;
 }
 
@@ -201,11 +204,15 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->k.fmt, cache->head_dim, false)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->v.fmt, cache->head_dim, true)) != KVQ_OK) return st;
-  if (cache->k.fmt != KVQ_FMT_INT8_G64)
-    return fail(KVQ_ERR_UNSUPPORTED, "decode needs an INT8_G64 K store (got format %d)", cache->k.fmt);
-  if (cache->v.fmt == KVQ_FMT_ISO3)
-    return fail(KVQ_ERR_UNSUPPORTED, "decode over an ISO3 V store is not provided; use INT8_G64 or Q4_0_H256");
+  const bool iso = cache->k.fmt == KVQ_FMT_ISO3 && cache->v.fmt == KVQ_FMT_ISO3;
+  if (!iso && cache->k.fmt != KVQ_FMT_INT8_G64)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode needs an INT8_G64 K store or ISO3 K and V stores (got formats %d / %d)",
+                cache->k.fmt, cache->v.fmt);
+  if (!iso && cache->v.fmt == KVQ_FMT_ISO3)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode over an ISO3 V store needs an ISO3 K store");
   const int D = cache->head_dim;
+  if (iso && D != 128 && D != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "ISO3 decode supports head_dim 128 or 256 (got %d)", D);
   if (D != 64 && D != 128 && D != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "decode supports head_dim 64, 128 or 256 (got %d)", D);
   if (batch < 1 || batch > 65535) return fail(KVQ_ERR_SHAPE, "batch %d out of range", batch);
@@ -217,7 +224,11 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if ((long)n_q * max_g > KVQ_MAX_ROWS_PER_KV_HEAD)
     return fail(KVQ_ERR_UNSUPPORTED, "n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
                 KVQ_MAX_ROWS_PER_KV_HEAD);
-  *plan = plan_decode(cache->v.fmt, D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
+  if (iso && (long)n_q * max_g > kIsoDecodeMaxRows)
+    return fail(KVQ_ERR_UNSUPPORTED, "ISO3 decode: n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
+                kIsoDecodeMaxRows);
+  *plan = iso ? plan_decode_iso3(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
+              : plan_decode(cache->v.fmt, D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
   if (plan->n_splits > decode_max_splits())
     return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d needs %d context splits; decode supports %d", max_pages,
                 plan->n_splits, decode_max_splits());
@@ -274,12 +285,15 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   a.row_groups = plan.row_groups;
   a.row_alloc = 8 * plan.row_groups;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  for (int e = 0; e < 4; ++e) a.quat[e] = cache->iso_quat[e];
   // the default grouping (explicit maps that coincide with it included) lets kernels skip the lists
   a.g_uniform = n_q_heads % cache->n_kv_heads == 0 ? n_q_heads / cache->n_kv_heads : 0;
   for (int h = 0; h < n_q_heads && a.g_uniform; ++h)
     if (a.head_list[h] != h || (h % a.g_uniform == 0 && a.head_off[h / a.g_uniform] != h)) a.g_uniform = 0;
-  return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, static_cast<hipStream_t>(stream)),
-                    "decode launch");
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (cache->k.fmt == KVQ_FMT_ISO3)
+    return hip_status(launch_decode_iso3(cache->head_dim, plan, a, hs), "decode launch");
+  return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, hs), "decode launch");
 }
 
 kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, int32_t n_q,

@@ -86,8 +86,10 @@ struct DecodeArgs {
   // attention reads it; nullptr: plain decode
   const uint16_t* k_new;
   const uint16_t* v_new;
+  float quat[4];            // ISO3 stores: the rotation quaternion (w, x, y, z)
 };
 constexpr int kDecodeMaxFused = 4;     // new tokens per sequence of a fused decode
+constexpr int kIsoDecodeMaxRows = 16;  // query rows per KV head of an ISO3 decode
 
 struct DecodePlan {
   int shape;            // launch shape (waves, pages per wave, prefetch depth)
@@ -104,6 +106,11 @@ struct DecodePlan {
 DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const DecodeArgs& a,
                          hipStream_t s);
+// the log-sum-exp combine of the split partials (every decode kernel writes the same layout)
+hipError_t launch_decode_combine(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
+// ISO3 K and V stores (head_dim 128 or 256, at most kIsoDecodeMaxRows rows per KV head)
+DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int max_rows);
+hipError_t launch_decode_iso3(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 
 // Extend over an ISO3 prefix: one row per (new token, query head); rows of KV head j use the query
 // heads head_list[head_off[j] .. head_off[j+1]).

@@ -167,6 +167,40 @@ def batched_int8_decode(seed: int = 3, n_seqs: int = 32, len_lo: int = 4096, len
                     PAGE_SIZE, lens, table, npages, ks, vs, q)
 
 
+def batched_iso3_decode(seed: int = 6, n_seqs: int = 32, len_lo: int = 4096, len_hi: int = 32768,
+                        n_q_heads: int = 32, n_kv_heads: int = 8, head_dim: int = 128) -> Workload:
+    """batched_int8_decode's shapes over ISO3 K and V stores (one seeded rotation quaternion)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(len_lo, len_hi, size=n_seqs, endpoint=True).astype(np.int32)
+    table, npages = _page_table(rng, lens, PAGE_SIZE, identity=False)
+    q = normal_bf16(rng, (n_seqs, 1, n_q_heads, head_dim))
+    ks, vs = [], []
+    for b in range(n_seqs):
+        sub = np.random.default_rng(seed * 1000 + b)
+        ks.append(normal_bf16(sub, (int(lens[b]), n_kv_heads, head_dim)))
+        vs.append(normal_bf16(sub, (int(lens[b]), n_kv_heads, head_dim)))
+    quat = random_quaternion(seed + 1000)
+    return Workload("batched_iso3_decode", "iso3", "iso3", n_seqs, n_q_heads, n_kv_heads, head_dim,
+                    PAGE_SIZE, lens, table, npages, ks, vs, q, quat=quat)
+
+
+def moe_iso3_decode(ctx: int = 131072, seed: int = 7, n_q_heads: int = 16, n_kv_heads: int = 2,
+                    head_dim: int = 256, n_outliers: int = 4) -> Workload:
+    """moe_int8_decode's layer (GQA 16:2, head_dim 256, K outlier channels x20) over ISO3 K and V."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([ctx], np.int32)
+    table, npages = _page_table(rng, lens, PAGE_SIZE, identity=False)
+    outliers = np.sort(rng.choice(head_dim, size=n_outliers, replace=False)) if n_outliers else []
+    k = normal_bf16(rng, (ctx, n_kv_heads, head_dim), outlier_channels=outliers)
+    v = normal_bf16(rng, (ctx, n_kv_heads, head_dim))
+    q = normal_bf16(rng, (1, 1, n_q_heads, head_dim))
+    quat = random_quaternion(seed + 1000)
+    w = Workload("moe_iso3_decode", "iso3", "iso3", 1, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
+                 lens, table, npages, [k], [v], q, quat=quat)
+    w.meta["outlier_channels"] = [int(c) for c in outliers]
+    return w
+
+
 def k8v4_verify(ctx: int = 118750, seed: int = 4, n_q: int = 3, n_q_heads: int = 16,
                 n_kv_heads: int = 2, head_dim: int = 256) -> Workload:
     """int8 K + Hadamard-rotated q4_0 V; an MTP verify window of ``n_q`` query tokens whose

@@ -73,7 +73,10 @@ def test_decode_validation_errors():
     assert decode(make_cache(), None) == 1
     assert decode(make_cache(page=8), make_pages()) == 3
     assert decode(make_cache(fk=2), make_pages()) == 3                 # q4_0 K refused
-    assert decode(make_cache(fk=3, fv=3, D=128), make_pages()) == 3     # ISO3 decode not provided
+    assert decode(make_cache(fk=3, fv=1, D=128), make_pages()) == 3     # ISO3 K needs an ISO3 V store
+    assert decode(make_cache(fk=1, fv=3, D=128), make_pages()) == 3     # and ISO3 V an ISO3 K store
+    assert decode(make_cache(fk=3, fv=3, D=128), make_pages(), n_q=3) == 3    # ISO3: 24 rows > 16
+    assert decode(make_cache(fk=3, fv=3, D=384), make_pages()) == 3     # ISO3 decode: head_dim 128 or 256
     assert decode(make_cache(D=100), make_pages()) == 3                 # int8 needs head_dim % 64
     assert decode(make_cache(fv=2, D=128), make_pages()) == 3           # Hadamard V needs 256
     assert decode(make_cache(), make_pages(), hq=15) == 2               # Hq % Hkv
@@ -117,6 +120,10 @@ def test_decode_workspace_size_formula():
     n = L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 1, 16, None)
     assert n == 2 * 128 * 8 * (256 + 2) * 4           # 2 KV heads x 128 splits x 8 rows x (D + m, l) fp32
     assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 5, 16, None) == 0
+    iso = make_cache(fk=3, fv=3, D=128)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (128 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 2, 16, None) == 2 * 128 * 16 * (128 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 3, 16, None) == 0
 
 
 def test_append_and_gather_validation_errors():

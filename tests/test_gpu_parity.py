@@ -139,6 +139,12 @@ def test_decode_edge_lengths_and_head_map():
     check_decode(w, head_map=hm)
 
 
+def test_decode_last_kv_head_idle():
+    """The last KV head serves no query head (its workgroups find no rows)."""
+    w = synth.ragged_decode("int8", "int8", [70, 300], seed=71, n_q_heads=4, n_kv_heads=3, head_dim=128)
+    check_decode(w, head_map=[0, 1, 0, 1])
+
+
 def test_decode_mha_and_mqa():
     check_decode(synth.ragged_decode("int8", "int8", [200, 45], seed=33, n_q_heads=4, n_kv_heads=4, head_dim=128))
     check_decode(synth.ragged_decode("int8", "int8", [513], seed=34, n_q_heads=16, n_kv_heads=1, head_dim=128))
