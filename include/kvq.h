@@ -175,7 +175,9 @@ kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages,
  *   workspace: device, >= kvq_decode_workspace_bytes(...) bytes, 256-byte aligned.
  * Requires n_q * (largest number of query heads of one KV head) <= 32, head_dim 64,
  * 128 or 256, and a K store of format INT8_G64 (the V store may be INT8_G64 or
- * Q4_0_H256). */
+ * Q4_0_H256); or ISO3 K and V stores ([FT398] "Pull request overview": the ISO backend's
+ * decode attention over packed cells) with head_dim 128 or 256 and n_q * (largest number
+ * of query heads of one KV head) <= 16.  ISO3 outputs are in the original basis. */
 kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
                            const void* q, int32_t n_q, int32_t n_q_heads,
                            const int32_t* q_lens, const int32_t* head_map,

@@ -1,6 +1,8 @@
 // Split-K decode / verify attention over ISO3 K and V stores.
 //
-// FreeToken PR #398, "What": an ISO3 cell holds, per 128-value block, the 3-bit codes of the block's
+// FreeToken PR #398, "Pull request overview": the ISO backend attends decode tokens over the packed
+// cells with its own kernel ("What": decode tokens are quantised as they are written), checked
+// against attention over the dequantised cells ("Correctness").  "What": an ISO3 cell holds, per 128-value block, the 3-bit codes of the block's
 // unit vector after every 4-value group was rotated by one unit quaternion r, and the block's norm
 // n.  A key block is k = n * conj(r) (x) c group by group (c: the level values of its codes), so its
 // score is <q, k> = n * <r (x) q, c>: the query is rotated once per workgroup and the codes enter
@@ -46,9 +48,27 @@ constexpr float kPScale = 1.0f / 512.0f;
 constexpr int kBufFlags = 0x00020000;           // buffer resource word 3 (raw 32-bit data)
 constexpr int kNonTemporal = 2;                 // streaming loads: each cell is read once
 
-// Launch shapes: waves per workgroup, pages per wave per split, pages each wave keeps in flight.
-struct IsoShape { int nw, ppw, pd; };
-constexpr IsoShape kIsoShapes[] = {{4, 16, 2}, {4, 8, 1}};
+// Launch shapes: waves per workgroup, pages per wave per split, pages each wave keeps in flight
+// with head_dim 128 (half as many with head_dim 256, whose pages are twice as large), waves per SIMD
+// the registers allow.  Measured on 32 sequences of 4K-32K tokens (head_dim 128): 2 pages in flight
+// at 4 waves per SIMD beat 4, 6 or 8 pages at 2-3 waves per SIMD (the kernel is bound by its VALU
+// work per page, not by memory latency).
+struct IsoShape { int nw, ppw, pd, occ; };
+constexpr IsoShape kIsoShapes[] = {{4, 16, 2, 2}, {4, 8, 1, 2}};
+constexpr int kNumIsoShapes = (int)(sizeof(kIsoShapes) / sizeof(kIsoShapes[0]));
+
+// KVQ_ISO3_DECODE_SHAPE overrides the choice (for tuning); -1 when unset
+int iso_shape_override() {
+  static int idx = -2;
+  if (idx == -2) {
+    idx = -1;
+    if (const char* e = getenv("KVQ_ISO3_DECODE_SHAPE")) {
+      const int v = atoi(e);
+      if (v >= 0 && v < kNumIsoShapes) idx = v;
+    }
+  }
+  return idx;
+}
 
 // Hamilton product a (x) u of quaternions (w, x, y, z).
 __device__ __forceinline__ void quat_mul(const float a[4], const float u[4], float o[4]) {
@@ -218,8 +238,8 @@ __device__ __forceinline__ void iso_page_step(const IsoPage<D / 128>& pb, int p,
   }
 }
 
-template <int D, bool DUP, int NW, int PPW, int PD>
-__global__ __launch_bounds__(NW * 64, 2) void k_decode_iso3(const DecodeArgs a) {
+template <int D, bool DUP, int NW, int PPW, int PD, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a) {
   constexpr int NB = D / 128;
   constexpr int NT = D / 16;                        // PV tiles of 16 head_dim rows
   constexpr int NTG = NT / 4;                       // groups of 4 tiles: 4 consecutive head_dim per lane
@@ -426,15 +446,19 @@ __global__ __launch_bounds__(NW * 64, 2) void k_decode_iso3(const DecodeArgs a) 
 template <int D, bool DUP, int SH>
 hipError_t launch_iso3_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   constexpr IsoShape sh = kIsoShapes[SH];
-  k_decode_iso3<D, DUP, sh.nw, sh.ppw, sh.pd><<<dim3((unsigned)plan.n_splits, a.hkv, a.batch), dim3(sh.nw * 64), 0, s>>>(a);
+  constexpr int pd = D == 128 ? sh.pd : (sh.pd + 1) / 2;
+  k_decode_iso3<D, DUP, sh.nw, sh.ppw, pd, sh.occ>
+      <<<dim3((unsigned)plan.n_splits, a.hkv, a.batch), dim3(sh.nw * 64), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine(D, plan, a, s);
 }
 
-template <int D, bool DUP>
+template <int D, bool DUP, int SH = 0>
 hipError_t launch_iso3_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
-  return plan.shape == 1 ? launch_iso3_t<D, DUP, 1>(plan, a, s) : launch_iso3_t<D, DUP, 0>(plan, a, s);
+  if constexpr (SH + 1 < kNumIsoShapes)
+    if (plan.shape != SH) return launch_iso3_shape<D, DUP, SH + 1>(plan, a, s);
+  return launch_iso3_t<D, DUP, SH>(plan, a, s);
 }
 
 }  // namespace
@@ -449,7 +473,8 @@ DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int
     const int pps = kIsoShapes[sh].nw * kIsoShapes[sh].ppw;
     return (max_pages + pps - 1) / pps;
   };
-  p.shape = ((long)splits_of(0) * hkv * batch * 20 <= (long)device_cu_count() * 11) ? 1 : 0;
+  p.shape = iso_shape_override();
+  if (p.shape < 0) p.shape = ((long)splits_of(0) * hkv * batch * 20 <= (long)device_cu_count() * 11) ? 1 : 0;
   p.waves = kIsoShapes[p.shape].nw;
   p.pages_per_split = kIsoShapes[p.shape].nw * kIsoShapes[p.shape].ppw;
   p.n_splits = splits_of(p.shape);
