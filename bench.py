@@ -56,6 +56,8 @@ def make_workload(name: str):
         return synth.batched_iso3_decode()
     if name == "moe_iso3_decode":
         return synth.moe_iso3_decode(ctx=131072)
+    if name == "moe_q4h_decode":
+        return synth.moe_q4h_decode(ctx=131072)
     raise SystemExit(f"unknown workload {name}")
 
 

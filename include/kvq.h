@@ -45,6 +45,11 @@
  *                                 (attention contracts V over tokens: 4 consecutive slots of one
  *                                 code byte form a 32-bit word, and the words of code bytes c,
  *                                 c+16, c+32, c+48 form one 16-byte unit);
+ *     Q4_0_H256 K store           (((c / 64) * 4 + (c / 4) % 4) * 16 + t) * 16
+ *                                 + ((c / 16) % 4) * 4 + c % 4
+ *                                 (attention contracts K over head_dim in 32-value scale groups:
+ *                                 one 16-byte unit holds, for slot t, bytes 4w .. 4w+3 of four
+ *                                 consecutive groups; a wave load covers a contiguous kilobyte);
  *     ISO3 store (K or V)         t * code_bytes + c   (token-major).
  *   Every fp16 scale in the slabs must be finite, including those of slots no append has
  *   written yet (zero-initialise new slabs): attention weighs cells past a sequence's length
@@ -60,14 +65,15 @@
  *                     -127, 127) with the binary32 divisor, ties to even; an all-zero
  *                     group stores scale +0 and codes 0.  D % 64 == 0, D <= 512.
  *                     ([ST2698] "What it does"; ties-to-even: [ST120] "Tests".)
- *   KVQ_FMT_Q4_0_H256 D/2 / D/32.  V only.  The vector is rotated by the orthonormal
+ *   KVQ_FMT_Q4_0_H256 D/2 / D/32.  K or V.  The vector is rotated by the orthonormal
  *                     Walsh-Hadamard transform H = H_256/16 (Sylvester order; binary32
  *                     butterflies of span 1, 2, ..., 128, then x 1/16), then q4_0: per
  *                     32 values d = m / -8 with m the first value of largest magnitude,
  *                     stored fp16; code = clamp(rint(z / d) + 8, 0, 15); byte j holds
  *                     code 2j (low nibble) and 2j+1 (high nibble); a zero block stores
  *                     d = +0, codes 8.  Values stay in the rotated basis; attention
- *                     rotates its output back.  D == 256.
+ *                     rotates its output back, and with a Q4_0_H256 K store rotates q
+ *                     (<q, k> = <Hq, Hk>).  D == 256.
  *                     ([ST120] "What"/"How"; [ST2698] "Not in this PR".)
  *   KVQ_FMT_ISO3      D/128*48 / D/128.  Per 128 values: n = ||x|| (binary32 pairwise
  *                     halving sum of squares, then sqrt); u = x / n; each 4-group

@@ -30,6 +30,7 @@ UNITS = {
     "gather.hip": ["-ffp-contract=off"],
     "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
     "decode_iso3.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+    "decode_q4.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
     "extend.hip": [],
 }
 

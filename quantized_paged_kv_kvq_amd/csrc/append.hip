@@ -85,7 +85,8 @@ __device__ __forceinline__ void append_int8(const AppendArgs& a, const uint16_t*
 }
 
 // ---------------------------------------------------------------------------------------------
-// Q4_0_H256 (V only).  One wave per cell; lane l holds elements 4l .. 4l+3.
+// Q4_0_H256 (K or V; their tiles differ in byte order).  One wave per cell; lane l holds elements
+// 4l .. 4l+3.
 // FWHT butterflies run in the order of spans 1, 2, 4, ..., 128: spans 1 and 2 inside a lane,
 // spans 4..128 between lanes l and l ^ (span / 4).  Each butterfly maps (a, b) -> (a + b, a - b)
 // for the pair (i, i + span), exactly as the definition, so the result is bit-identical to any
@@ -107,7 +108,8 @@ __device__ __forceinline__ void fwht256_lane(float y[4], int lane) {
 }
 
 __device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* __restrict__ x,
-                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int block) {
+                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, bool is_v,
+                                           int block) {
   const int lane = threadIdx.x & 63;
   const long cell = (long)block * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const bool active = cell < (long)a.n_tok * a.hkv;
@@ -143,8 +145,10 @@ __device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* 
   locate(a, tok, page, slot);
   const size_t tile = (size_t)page * a.hkv + head;
   uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128;
-  base[v_tile_offset(2 * lane, slot)] = (uint8_t)(q[0] | (q[1] << 4));
-  base[v_tile_offset(2 * lane + 1, slot)] = (uint8_t)(q[2] | (q[3] << 4));
+  const int o0 = is_v ? v_tile_offset(2 * lane, slot) : k4_tile_offset(2 * lane, slot);
+  const int o1 = is_v ? v_tile_offset(2 * lane + 1, slot) : k4_tile_offset(2 * lane + 1, slot);
+  base[o0] = (uint8_t)(q[0] | (q[1] << 4));
+  base[o1] = (uint8_t)(q[2] | (q[3] << 4));
   if ((lane & 7) == 0)
     scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)] = f32_to_f16_bits(best != 0.0f ? d : 0.0f);
 }
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, StoreArgs k, Store
   if ((long)blockIdx.x >= st.blocks) return;
   const float quat[4] = {qw, qx, qy, qz};
   if (st.fmt == KVQ_FMT_INT8_G64) append_int8(a, st.x, st.codes, st.scales, D, st.is_v != 0, blockIdx.x);
-  else if (st.fmt == KVQ_FMT_Q4_0_H256) append_q4h(a, st.x, st.codes, st.scales, blockIdx.x);
+  else if (st.fmt == KVQ_FMT_Q4_0_H256) append_q4h(a, st.x, st.codes, st.scales, st.is_v != 0, blockIdx.x);
   else append_iso3(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
 }
 

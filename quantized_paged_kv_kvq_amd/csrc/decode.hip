@@ -31,6 +31,7 @@
 #include "kvq_internal.h"
 #include "device_util.h"
 #include "int8_cell.h"
+#include "decode_parts.h"
 
 namespace kvq {
 namespace {
@@ -79,13 +80,6 @@ __device__ __forceinline__ s16x4 codes_to_bf16_biased(uint32_t w) {
   return __builtin_bit_cast(s16x4, make_uint2(lo, hi));
 }
 
-// 4-bit codes of 4 tokens (one byte each; nibble picked by the caller) -> bf16 (128 + code), exact.
-__device__ __forceinline__ s16x4 nibbles_to_bf16_biased(uint32_t nib) {   // nib: 4 bytes, each 0..15
-  const uint32_t lo = __builtin_amdgcn_perm(0x43434343u, nib, 0x05010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(0x43434343u, nib, 0x05030402u);
-  return __builtin_bit_cast(s16x4, make_uint2(lo, hi));
-}
-
 // Split x into bf16 hi (truncated) + bf16 lo (rounded): hi + lo carries 16 significant bits.
 __device__ __forceinline__ void split_bf16(const float x[4], s16x4& hi, s16x4& lo) {
   uint32_t hb[4];
@@ -127,27 +121,8 @@ __device__ __forceinline__ void load_words(uint32_t (&dst)[N], const uint32_t* s
   }
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& q, int k) {
-  return k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
-}
-
 // One page of one KV head as a lane holds it.  Every code load is one 16-byte load per lane that
 // covers a contiguous kilobyte of the tile across the wave (see the tile byte orders in kvq.h).
-// One part of the hi/lo split, as the bf16 B operand and as the fp32 values it represents: the
-// truncated bf16 hi part (lo_mask == 0) or the truncated bf16 part of the remainder x - hi
-// (lo_mask == ~0).  hi + lo keeps 16 significant bits of x.
-__device__ __forceinline__ void split_bf16_select(const float x[4], uint32_t lo_mask, s16x4& part, float used[4]) {
-  uint32_t b[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t xb = __float_as_uint(x[e]);
-    b[e] = __float_as_uint(x[e] - __uint_as_float(xb & 0xffff0000u & lo_mask)) & 0xffff0000u;
-    used[e] = __uint_as_float(b[e]);
-  }
-  part = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(b[1], b[0], 0x07060302u),
-                                              __builtin_amdgcn_perm(b[3], b[2], 0x07060302u)));
-}
-
 template <int D, int VF>
 struct PageBuf {
   static constexpr int NG = D / 64;                      // K scale groups (one 16-byte K load each)
@@ -395,61 +370,6 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
         }
       }
     }
-  }
-}
-
-// y <- sum over butterflies of the rotated-basis row held as 64 values by the 4 lanes of a row
-// (k8v4): value (t, k) of O is head_dim 32*(t/2) + 8*j4 + 2*k + (t&1).  Applies H = H_256/16.
-template <int RT>
-__device__ __forceinline__ void hadamard_rows(f32x4 (&O)[RT][16], int lane) {
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    // bit 0 of head_dim: tile parity
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float e = O[rt][2 * b][k], o = O[rt][2 * b + 1][k];
-        O[rt][2 * b][k] = e + o; O[rt][2 * b + 1][k] = e - o;
-      }
-    // bits 1, 2: k
-#pragma unroll
-    for (int kb = 1; kb <= 2; kb <<= 1)
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (!(k & kb)) {
-            const float x = O[rt][t][k], y = O[rt][t][k | kb];
-            O[rt][t][k] = x + y; O[rt][t][k | kb] = x - y;
-          }
-    // bits 3, 4: lane groups (xor 16, 32)
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const bool upper = (lane & o) != 0;
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float other = o == 16 ? partner16(O[rt][t][k], lane) : partner32(O[rt][t][k], lane);
-          O[rt][t][k] = upper ? (other - O[rt][t][k]) : (O[rt][t][k] + other);
-        }
-    }
-    // bits 5..7: block index b = t/2
-#pragma unroll
-    for (int bb = 1; bb <= 4; bb <<= 1)
-#pragma unroll
-      for (int b = 0; b < 8; ++b)
-        if (!(b & bb))
-#pragma unroll
-          for (int par = 0; par < 2; ++par)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float x = O[rt][2 * b + par][k], y = O[rt][2 * (b | bb) + par][k];
-              O[rt][2 * b + par][k] = x + y; O[rt][2 * (b | bb) + par][k] = x - y;
-            }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) O[rt][t] *= 0.0625f;
   }
 }
 

@@ -78,10 +78,6 @@ __device__ __forceinline__ void quat_mul(const float a[4], const float u[4], flo
   o[3] = a[0] * u[3] + a[1] * u[2] - a[2] * u[1] + a[3] * u[0];
 }
 
-__device__ __forceinline__ float dpp_ror8(float x) {   // value of lane (l & ~15) | ((l + 8) & 15)
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-}
-
 // One page of one KV head as a lane holds it (NB = head_dim / 128 blocks per cell).
 template <int NB>
 struct IsoPage {

@@ -1,0 +1,92 @@
+// Device pieces shared by the decode kernels whose V store is Hadamard-rotated q4_0 (strata PR #120,
+// "What"/"How": V rotated by H = H_256/16 and stored in q4_0; the attention output is rotated back):
+// the biased bf16 operand of 4 tokens' 4-bit codes, the hi / lo split of the softmax weights into
+// bf16 MFMA columns, and the back-rotation of a partial output row.
+#pragma once
+
+#include "device_util.h"
+
+namespace kvq {
+
+// 4-bit codes of 4 tokens (one byte each; nibble picked by the caller) -> bf16 (128 + code), exact.
+__device__ __forceinline__ s16x4 nibbles_to_bf16_biased(uint32_t nib) {   // nib: 4 bytes, each 0..15
+  const uint32_t lo = __builtin_amdgcn_perm(0x43434343u, nib, 0x05010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x43434343u, nib, 0x05030402u);
+  return __builtin_bit_cast(s16x4, make_uint2(lo, hi));
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& q, int k) {
+  return k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
+}
+
+// One part of the hi/lo split, as the bf16 B operand and as the fp32 values it represents: the
+// truncated bf16 hi part (lo_mask == 0) or the truncated bf16 part of the remainder x - hi
+// (lo_mask == ~0).  hi + lo keeps 16 significant bits of x.
+__device__ __forceinline__ void split_bf16_select(const float x[4], uint32_t lo_mask, s16x4& part, float used[4]) {
+  uint32_t b[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t xb = __float_as_uint(x[e]);
+    b[e] = __float_as_uint(x[e] - __uint_as_float(xb & 0xffff0000u & lo_mask)) & 0xffff0000u;
+    used[e] = __uint_as_float(b[e]);
+  }
+  part = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(b[1], b[0], 0x07060302u),
+                                              __builtin_amdgcn_perm(b[3], b[2], 0x07060302u)));
+}
+
+// y <- sum over butterflies of the rotated-basis row held as 64 values by the 4 lanes of a row
+// (k8v4): value (t, k) of O is head_dim 32*(t/2) + 8*j4 + 2*k + (t&1).  Applies H = H_256/16.
+template <int RT>
+__device__ __forceinline__ void hadamard_rows(f32x4 (&O)[RT][16], int lane) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    // bit 0 of head_dim: tile parity
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e = O[rt][2 * b][k], o = O[rt][2 * b + 1][k];
+        O[rt][2 * b][k] = e + o; O[rt][2 * b + 1][k] = e - o;
+      }
+    // bits 1, 2: k
+#pragma unroll
+    for (int kb = 1; kb <= 2; kb <<= 1)
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (!(k & kb)) {
+            const float x = O[rt][t][k], y = O[rt][t][k | kb];
+            O[rt][t][k] = x + y; O[rt][t][k | kb] = x - y;
+          }
+    // bits 3, 4: lane groups (xor 16, 32)
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const bool upper = (lane & o) != 0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float other = o == 16 ? partner16(O[rt][t][k], lane) : partner32(O[rt][t][k], lane);
+          O[rt][t][k] = upper ? (other - O[rt][t][k]) : (O[rt][t][k] + other);
+        }
+    }
+    // bits 5..7: block index b = t/2
+#pragma unroll
+    for (int bb = 1; bb <= 4; bb <<= 1)
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if (!(b & bb))
+#pragma unroll
+          for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float x = O[rt][2 * b + par][k], y = O[rt][2 * (b | bb) + par][k];
+              O[rt][2 * b + par][k] = x + y; O[rt][2 * (b | bb) + par][k] = x - y;
+            }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) O[rt][t] *= 0.0625f;
+  }
+}
+
+}  // namespace kvq

@@ -47,6 +47,11 @@ static __device__ __forceinline__ float sum_over_row_lanes(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Value of lane (l & ~15) | ((l + 8) & 15): the other half of the lane's 16-lane row.
+static __device__ __forceinline__ float dpp_ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+}
+
 // Data read once per call: non-temporal loads keep it from displacing reusable lines.
 static __device__ __forceinline__ uint4 stream_load(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

@@ -61,10 +61,10 @@ __global__ __launch_bounds__(256) void k_gather_int8(GatherArgs g, const uint8_t
   store4(out, ((size_t)i * g.hkv + head) * D + 4 * part, v, dtype);
 }
 
-// Q4_0_H256 (V): one wave per cell, lane l holds elements 4l .. 4l+3.
+// Q4_0_H256 (K or V tile order): one wave per cell, lane l holds elements 4l .. 4l+3.
 __global__ __launch_bounds__(256) void k_gather_q4h(GatherArgs g, const uint8_t* __restrict__ codes,
-                                                    const uint16_t* __restrict__ scales, void* out, int dtype,
-                                                    int unrotate) {
+                                                    const uint16_t* __restrict__ scales, int is_v, void* out,
+                                                    int dtype, int unrotate) {
   const int lane = threadIdx.x & 63;
   const long cell = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const bool active = cell < (long)g.count * g.hkv;
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256) void k_gather_q4h(GatherArgs g, const uint8_t*
   int slot;
   const size_t tile = tile_of(g, i, head, slot);
   const uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128;
-  const uint32_t b0 = base[v_tile_offset(2 * lane, slot)], b1 = base[v_tile_offset(2 * lane + 1, slot)];
+  const uint32_t b0 = base[is_v ? v_tile_offset(2 * lane, slot) : k4_tile_offset(2 * lane, slot)];
+  const uint32_t b1 = base[is_v ? v_tile_offset(2 * lane + 1, slot) : k4_tile_offset(2 * lane + 1, slot)];
   const float d = f16_bits_to_f32(scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)]);
   float y[4] = {(float)((int)(b0 & 15) - 8) * d, (float)((int)(b0 >> 4) - 8) * d, (float)((int)(b1 & 15) - 8) * d,
                 (float)((int)(b1 >> 4) - 8) * d};
@@ -137,8 +138,8 @@ hipError_t launch_gather(int fmt, bool is_v, const uint8_t* codes, const uint16_
     k_gather_int8<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, is_v ? 1 : 0,
                                                                                out, out_dtype);
   } else if (fmt == KVQ_FMT_Q4_0_H256) {
-    k_gather_q4h<<<dim3((unsigned)((cells + 3) / 4)), dim3(256), 0, s>>>(g, codes, scales, out, out_dtype,
-                                                                          unrotate ? 1 : 0);
+    k_gather_q4h<<<dim3((unsigned)((cells + 3) / 4)), dim3(256), 0, s>>>(g, codes, scales, is_v ? 1 : 0, out,
+                                                                          out_dtype, unrotate ? 1 : 0);
   } else {
     const long threads = cells * (D / 4);
     k_gather_iso3<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, quat[0], quat[1],

@@ -33,8 +33,6 @@ kvq_status check_store_fmt(int fmt, int D, bool is_v) {
     return fail(KVQ_ERR_UNSUPPORTED, "INT8_G64 needs head_dim %% 64 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
   if (fmt == KVQ_FMT_Q4_0_H256 && D != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "Q4_0_H256 needs head_dim == 256 (got %d)", D);
-  if (fmt == KVQ_FMT_Q4_0_H256 && !is_v)
-    return fail(KVQ_ERR_UNSUPPORTED, "Q4_0_H256 is a V-store format (K would need q rotated as well)");
   if (fmt == KVQ_FMT_ISO3 && (D % 128 != 0 || D > KVQ_MAX_HEAD_DIM))
     return fail(KVQ_ERR_UNSUPPORTED, "ISO3 needs head_dim %% 128 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
   return KVQ_OK;
@@ -205,8 +203,13 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if ((st = check_store_fmt(cache->k.fmt, cache->head_dim, false)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->v.fmt, cache->head_dim, true)) != KVQ_OK) return st;
   const bool iso = cache->k.fmt == KVQ_FMT_ISO3 && cache->v.fmt == KVQ_FMT_ISO3;
-  if (!iso && cache->k.fmt != KVQ_FMT_INT8_G64)
-    return fail(KVQ_ERR_UNSUPPORTED, "decode needs an INT8_G64 K store or ISO3 K and V stores (got formats %d / %d)",
+  const bool q4k = cache->k.fmt == KVQ_FMT_Q4_0_H256;
+  if (q4k && cache->v.fmt != KVQ_FMT_Q4_0_H256)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode over a Q4_0_H256 K store needs a Q4_0_H256 V store (got %d)",
+                cache->v.fmt);
+  if (!iso && !q4k && cache->k.fmt != KVQ_FMT_INT8_G64)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "decode needs an INT8_G64 or Q4_0_H256 K store, or ISO3 K and V stores (got formats %d / %d)",
                 cache->k.fmt, cache->v.fmt);
   if (!iso && cache->v.fmt == KVQ_FMT_ISO3)
     return fail(KVQ_ERR_UNSUPPORTED, "decode over an ISO3 V store needs an ISO3 K store");
@@ -227,8 +230,12 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if (iso && (long)n_q * max_g > kIsoDecodeMaxRows)
     return fail(KVQ_ERR_UNSUPPORTED, "ISO3 decode: n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
                 kIsoDecodeMaxRows);
-  *plan = iso ? plan_decode_iso3(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
-              : plan_decode(cache->v.fmt, D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
+  if (q4k && (long)n_q * max_g > kQ4DecodeMaxRows)
+    return fail(KVQ_ERR_UNSUPPORTED, "q4_0 K decode: n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
+                kQ4DecodeMaxRows);
+  *plan = iso   ? plan_decode_iso3(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
+          : q4k ? plan_decode_q4(cache->n_kv_heads, batch, max_pages, n_q * max_g)
+                : plan_decode(cache->v.fmt, D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
   if (plan->n_splits > decode_max_splits())
     return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d needs %d context splits; decode supports %d", max_pages,
                 plan->n_splits, decode_max_splits());
@@ -293,6 +300,7 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (cache->k.fmt == KVQ_FMT_ISO3)
     return hip_status(launch_decode_iso3(cache->head_dim, plan, a, hs), "decode launch");
+  if (cache->k.fmt == KVQ_FMT_Q4_0_H256) return hip_status(launch_decode_q4(plan, a, hs), "decode launch");
   return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, hs), "decode launch");
 }
 

@@ -12,8 +12,13 @@ namespace kvq {
 //   INT8_G64 K stores: 16-byte chunks, chunk-major -- a wave reads a contiguous kilobyte per load
 //   INT8_G64 / Q4_0_H256 V stores: 4 consecutive slots of one code byte form a 32-bit word; the
 //     words of code bytes c, c+16, c+32, c+48 (c % 64 < 16) form a 16-byte unit
+//   Q4_0_H256 K stores: 16-byte units, unit (c/64, (c/4)%4, t) holds bytes 4w .. 4w+3 (w = (c/4)%4) of
+//     the four 32-value groups c/64*4 .. +3 of slot t -- one wave load covers a contiguous kilobyte
 //   ISO3 stores: token-major
 __host__ __device__ inline int k_tile_offset(int c, int t) { return ((c >> 4) * 16 + t) * 16 + (c & 15); }
+__host__ __device__ inline int k4_tile_offset(int c, int t) {
+  return (((c >> 6) * 4 + ((c >> 2) & 3)) * 16 + t) * 16 + ((c >> 4) & 3) * 4 + (c & 3);
+}
 __host__ __device__ inline int v_tile_offset(int c, int t) {
   return ((((c >> 6) << 4) | (c & 15)) * 4 + (t >> 2)) * 16 + ((c >> 4) & 3) * 4 + (t & 3);
 }
@@ -111,6 +116,10 @@ hipError_t launch_decode_combine(int head_dim, const DecodePlan& plan, const Dec
 // ISO3 K and V stores (head_dim 128 or 256, at most kIsoDecodeMaxRows rows per KV head)
 DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode_iso3(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
+// Q4_0_H256 K and V stores (head_dim 256, at most kQ4DecodeMaxRows rows per KV head)
+constexpr int kQ4DecodeMaxRows = 8;
+DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows);
+hipError_t launch_decode_q4(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 
 // Extend over an ISO3 prefix: one row per (new token, query head); rows of KV head j use the query
 // heads head_list[head_off[j] .. head_off[j+1]).

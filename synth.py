@@ -201,6 +201,23 @@ def moe_iso3_decode(ctx: int = 131072, seed: int = 7, n_q_heads: int = 16, n_kv_
     return w
 
 
+def moe_q4h_decode(ctx: int = 131072, seed: int = 8, n_q_heads: int = 16, n_kv_heads: int = 2,
+                   head_dim: int = 256, n_outliers: int = 4) -> Workload:
+    """moe_int8_decode's layer (GQA 16:2, head_dim 256, K outlier channels x20) over Hadamard-rotated
+    q4_0 K and V stores (strata PR #2698, "Not in this PR": rotate K and V, the queries and the output)."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([ctx], np.int32)
+    table, npages = _page_table(rng, lens, PAGE_SIZE, identity=False)
+    outliers = np.sort(rng.choice(head_dim, size=n_outliers, replace=False)) if n_outliers else []
+    k = normal_bf16(rng, (ctx, n_kv_heads, head_dim), outlier_channels=outliers)
+    v = normal_bf16(rng, (ctx, n_kv_heads, head_dim))
+    q = normal_bf16(rng, (1, 1, n_q_heads, head_dim))
+    w = Workload("moe_q4h_decode", "q4h", "q4h", 1, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
+                 lens, table, npages, [k], [v], q)
+    w.meta["outlier_channels"] = [int(c) for c in outliers]
+    return w
+
+
 def k8v4_verify(ctx: int = 118750, seed: int = 4, n_q: int = 3, n_q_heads: int = 16,
                 n_kv_heads: int = 2, head_dim: int = 256) -> Workload:
     """int8 K + Hadamard-rotated q4_0 V; an MTP verify window of ``n_q`` query tokens whose

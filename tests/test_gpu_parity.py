@@ -53,7 +53,8 @@ def check_decode(w, head_map=None):
 # quantize-on-write and gather
 
 @pytest.mark.parametrize("fmt_k,fmt_v,D", [("int8", "int8", 128), ("int8", "int8", 256), ("int8", "int8", 64),
-                                           ("int8", "q4h", 256), ("iso3", "iso3", 128), ("iso3", "iso3", 256)])
+                                           ("int8", "q4h", 256), ("q4h", "q4h", 256), ("iso3", "iso3", 128),
+                                           ("iso3", "iso3", 256)])
 def test_append_bitexact_through_random_pages(fmt_k, fmt_v, D):
     w = synth.ragged_decode(fmt_k, fmt_v, [37, 64, 5, 1, 130], head_dim=D, seed=21, n_q_heads=4, n_kv_heads=2)
     print(f"[append] {fmt_k}/{fmt_v} D={D}", flush=True)
@@ -90,11 +91,12 @@ def test_append_special_values():
     assert_slabs_equal(cache, sk, sv)
 
 
-@pytest.mark.parametrize("fmt,D", [("int8", 128), ("int8", 256), ("q4h", 256), ("iso3", 128), ("iso3", 256)])
-def test_gather_bitexact(fmt, D):
+@pytest.mark.parametrize("fmt,D,fk", [("int8", 128, None), ("int8", 256, None), ("q4h", 256, "int8"), ("q4h", 256, "q4h"),
+                                      ("iso3", 128, None), ("iso3", 256, None)])
+def test_gather_bitexact(fmt, D, fk):
     import torch
     import quantized_paged_kv_kvq_amd as kvq
-    fk = "int8" if fmt == "q4h" else fmt
+    fk = fk or fmt
     w = synth.ragged_decode(fk, fmt, [77, 33], head_dim=D, seed=23, n_q_heads=2, n_kv_heads=2)
     cache, pages = gpu_cache(w)
     gpu_append(w, cache, pages, "prefix")
