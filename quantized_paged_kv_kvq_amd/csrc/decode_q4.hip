@@ -105,14 +105,14 @@ __device__ __forceinline__ f16x8 k_group_f16(uint32_t x) {
 
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
 __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, bool lo_col, int Lrow,
-                                             const f16x8 (&qb)[kGroups], float qmul, float& m_run, float& l_run,
+                                             const f16x8* qb, float qmul, float& m_run, float& l_run,
                                              float (&ls)[kGroups], f32x4 (&O)[kTiles]) {
   // ---- QK: per group, S^T[token 4w + k][column]; weighted by the group's d; hi + lo columns
   float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int G = 0; G < kGroups; ++G) {
     const f16x8 av = k_group_f16(word_of(pb.k[G >> 2], G & 3));
-    const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[G], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[64 * G], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) sp[k] = fmaf(acc[k], pb.kd(k, G), sp[k]);
   }
@@ -161,6 +161,8 @@ __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, boo
 template <int NW, int PPW, int PD, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) {
   __shared__ __align__(16) float mrg[NW * (kTiles * 64 * 4 + 2 * 64)];
+  __shared__ __align__(16) f16x8 qlds[kGroups * 64];    // B operands of QK: [group][lane]
+  __shared__ float qmul_lds[64];
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15, w = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -222,9 +224,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
   // ---- B operands of QK: Hq (FWHT-256 of the row, x 1/16), times 2^ex (max |.| of the row in
   // [2^14, 2^15)), hi parts in columns 0-7, lo parts in 8-15.  The lane holds head_dim
   // 32G + 8w + j: bits 0-2 (j) and 5-7 (G) of the index are in-lane, bits 3-4 (w) across lanes.
-  f16x8 qb[kGroups];
-  float qmul;
-  {
+  // Wave 0 builds them into LDS for the workgroup (every wave holds the same rows).
+  if (wv == 0) {
     float x[kGroups][8];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
@@ -283,10 +284,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
       for (int j = 0; j < 8; ++j) {
         const float y = ldexpf(x[g][j], ex);
         const _Float16 hi = (_Float16)y, lo = (_Float16)(y - (float)hi);
-        qb[g][j] = lo_col ? lo : hi;
+        qlds[64 * g + lane][j] = lo_col ? lo : hi;
       }
-    qmul = ldexpf(a.scale_log2, -ex);
+    qmul_lds[lane] = ldexpf(a.scale_log2, -ex);
   }
+  __syncthreads();
+  const float qmul = qmul_lds[lane];
+  const f16x8* qb = qlds + lane;
 
   float m_run = kNegInf, l_run = 0.0f, ls[kGroups];
   f32x4 O[kTiles];
