@@ -183,7 +183,9 @@ kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages,
  * 128 or 256, and a K store of format INT8_G64 (the V store may be INT8_G64 or
  * Q4_0_H256); or ISO3 K and V stores ([FT398] "Pull request overview": the ISO backend's
  * decode attention over packed cells) with head_dim 128 or 256 and n_q * (largest number
- * of query heads of one KV head) <= 16.  ISO3 outputs are in the original basis. */
+ * of query heads of one KV head) <= 16.  ISO3 outputs are in the original basis.  A
+ * Q4_0_H256 K store needs a Q4_0_H256 V store and the same <= 16 rows ([ST2698] "Not in this
+ * PR": q4_0 K and V, rotated, with the queries rotated). */
 kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
                            const void* q, int32_t n_q, int32_t n_q_heads,
                            const int32_t* q_lens, const int32_t* head_map,

@@ -7,19 +7,20 @@
 // values accumulate in the rotated basis (the partial is rotated back, as for k8v4).
 //
 // Work decomposition: one workgroup = one (sequence, KV head, split of NW * PPW pages); wave w takes
-// pages w, w + NW, ... of the split.  At most 8 query rows per KV head: one MFMA column each, the
-// columns 8-15 repeat them for the lo parts of split operands.
+// pages w, w + NW, ... of the split.  At most 16 query rows per KV head, one MFMA column each; with
+// at most 8 rows the columns 8-15 repeat them and take the lo parts of split operands (one MFMA
+// where 9-16 rows need two).
 //   * QK: S^T[token][row] on v_mfma_f32_16x16x32_f16, one MFMA per 32-value scale group.  Lane
 //     (w = lane / 16, t = lane % 16) holds slot t's 8 codes 32G + 8w .. +7 of group G (4 bytes of
 //     one 16-byte unit of the K tile order); they become the exact fp16 values code - 8 with one
 //     byte permute, a mask and a packed fp16 fma per pair.  The B operand is Hq scaled per row by
-//     a power of two, hi parts in columns 0-7, lo parts in 8-15; each group's accumulator is
-//     weighted by its (token, group) d in fp32 and one DPP add joins the hi and lo columns.
+//     a power of two in fp16 hi + lo parts; each group's accumulator is weighted by its (token,
+//     group) d in fp32.
 //   * Online softmax in base 2 with a lazily moved reference max (as the other decode kernels).
 //   * PV: O^T[d][row] on v_mfma_f32_16x16x16bf16_1k, as the k8v4 kernel: the A operand is 4 tokens'
 //     4-bit codes at one head_dim row as bf16 (128 + code), the B operand the weights times the
-//     token's V d split into bf16 hi (columns 0-7) and lo (8-15) parts; the code offset comes off at
-//     the end through the per-group weight sums.
+//     token's V d split into bf16 hi and lo parts; the code offset comes off at the end through the
+//     per-group weight sums.
 //   * The waves merge through LDS (wave 0 takes whole rows), the partial is rotated back by H and
 //     goes to the log-sum-exp combine shared with the other decode kernels.
 #include "kvq_internal.h"
@@ -103,16 +104,20 @@ __device__ __forceinline__ f16x8 k_group_f16(uint32_t x) {
   return r;
 }
 
-// One page of one wave: QK on MFMA, online softmax, PV on MFMA.
+// One page of one wave: QK on MFMA, online softmax, PV on MFMA.  qb: the lane's query fragments
+// in LDS, [group][part][lane] (one part with DUP: hi or lo by column).
+template <bool DUP>
 __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, bool lo_col, int Lrow,
                                              const f16x8* qb, float qmul, float& m_run, float& l_run,
                                              float (&ls)[kGroups], f32x4 (&O)[kTiles]) {
-  // ---- QK: per group, S^T[token 4w + k][column]; weighted by the group's d; hi + lo columns
+  constexpr int NP = DUP ? 1 : 2;
+  // ---- QK: per group, S^T[token 4w + k][column]; weighted by the group's d
   float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int G = 0; G < kGroups; ++G) {
     const f16x8 av = k_group_f16(word_of(pb.k[G >> 2], G & 3));
-    const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[64 * G], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[64 * NP * G], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    if constexpr (!DUP) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[64 * (NP * G + 1)], acc, 0, 0, 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) sp[k] = fmaf(acc[k], pb.kd(k, G), sp[k]);
   }
@@ -121,7 +126,7 @@ __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, boo
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float x = sp[k];
-    s[k] = k < vis ? (x + dpp_ror8(x)) * qmul : kNegInf;
+    s[k] = k < vis ? (DUP ? x + dpp_ror8(x) : x) * qmul : kNegInf;   // DUP: hi + lo columns
   }
   const float mx = max_over_row_lanes(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
   const bool move = mx > m_run + kLazyQ4;
@@ -146,22 +151,30 @@ __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, boo
     float pw[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) pw[k] = pk[k] * pb.vd(k, g);
-    s16x4 bpart;
-    float used[4];
-    split_bf16_select(pw, lo_col ? 0xffffffffu : 0u, bpart, used);
+    s16x4 bpart, blo;
+    float used[4], used_lo[4];
+    split_bf16_select(pw, lo_col ? 0xffffffffu : 0u, bpart, used);            // DUP: hi or lo by column
     ls[g] += (used[0] + used[1]) + (used[2] + used[3]);
+    if constexpr (!DUP) {
+      split_bf16_select(pw, 0xffffffffu, blo, used_lo);                       // the lo part as well
+      ls[g] += (used_lo[0] + used_lo[1]) + (used_lo[2] + used_lo[3]);
+    }
     const uint32_t wv = word_of(pb.v[g >> 2], g & 3);      // byte k: token 4w + k; nibbles: dims 32g + 2t (+1)
-    O[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nibbles_to_bf16_biased(wv & 0x0f0f0f0fu), bpart, O[2 * g],
-                                                         0, 0, 0);
-    O[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nibbles_to_bf16_biased((wv >> 4) & 0x0f0f0f0fu), bpart,
-                                                             O[2 * g + 1], 0, 0, 0);
+    const s16x4 alo = nibbles_to_bf16_biased(wv & 0x0f0f0f0fu), ahi = nibbles_to_bf16_biased((wv >> 4) & 0x0f0f0f0fu);
+    O[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bpart, O[2 * g], 0, 0, 0);
+    O[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bpart, O[2 * g + 1], 0, 0, 0);
+    if constexpr (!DUP) {
+      O[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, O[2 * g], 0, 0, 0);
+      O[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, O[2 * g + 1], 0, 0, 0);
+    }
   }
 }
 
-template <int NW, int PPW, int PD, int OCC>
+template <bool DUP, int NW, int PPW, int PD, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) {
+  constexpr int NP = DUP ? 1 : 2;                       // query fragment parts per group
   __shared__ __align__(16) float mrg[NW * (kTiles * 64 * 4 + 2 * 64)];
-  __shared__ __align__(16) f16x8 qlds[kGroups * 64];    // B operands of QK: [group][lane]
+  __shared__ __align__(16) f16x8 qlds[kGroups * NP * 64];    // B operands of QK: [group][part][lane]
   __shared__ float qmul_lds[64];
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15, w = lane >> 4;
@@ -179,8 +192,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
   const int R = a.n_q * G;
   const int RA = a.row_alloc;
   const int cap = a.max_pages * KVQ_PAGE_SIZE;
-  const bool lo_col = t16 >= 8;
-  const int r = t16 & 7;
+  const bool lo_col = DUP && t16 >= 8;
+  const int r = DUP ? (t16 & 7) : t16;
   const bool valid = r < R;
   const int tq = valid ? r / G : 0, iq = valid ? r % G : 0;
   const int hq = a.g_uniform > 0 ? h0 + iq : a.head_list[h0 + iq];
@@ -222,7 +235,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
   }
 
   // ---- B operands of QK: Hq (FWHT-256 of the row, x 1/16), times 2^ex (max |.| of the row in
-  // [2^14, 2^15)), hi parts in columns 0-7, lo parts in 8-15.  The lane holds head_dim
+  // [2^14, 2^15)), as fp16 hi + lo parts (DUP: hi in columns 0-7, lo in 8-15).  The lane holds head_dim
   // 32G + 8w + j: bits 0-2 (j) and 5-7 (G) of the index are in-lane, bits 3-4 (w) across lanes.
   // Wave 0 builds them into LDS for the workgroup (every wave holds the same rows).
   if (wv == 0) {
@@ -284,7 +297,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
       for (int j = 0; j < 8; ++j) {
         const float y = ldexpf(x[g][j], ex);
         const _Float16 hi = (_Float16)y, lo = (_Float16)(y - (float)hi);
-        qlds[64 * g + lane][j] = lo_col ? lo : hi;
+        if constexpr (DUP) {
+          qlds[64 * g + lane][j] = lo_col ? lo : hi;
+        } else {
+          qlds[64 * (2 * g) + lane][j] = hi;
+          qlds[64 * (2 * g + 1) + lane][j] = lo;
+        }
       }
     qmul_lds[lane] = ldexpf(a.scale_log2, -ex);
   }
@@ -311,7 +329,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
       if (i + PD < PPW)
         load_q4_page(buf[(i + PD) % (PD + 1)], a, clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1),
                      kvh, lane);
-      q4_page_step(buf[i % (PD + 1)], pc, w, lo_col, Lrow, qb, qmul, m_run, l_run, ls, O);
+      q4_page_step<DUP>(buf[i % (PD + 1)], pc, w, lo_col, Lrow, qb, qmul, m_run, l_run, ls, O);
       if (i + 1 >= n_mine) break;
     }
   }
@@ -355,9 +373,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
 #pragma unroll
     for (int v = 1; v < NW; ++v) acc += cv[v] * *reinterpret_cast<const f32x4*>(lds_o + ((v * kTiles + t) * 64 + lane) * 4);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {   // column r + 8 holds the lo-part sums of row r
+    for (int k = 0; k < 4; ++k) {   // DUP: column r + 8 holds the lo-part sums of row r
       const float x = acc[k];
-      Om[0][t][k] = x + dpp_ror8(x);
+      Om[0][t][k] = DUP ? x + dpp_ror8(x) : x;
     }
   }
   hadamard_rows<1>(Om, lane);
@@ -379,7 +397,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
 template <int SH>
 hipError_t launch_q4_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   constexpr Q4Shape sh = kQ4Shapes[SH];
-  k_decode_q4<sh.nw, sh.ppw, sh.pd, sh.occ><<<dim3((unsigned)plan.n_splits, a.hkv, a.batch), dim3(sh.nw * 64), 0, s>>>(a);
+  const dim3 grid((unsigned)plan.n_splits, a.hkv, a.batch), block(sh.nw * 64);
+  if (plan.rows <= 8)
+    k_decode_q4<true, sh.nw, sh.ppw, sh.pd, sh.occ><<<grid, block, 0, s>>>(a);
+  else
+    k_decode_q4<false, sh.nw, sh.ppw, sh.pd, sh.occ><<<grid, block, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine(kD, plan, a, s);
@@ -397,7 +419,7 @@ hipError_t launch_q4_shape(const DecodePlan& plan, const DecodeArgs& a, hipStrea
 DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows) {
   DecodePlan p{};
   p.rows = max_rows;
-  p.row_groups = 1;                                 // at most 8 rows: partial rows 8
+  p.row_groups = max(1, (max_rows + 7) / 8);       // partial rows: 8 or 16
   p.row_tiles = 0;
   auto splits_of = [&](int sh) {
     const int pps = kQ4Shapes[sh].nw * kQ4Shapes[sh].ppw;
@@ -409,7 +431,7 @@ DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows) {
   p.waves = kQ4Shapes[p.shape].nw;
   p.pages_per_split = kQ4Shapes[p.shape].nw * kQ4Shapes[p.shape].ppw;
   p.n_splits = splits_of(p.shape);
-  p.part_bytes = (size_t)batch * hkv * p.n_splits * 8 * (kD + 2) * sizeof(float);
+  p.part_bytes = (size_t)batch * hkv * p.n_splits * (8 * p.row_groups) * (kD + 2) * sizeof(float);
   return p;
 }
 

@@ -117,7 +117,7 @@ hipError_t launch_decode_combine(int head_dim, const DecodePlan& plan, const Dec
 DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode_iso3(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 // Q4_0_H256 K and V stores (head_dim 256, at most kQ4DecodeMaxRows rows per KV head)
-constexpr int kQ4DecodeMaxRows = 8;
+constexpr int kQ4DecodeMaxRows = 16;
 DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode_q4(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 

@@ -73,7 +73,7 @@ def test_decode_validation_errors():
     assert decode(make_cache(), None) == 1
     assert decode(make_cache(page=8), make_pages()) == 3
     assert decode(make_cache(fk=2), make_pages()) == 3                 # q4_0 K needs a q4_0 V store
-    assert decode(make_cache(fk=2, fv=2), make_pages(), n_q=2) == 3    # q4_0 K: 16 rows > 8
+    assert decode(make_cache(fk=2, fv=2), make_pages(), n_q=3) == 3    # q4_0 K: 24 rows > 16
     assert decode(make_cache(fk=3, fv=1, D=128), make_pages()) == 3     # ISO3 K needs an ISO3 V store
     assert decode(make_cache(fk=1, fv=3, D=128), make_pages()) == 3     # and ISO3 V an ISO3 K store
     assert decode(make_cache(fk=3, fv=3, D=128), make_pages(), n_q=3) == 3    # ISO3: 24 rows > 16
@@ -127,7 +127,8 @@ def test_decode_workspace_size_formula():
     assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 3, 16, None) == 0
     q4 = make_cache(fk=2, fv=2)
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 2, 16, None) == 0
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 2, 16, None) == 2 * 128 * 16 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 3, 16, None) == 0
 
 
 def test_append_and_gather_validation_errors():

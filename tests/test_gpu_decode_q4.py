@@ -51,9 +51,12 @@ def test_q4_decode_eight_rows():
     check(q4([5, 700, 4100], 82, n_q_heads=16, n_kv_heads=2))
 
 
-def test_q4_verify_window():
-    """Two query tokens x 4 heads = 8 rows with per-query causal lengths."""
-    check(q4([40, 17, 1000, 2049], 83, n_q=2, q_len_back=[1, 0], n_q_heads=8, n_kv_heads=2))
+@pytest.mark.parametrize("n_q,hq", [(2, 8), (3, 8), (2, 16)])
+def test_q4_verify_window(n_q, hq):
+    """Verify windows with per-query causal lengths: 8 rows (hi / lo in one MFMA's columns), 12 and
+    16 rows (separate hi and lo MFMAs)."""
+    back = list(range(n_q - 1, -1, -1))
+    check(q4([40, 17, 1000, 2049], 83 + n_q + hq, n_q=n_q, q_len_back=back, n_q_heads=hq, n_kv_heads=2))
 
 
 def test_q4_decode_head_map_and_idle_kv_heads():
