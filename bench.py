@@ -271,6 +271,29 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}))
 
 
+def read_probe(nbytes: int):
+    """Context for the HBM roofline: the rate of a plain streaming read (torch's sum over a float32
+    tensor of nbytes, which reads it once) and of a plain copy, timed with HIP events."""
+    import torch
+    n = nbytes // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    res = {}
+    for name, fn, moved in (("read", lambda: x.sum(), nbytes), ("copy", lambda: y.copy_(x), 2 * nbytes)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        res[name] = {"us": round(us, 2), "GB/s": round(moved / (us * 1e-6) / 1e9, 1)}
+    print(json.dumps({"probe_bytes": nbytes, **res}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +307,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="cache copies to rotate (0 = enough to exceed the MALL)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run only a plain device copy of BYTES (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="BYTES",
+                    help="time only a plain streaming read and a plain copy of BYTES (context for the roofline)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
@@ -298,6 +323,8 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.read_probe:
+        return read_probe(args.read_probe)
     kvq.lib()
     if args.workload == "iso3_extend":
         return bench_extend(args)
