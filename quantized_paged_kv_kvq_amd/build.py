@@ -23,14 +23,16 @@ LIB = os.path.join(HERE, "libkvq.so")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
-# translation unit -> extra flags
+# translation unit -> extra flags.  The decode kernels need their page loops fully unrolled (a rolled
+# loop waits for every outstanding load); the k8v4 row-tile and q4_0-K kernels keep their MFMA
+# accumulators in VGPRs (the default placed them in AGPRs and copied them around every MFMA).
 UNITS = {
     "kvq_api.hip": [],
     "append.hip": ["-ffp-contract=off"],
     "gather.hip": ["-ffp-contract=off"],
-    "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+    "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode_iso3.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
-    "decode_q4.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+    "decode_q4.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "extend.hip": [],
 }
 
