@@ -531,9 +531,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
 
   if (R == 0) return;
   if (p_begin >= p_end) {                                   // nothing visible in this split
-    const int r = DUP ? 8 * rg + (int)threadIdx.x : (int)threadIdx.x;
-    if ((int)threadIdx.x < (DUP ? 8 * RT : RA) && r < RA) {
-      float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
+    const int r_lo = DUP ? 8 * rg : 0, r_hi = min(R, r_lo + (DUP ? 8 * RT : RA));
+    if (a.n_splits == 1) {                                  // the only split writes the output: zeros
+      for (int i = (int)threadIdx.x; i < (r_hi - r_lo) * (D / 4); i += NW * 64)
+        *reinterpret_cast<float4*>(a.out + (size_t)decode_out_row(a, b, kvh, r_lo + i / (D / 4), G, h0) * D +
+                                   4 * (i % (D / 4))) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else if ((int)threadIdx.x < r_hi - r_lo) {
+      float* ml = part_ml + ((row0 + r_lo + threadIdx.x) * a.n_splits + split) * 2;
       ml[0] = kNegInf; ml[1] = 0.0f;
     }
     return;
@@ -690,16 +694,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   // k8v4: rotate the (unnormalised) partial back now; the combine is linear, so H commutes with it
   if constexpr (VF == 2) hadamard_rows<RT>(O, lane);
 
-  // ---- write the workgroup's partial for rows r < R
+  // ---- write the workgroup's partial for rows r < R; with a single split, the normalised output
+  // itself (no combine launch follows)
+  const bool direct = a.n_splits == 1;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = DUP ? 8 * (rg + rt) + i16 : 16 * rt + i16;
     if (r >= R || (DUP && i16 >= 8)) continue;
-    float* row = part_o + ((row0 + r) * a.n_splits + split) * D;
+    float* row = direct ? a.out + (size_t)qrow[rt] * D : part_o + ((row0 + r) * a.n_splits + split) * D;
+    const float sc = direct ? (l_run[rt] > 0.0f ? 1.0f / l_run[rt] : 0.0f) : 1.0f;
     auto put4 = [&](float* p, float x0, float x1, float x2, float x3) {
-      *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+      *reinterpret_cast<float4*>(p) = make_float4(x0 * sc, x1 * sc, x2 * sc, x3 * sc);
     };
-    if (j4 == 0 && wv == 0) {
+    if (!direct && j4 == 0 && wv == 0) {
       float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
       ml[0] = m_run[rt]; ml[1] = l_run[rt];
     }
@@ -847,7 +854,7 @@ hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_combine_t<D>(plan, a, s);
+  return plan.n_splits > 1 ? launch_combine_t<D>(plan, a, s) : hipSuccess;   // one split wrote the output
 }
 
 template <int D, int RT, int VF>

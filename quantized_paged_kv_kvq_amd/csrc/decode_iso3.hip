@@ -302,7 +302,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   if (R == 0) return;
   if (p_begin >= p_end) {                           // nothing visible in this split
-    if ((int)threadIdx.x < RA) {
+    if (a.n_splits == 1) {                          // the only split writes the output: zeros
+      for (int i = (int)threadIdx.x; i < R * (D / 4); i += NW * 64)
+        *reinterpret_cast<float4*>(a.out + (size_t)decode_out_row(a, b, kvh, i / (D / 4), G, h0) * D +
+                                   4 * (i % (D / 4))) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else if ((int)threadIdx.x < R) {
       float* ml = part_ml + ((row0 + threadIdx.x) * a.n_splits + split) * 2;
       ml[0] = kNegInf; ml[1] = 0.0f;
     }
@@ -405,7 +409,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a
     l += cv[v] * lds_ml[(v * 2 + 1) * 64 + lane];
   }
   const bool writer = valid && !lo_col;
-  if (wv == 0 && g == 0 && writer) {
+  // with a single split the workgroup writes the normalised output itself (no combine follows)
+  const bool direct = a.n_splits == 1;
+  const float sc = direct ? (l > 0.0f ? 512.0f / l : 0.0f) : 512.0f;   // 512: the weights' 2^-9
+  if (!direct && wv == 0 && g == 0 && writer) {
     float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
     ml[0] = M; ml[1] = l;
   }
@@ -423,11 +430,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[k] += dpp_ror8(acc[k]);
       }
-      o[q] = acc * 512.0f;          // undo the 2^-9 of the weights
+      o[q] = acc * sc;
     }
     // tile 4tg + q, element i: head_dim 128 * (tg / 2) + 32g + 8i + 4 * (tg % 2) + q
     if (writer) {
-      float* row = part_o + ((row0 + r) * a.n_splits + split) * D + 128 * (tg >> 1) + 32 * g + 4 * (tg & 1);
+      float* row = (direct ? a.out + (size_t)((b * a.n_q + tq) * a.n_q_heads + hq) * D
+                           : part_o + ((row0 + r) * a.n_splits + split) * D) +
+                   128 * (tg >> 1) + 32 * g + 4 * (tg & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float u[4] = {o[0][i], o[1][i], o[2][i], o[3][i]};
@@ -447,7 +456,7 @@ hipError_t launch_iso3_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_
       <<<dim3((unsigned)plan.n_splits, a.hkv, a.batch), dim3(sh.nw * 64), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_decode_combine(D, plan, a, s);
+  return plan.n_splits > 1 ? launch_decode_combine(D, plan, a, s) : hipSuccess;   // one split wrote the output
 }
 
 template <int D, bool DUP, int SH = 0>

@@ -227,7 +227,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   if (R == 0) return;
   if (p_begin >= p_end) {                           // nothing visible in this split
-    if ((int)threadIdx.x < RA) {
+    if (a.n_splits == 1) {                          // the only split writes the output: zeros
+      for (int i = (int)threadIdx.x; i < R * (kD / 4); i += NW * 64)
+        *reinterpret_cast<float4*>(a.out + (size_t)decode_out_row(a, b, kvh, i / (kD / 4), G, h0) * kD +
+                                   4 * (i % (kD / 4))) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else if ((int)threadIdx.x < R) {
       float* ml = part_ml + ((row0 + threadIdx.x) * a.n_splits + split) * 2;
       ml[0] = kNegInf; ml[1] = 0.0f;
     }
@@ -380,15 +384,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
   }
   hadamard_rows<1>(Om, lane);
   if (!valid || lo_col) return;
-  if (w == 0) {
+  // with a single split the workgroup writes the normalised output itself (no combine follows)
+  const bool direct = a.n_splits == 1;
+  if (!direct && w == 0) {
     float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
     ml[0] = M; ml[1] = l;
   }
+  const float sc = direct ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f;
   // value (t, k) of Om: head_dim 32 * (t / 2) + 8w + 2k + (t & 1)
-  float* row = part_o + ((row0 + r) * a.n_splits + split) * kD;
+  float* row = direct ? a.out + (size_t)((b * a.n_q + tq) * a.n_q_heads + hq) * kD
+                      : part_o + ((row0 + r) * a.n_splits + split) * kD;
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
-    const f32x4 e = Om[0][2 * g], o = Om[0][2 * g + 1];
+    const f32x4 e = Om[0][2 * g] * sc, o = Om[0][2 * g + 1] * sc;
     *reinterpret_cast<float4*>(row + 32 * g + 8 * w) = make_float4(e[0], o[0], e[1], o[1]);
     *reinterpret_cast<float4*>(row + 32 * g + 8 * w + 4) = make_float4(e[2], o[2], e[3], o[3]);
   }
@@ -404,7 +412,7 @@ hipError_t launch_q4_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t 
     k_decode_q4<false, sh.nw, sh.ppw, sh.pd, sh.occ><<<grid, block, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_decode_combine(kD, plan, a, s);
+  return plan.n_splits > 1 ? launch_decode_combine(kD, plan, a, s) : hipSuccess;   // one split wrote the output
 }
 
 template <int SH = 0>

@@ -94,6 +94,13 @@ struct DecodeArgs {
   float quat[4];            // ISO3 stores: the rotation quaternion (w, x, y, z)
 };
 constexpr int kDecodeMaxFused = 4;     // new tokens per sequence of a fused decode
+
+// Output row (b, query token, query head) of row r of KV head kvh (G rows per token, heads from h0).
+__device__ __forceinline__ int decode_out_row(const DecodeArgs& a, int b, int kvh, int r, int G, int h0) {
+  const int t = r / G, i = r % G;
+  const int hq = a.g_uniform > 0 ? kvh * a.g_uniform + i : a.head_list[h0 + i];
+  return (b * a.n_q + t) * a.n_q_heads + hq;
+}
 constexpr int kIsoDecodeMaxRows = 16;  // query rows per KV head of an ISO3 decode
 
 struct DecodePlan {

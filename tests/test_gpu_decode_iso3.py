@@ -66,6 +66,13 @@ def test_iso3_decode_head_map_and_idle_kv_head():
     check(w, head_map=[2, 0, 2, 0, 2, 2])
 
 
+@pytest.mark.parametrize("lens", [[0, 5, 300], [0, 2000, 17]])
+def test_iso3_decode_empty_sequence(lens):
+    """A sequence with no cells gets zeros: written by its only split when the context takes one
+    split (no combine launch), by the combine otherwise."""
+    check(synth.ragged_decode("iso3", "iso3", lens, seed=72 + lens[1], n_q_heads=8, n_kv_heads=2, head_dim=128))
+
+
 def test_iso3_decode_last_kv_head_idle():
     """The last KV head serves no query head (its workgroups find no rows)."""
     w = synth.ragged_decode("iso3", "iso3", [70, 300], seed=70, n_q_heads=4, n_kv_heads=3, head_dim=128)

@@ -64,6 +64,13 @@ def test_q4_decode_head_map_and_idle_kv_heads():
     check(q4([33, 500], 84, n_q_heads=6, n_kv_heads=4), head_map=[2, 0, 2, 0, 2, 2])
 
 
+@pytest.mark.parametrize("lens", [[0, 5, 300], [0, 2000, 17]])
+def test_q4_decode_empty_sequence(lens):
+    """A sequence with no cells gets zeros, from its only split (one split: no combine launch) or
+    from the combine."""
+    check(q4(lens, 90 + lens[1], n_q_heads=8, n_kv_heads=2))
+
+
 def test_q4_decode_mha_and_mqa():
     check(q4([90, 260], 85, n_q_heads=4, n_kv_heads=4))
     check(q4([90, 260], 86, n_q_heads=8, n_kv_heads=1))

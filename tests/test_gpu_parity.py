@@ -141,6 +141,13 @@ def test_decode_edge_lengths_and_head_map():
     check_decode(w, head_map=hm)
 
 
+@pytest.mark.parametrize("fmt_v", ["int8", "q4h"])
+def test_decode_empty_sequence_multi_split(fmt_v):
+    """An empty sequence next to one that takes several splits: its zeros come from the combine."""
+    check_decode(synth.ragged_decode("int8", fmt_v, [0, 2000, 17], seed=73, n_q_heads=8, n_kv_heads=2,
+                                     head_dim=256))
+
+
 def test_decode_last_kv_head_idle():
     """The last KV head serves no query head (its workgroups find no rows)."""
     w = synth.ragged_decode("int8", "int8", [70, 300], seed=71, n_q_heads=4, n_kv_heads=3, head_dim=128)
