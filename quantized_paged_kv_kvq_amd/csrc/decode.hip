@@ -28,6 +28,8 @@
 //   * The NW waves of a workgroup merge (m, l, O) through LDS in one round (each wave merges and
 //     writes a share of the head_dim tiles); the workgroup writes one unnormalised partial.  A second kernel merges the splits with a log-sum-exp combine,
 //     normalises, applies H to k8v4 outputs and writes fp32 rows.
+#include <type_traits>
+
 #include "kvq_internal.h"
 #include "device_util.h"
 #include "int8_cell.h"
@@ -208,7 +210,7 @@ constexpr float kLazyLog2 = 8.0f;     // weights stay below 2^8 between rescalin
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
 // DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the bf16 hi part of
 // the softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both.
-template <int D, int RT, int VF, bool DUP, class QF>
+template <int D, int RT, int VF, bool DUP, bool V16, class QF>
 __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j4, bool lo_col, const int (&Lrow)[RT],
                                           const QF& qf, const float (&qmul)[RT],
                                           float (&m_run)[RT], float (&l_run)[RT],
@@ -217,13 +219,18 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
   constexpr int NVG = VF == 1 ? D / 64 : D / 32;
   constexpr int NT = D / 16;
   // k8v4 with more than 8 rows (verify windows; 16 rows per row tile, no duplicated columns):
-  // V enters the MFMA as the exact product (code - 8) x scale in two bf16 parts (a 4-bit code
-  // times an fp16 scale has at most 15 significant bits; the hi part keeps 8, the lo part the
-  // remaining 7), built once per page for all row tiles, and the softmax weights are split into
-  // hi / lo once per row tile instead of once per 32-value scale group.  The lo x lo product
-  // (below 2^-16 of the term) is left out.
+  // V enters the MFMA as a two-part product built once per page for all row tiles, and the softmax
+  // weights are split into hi / lo once per row tile instead of once per 32-value scale group; three
+  // K = 16 MFMAs take V hi x w hi, V lo x w hi and V hi x w lo (V lo x w lo is below 2^-16 of the
+  // term).  When every V scale of the wave's pages is 0 or at least 2^-10 (V16), the product is
+  // (code - 8) x scale / 16 in fp16 (hi = the rounded product, lo = its exact rounding error from one
+  // fma, exact since its last bit is at least 2^-24; the 1/16 keeps it below 2^15) from packed fp16
+  // arithmetic, against fp16 parts of 16 x the weights (a weight's parts miss it by at most 2^-29,
+  // with the largest weight at least 1); otherwise (code - 8) x scale in bf16 parts (a 4-bit code
+  // times an fp16 scale has at most 15 significant bits: 8 in hi, 7 in lo) against bf16 parts of the
+  // weights.
   constexpr bool Q4A = VF == 2 && !DUP;
-  s16x4 bqh[RT], bql[RT];
+  float pkr[RT][4];
 
   // ---- QK: S^T[token 4*j4 + k][row] per 64-group
   f32x4 acc[RT][NG];
@@ -275,7 +282,8 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
       }
     }
     if constexpr (Q4A) {
-      split_bf16(pk, bqh[rt], bql[rt]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pkr[rt][k] = pk[k];
       continue;
     }
 
@@ -330,43 +338,79 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
     }
   }
   if constexpr (Q4A) {
+    if constexpr (V16) {
+      f16x4 wh[RT], wl[RT];
 #pragma unroll
-    for (int g = 0; g < NVG; ++g) {
-      // byte k of the word: token 4*j4 + k; its low / high nibble: head_dim 32g + 2*i16 (+1)
-      const uint32_t w = word_of(pb.v[g >> 2], g & 3);
-      float sc[4], off[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        sc[k] = pb.vscale(k, g);
-        off[k] = -8.0f * sc[k];
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
-        asm volatile("" : "+v"(nib));         // keep the 4 codes as bytes: one byte-to-float each
-        uint32_t hb[4], lb[4];
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float x = fmaf((float)((nib >> (8 * k)) & 0xffu), sc[k], off[k]);   // exact
-          hb[k] = __float_as_uint(x) & 0xffff0000u;
-          lb[k] = __float_as_uint(x - __uint_as_float(hb[k]));                    // exact, low half 0
+          const float x = 16.0f * pkr[rt][k];
+          wh[rt][k] = (_Float16)x;
+          wl[rt][k] = (_Float16)(x - (float)wh[rt][k]);
         }
-        const s16x4 ahi = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
-                                                               __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)));
-        const s16x4 alo = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
-                                                               __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)));
-        // the three products as two K = 32 MFMAs: lane k-block j4 carries tokens 4*j4 .. +3 twice,
-        // [V hi | V lo] x [w hi | w hi], then [V hi | V hi] x [w lo | 0]
-        const uint2 hu = __builtin_bit_cast(uint2, ahi), lu = __builtin_bit_cast(uint2, alo);
-        const bf16x8 a2 = __builtin_bit_cast(bf16x8, u32x4{hu.x, hu.y, lu.x, lu.y});
-        const bf16x8 a3 = __builtin_bit_cast(bf16x8, u32x4{hu.x, hu.y, hu.x, hu.y});
+      const f16x2 mul = {(_Float16)0.0625f, (_Float16)0.0625f}, add = {(_Float16)-64.5f, (_Float16)-64.5f};
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const uint2 bu = __builtin_bit_cast(uint2, bqh[rt]), bl = __builtin_bit_cast(uint2, bql[rt]);
-          const bf16x8 b2 = __builtin_bit_cast(bf16x8, u32x4{bu.x, bu.y, bu.x, bu.y});
-          const bf16x8 b3 = __builtin_bit_cast(bf16x8, u32x4{bl.x, bl.y, 0u, 0u});
-          O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, O[rt][2 * g + e], 0, 0, 0);
-          O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, b3, O[rt][2 * g + e], 0, 0, 0);
+      for (int g = 0; g < NVG; ++g) {
+        // byte k of the word: token 4*j4 + k; its low / high nibble: head_dim 32g + 2*i16 (+1)
+        const uint32_t w = word_of(pb.v[g >> 2], g & 3);
+        // (scale of token 4*j4, of token 4*j4 + 1) and tokens + 2, + 3: half k * NVG + g of vs
+        const uint32_t hsel = (g & 1) ? 0x07060302u : 0x05040100u;
+        const f16x2 d01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(pb.vs[4 + (g >> 1)], pb.vs[g >> 1], hsel));
+        const f16x2 d23 =
+            __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(pb.vs[12 + (g >> 1)], pb.vs[8 + (g >> 1)], hsel));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
+          // [code, 0x64] per token pair reads 1024 + code; one packed fma gives (code - 8) / 16 exactly
+          const f16x2 c01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, nib, 0x04010400u)) * mul + add;
+          const f16x2 c23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, nib, 0x04030402u)) * mul + add;
+          const f16x2 h01 = c01 * d01, h23 = c23 * d23;
+          const f16x2 l01 = __builtin_elementwise_fma(c01, d01, -h01), l23 = __builtin_elementwise_fma(c23, d23, -h23);
+          const f16x4 ah = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(uint32_t, h01),
+                                                                __builtin_bit_cast(uint32_t, h23)));
+          const f16x4 al = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(uint32_t, l01),
+                                                                __builtin_bit_cast(uint32_t, l23)));
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, wh[rt], O[rt][2 * g + e], 0, 0, 0);
+            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(al, wh[rt], O[rt][2 * g + e], 0, 0, 0);
+            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, wl[rt], O[rt][2 * g + e], 0, 0, 0);
+          }
+        }
+      }
+    } else {                        // bf16 parts
+      s16x4 bqh[RT], bql[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) split_bf16(pkr[rt], bqh[rt], bql[rt]);
+#pragma unroll
+      for (int g = 0; g < NVG; ++g) {
+        const uint32_t w = word_of(pb.v[g >> 2], g & 3);
+        float sc[4], off[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          sc[k] = pb.vscale(k, g);
+          off[k] = -8.0f * sc[k];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float x = fmaf((float)((nib >> (8 * k)) & 0xffu), sc[k], off[k]);   // exact
+            hb[k] = __float_as_uint(x) & 0xffff0000u;
+            lb[k] = __float_as_uint(x - __uint_as_float(hb[k]));                    // exact, low half 0
+          }
+          const s16x4 ahi = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                                                                 __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)));
+          const s16x4 alo = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                                                                 __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)));
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bqh[rt], O[rt][2 * g + e], 0, 0, 0);
+            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bqh[rt], O[rt][2 * g + e], 0, 0, 0);
+            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bql[rt], O[rt][2 * g + e], 0, 0, 0);
+          }
         }
       }
     }
@@ -602,17 +646,53 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;          // pages of this wave, >= 1
     const int p_last = p0 + (n_mine - 1) * NW;
+    // page i of the wave sits in ring slot i % (PD + 1)
+    auto run = [&](auto v16_tag) {
+      constexpr bool V16 = decltype(v16_tag)::value;
 #pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      const int pc = p0 + i * NW;
-      if (i + PD < PPW) {
-        int page;
-        if constexpr (VF == 1) page = page_id(min(i + PD, n_mine - 1));
-        else page = clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1);
-        load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page, kvh, lane);
+      for (int i = 0; i < PPW; ++i) {
+        const int pc = p0 + i * NW;
+        if (i + PD < PPW) {
+          const int page = clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1);
+          load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page, kvh, lane);
+        }
+        page_step<D, RT, VF, DUP, V16>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
+        if (i + 1 >= n_mine) break;
       }
-      page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
-      if (i + 1 >= n_mine) break;
+    };
+    if constexpr (VF == 2 && !DUP) {
+      // The row-tile kernel's fp16 V parts need every V scale of the wave's pages to be 0 or at least
+      // 2^-10 (fp16 exponent field >= 5): one look at all of them up front (lane l reads the scales
+      // of tokens 4 (l % 4) .. +3 of the wave's page l / 4, NVG / 2 16-byte units), then one of two
+      // page loops.
+      static_assert(PPW <= 16, "the scale scan covers 16 pages");
+      const int pl = min(lane >> 2, n_mine - 1);
+      const int pid = clampi(bt_row[p0 + pl * NW], 0, a.num_pages - 1);
+      const uint4* vsp = reinterpret_cast<const uint4*>(a.v_scales + (((size_t)pid * a.hkv + kvh) * 16 + 4 * (lane & 3)) * NVG);
+      u16x2 mn = {0xffff, 0xffff};
+#pragma unroll
+      for (int c = 0; c < NVG / 2; ++c) {
+        const uint4 q = vsp[c];
+        const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, wd[e] & 0x7fff7fffu) - u16x2{1, 1});
+      }
+      if (__any(mn[0] < 0x13ffu || mn[1] < 0x13ffu)) run(std::false_type{});
+      else run(std::true_type{});
+    } else {
+#pragma unroll
+      for (int i = 0; i < PPW; ++i) {
+        const int pc = p0 + i * NW;
+        if (i + PD < PPW) {
+          int page;
+          if constexpr (VF == 1) page = page_id(min(i + PD, n_mine - 1));
+          else page = clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1);
+          load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page, kvh, lane);
+        }
+        page_step<D, RT, VF, DUP, false>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
+        if (i + 1 >= n_mine) break;
+      }
     }
   }
 

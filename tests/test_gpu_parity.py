@@ -172,11 +172,28 @@ def test_verify_k8v4_scaled():
 @pytest.mark.parametrize("n_q,hq,hkv", [(2, 16, 2), (3, 8, 2), (4, 16, 2), (1, 12, 1)])
 def test_verify_k8v4_row_tiles(n_q, hq, hkv):
     """k8v4 with more than 8 rows per KV head: one workgroup per split holds all rows in row tiles
-    of 16 (16, 12, 32 and 12 rows), V entering the MFMA as code x scale in two bf16 parts."""
+    of 16 (16, 12, 32 and 12 rows), V entering the MFMA as code x scale / 16 in two fp16 parts."""
     back = list(range(n_q - 1, -1, -1))
     w = synth.ragged_decode("int8", "q4h", [700, 33, 4000], seed=60 + n_q + hq, n_q=n_q, q_len_back=back,
                             n_q_heads=hq, n_kv_heads=hkv, head_dim=256)
     check_decode(w)
+
+
+@pytest.mark.parametrize("v_mul", [2.0e4, 1.0e-5])
+def test_verify_k8v4_row_tiles_value_range(v_mul):
+    """V far from unit scale through the row-tile kernel's fp16 V parts: scales near the top of fp16
+    (products up to 8 x d / 16) and scales so small the products are subnormal in fp16."""
+    w = synth.ragged_decode("int8", "q4h", [700, 33, 4000], seed=66, n_q=3, q_len_back=[2, 1, 0], n_q_heads=8,
+                            n_kv_heads=2, head_dim=256)
+    for b in range(w.batch):
+        w.v[b] = synth.bf16_bits(bf16_to_f32(w.v[b]) * np.float32(v_mul))
+    cache, pages, got = run_decode(w)
+    sk, sv = oracle_stores(w)
+    assert_slabs_equal(cache, sk, sv)
+    ref = oracle_decode(w, sk, sv)
+    scale = float(np.max(np.abs(ref)))
+    # the bound is relative to the output's magnitude (max-abs 1e-3 at unit scale)
+    assert_attention_close(got / scale, ref / scale)
 
 
 def test_decode_k8v4_single_query():
