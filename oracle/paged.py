@@ -3,7 +3,8 @@
 The cache is paged (FreeToken PR #398, section "What": a paged KV pool; strata
 PR #120, section "Tests": append/gather through a non-identity page table).
 Codes and scales live in separate arrays (strata PR #2698, section "What it
-does": int8 codes and their FP16 scales are separate buffers).
+does": int8 codes and their FP16 scales are separate buffers).  An unquantised
+FP32 store keeps its binary32 values in the code bytes and has no scales.
 
 Layout of one store (K or V) -- the same layout the library documents:
     codes  uint8   [num_pages][n_kv_heads][page_size][code_bytes]
@@ -17,10 +18,10 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import int8_g64, iso3, q4h
+from . import f32, int8_g64, iso3, q4h
 from .numerics import bf16_to_f32
 
-FORMATS = {"int8": int8_g64, "q4h": q4h, "iso3": iso3}
+FORMATS = {"int8": int8_g64, "q4h": q4h, "iso3": iso3, "f32": f32}
 
 
 def cell_bytes(fmt: str, head_dim: int):
@@ -58,6 +59,8 @@ def encode_cells(fmt: str, x_f32: np.ndarray, quat=None):
         return q4h.encode(x_f32)
     if fmt == "iso3":
         return iso3.encode(x_f32, quat)
+    if fmt == "f32":
+        return f32.encode(x_f32)
     raise ValueError(fmt)
 
 
@@ -70,6 +73,8 @@ def decode_cells(fmt: str, codes: np.ndarray, scales: np.ndarray, quat=None, rot
         return q4h.decode_rotated(codes, scales) if rotated else q4h.decode(codes, scales)
     if fmt == "iso3":
         return iso3.decode(codes, scales, quat)
+    if fmt == "f32":
+        return f32.decode(codes, scales)
     raise ValueError(fmt)
 
 
