@@ -51,6 +51,12 @@
  *                                 one 16-byte unit holds, for slot t, bytes 4w .. 4w+3 of four
  *                                 consecutive groups; a wave load covers a contiguous kilobyte);
  *     ISO3 store (K or V)         t * code_bytes + c   (token-major).
+ *     F32 K store                 as INT8_G64 K (16-byte chunks of 4 values, chunk-major)
+ *     F32 V store                 ((c / 4) * 16 + t) * 4 + c % 4
+ *                                 (head_dim-major: the 16 slots' values of one head_dim
+ *                                 index are 64 contiguous bytes, so 4 slots form 16 bytes).
+ *   An F32 store has no scales (its scales pointer may be NULL) and holds the values
+ *   themselves, which must be finite like the scales.
  *   Every fp16 scale in the slabs must be finite, including those of slots no append has
  *   written yet (zero-initialise new slabs): attention weighs cells past a sequence's length
  *   by exact zeros, which a NaN or infinite scale would turn into NaN.
@@ -85,6 +91,12 @@
  *                     stream (code i in bits 3i..3i+2, 8 codes per 3 bytes).
  *                     Dequant: conj(iso_quat) * centroid group, times the norm.
  *                     D % 128 == 0, D <= 512.  ([FT398] "What".)
+ *   KVQ_FMT_F32       4*D / 0.  Unquantised: value d of the cell as binary32 in code bytes
+ *                     4d .. 4d+3 (little-endian); written from bf16 inputs, the bf16 value
+ *                     exactly.  With an INT8_G64 store for the other side this is the
+ *                     single-store mode k8v32 (K int8, V FP32) or k32v8 (K FP32, V int8).
+ *                     D % 64 == 0, D <= 512.  ([ST2698] intro: FP32 caches of 2 KiB per
+ *                     cell per store; "What it does": `k8v32` / `k32v8` quantise one store.)
  *
  * Arithmetic contract of the encoders and of kvq_dequant_gather (F32 output):
  * binary32, one rounding per operation (no fused multiply-add), correctly rounded
@@ -119,7 +131,8 @@ typedef enum {
 typedef enum {
   KVQ_FMT_INT8_G64 = 1,
   KVQ_FMT_Q4_0_H256 = 2,
-  KVQ_FMT_ISO3 = 3
+  KVQ_FMT_ISO3 = 3,
+  KVQ_FMT_F32 = 4
 } kvq_fmt;
 
 typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1, KVQ_OUT_BF16 = 2 } kvq_out_dtype;
@@ -129,7 +142,8 @@ typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1, KVQ_OUT_BF16 = 2 } kvq_out_dtyp
 typedef struct {
   int32_t fmt;     /* kvq_fmt */
   void* codes;     /* uint8 [num_pages][n_kv_heads] tiles of page_size * code_bytes */
-  void* scales;    /* fp16  [num_pages][n_kv_heads][page_size][n_scales] */
+  void* scales;    /* fp16  [num_pages][n_kv_heads][page_size][n_scales]; unused (may be NULL)
+                      for an F32 store */
 } kvq_store;
 
 /* The cache: geometry plus the K and V stores ([ST120] "How": separate K/V pointers). */
@@ -185,7 +199,9 @@ kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages,
  * decode attention over packed cells) with head_dim 128 or 256 and n_q * (largest number
  * of query heads of one KV head) <= 16.  ISO3 outputs are in the original basis.  A
  * Q4_0_H256 K store needs a Q4_0_H256 V store and the same <= 16 rows ([ST2698] "Not in this
- * PR": q4_0 K and V, rotated, with the queries rotated). */
+ * PR": q4_0 K and V, rotated, with the queries rotated).  K and V stores that are each
+ * INT8_G64 or F32, at least one F32 ([ST2698] "What it does": k8v32 / k32v8, and the FP32
+ * default), take head_dim 128 or 256 and up to 32 rows. */
 kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
                            const void* q, int32_t n_q, int32_t n_q_heads,
                            const int32_t* q_lens, const int32_t* head_map,

@@ -11,6 +11,8 @@
 //              (orthonormal FWHT-256 of V, then q4_0 blocks of 32 with d = signed max-abs / -8).
 //   ISO3       FreeToken PR #398, "What" (per 128 values: L2-normalise, rotate each 4-group by a
 //              unit quaternion, nearest 3-bit Lloyd-Max centroid, corrected norm).
+//   F32        strata PR #2698, intro and "What it does" (the unquantised FP32 store of the
+//              single-store modes k8v32 / k32v8): the bf16 value widened to binary32, exact.
 #include "kvq_internal.h"
 #include "iso3_levels.h"
 #include "int8_cell.h"
@@ -82,6 +84,32 @@ __device__ __forceinline__ void append_int8(const AppendArgs& a, const uint16_t*
   }
   if ((part & 15) == 0)
     scales[(tile * KVQ_PAGE_SIZE + slot) * (D / 64) + (part >> 4)] = enc.scale_bits;
+}
+
+// ---------------------------------------------------------------------------------------------
+// F32: one thread writes 4 consecutive values of a cell.  K tiles take them as one 16-byte chunk;
+// V tiles keep each value's 16 slots together (4-byte stores, 64 bytes apart).
+__device__ __forceinline__ void append_f32(const AppendArgs& a, const uint16_t* __restrict__ x,
+                                           uint8_t* __restrict__ codes, int D, bool is_v, int block) {
+  const int tpc = D >> 2;                          // threads per cell
+  const int cpb = blockDim.x / tpc;                // cells per block
+  const int local = threadIdx.x / tpc;
+  const int part = threadIdx.x - local * tpc;      // values 4*part .. 4*part+3
+  const long cell = (long)block * cpb + local;
+  if (local >= cpb || cell >= (long)a.n_tok * a.hkv) return;
+  const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
+  const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * D + 4 * part);
+  const float v[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
+                      bf16_to_f32(raw.y >> 16)};
+  int page, slot;
+  locate(a, tok, page, slot);
+  uint8_t* base = codes + ((size_t)page * a.hkv + head) * KVQ_PAGE_SIZE * (4 * D);
+  if (!is_v) {
+    *reinterpret_cast<float4*>(base + k_tile_offset(16 * part, slot)) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(base + vf32_tile_offset(4 * (4 * part + e), slot)) = v[e];
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -238,7 +266,7 @@ __device__ __forceinline__ void append_iso3(const AppendArgs& a, const uint16_t*
 
 // Blocks needed by one store's encoder for n_tok tokens (256 threads per block).
 long blocks_for(int fmt, int D, long cells) {
-  if (fmt == KVQ_FMT_INT8_G64) {
+  if (fmt == KVQ_FMT_INT8_G64 || fmt == KVQ_FMT_F32) {
     const int cpb = 256 / (D / 4);
     return (cells + cpb - 1) / cpb;
   }
@@ -263,6 +291,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, StoreArgs k, Store
   const float quat[4] = {qw, qx, qy, qz};
   if (st.fmt == KVQ_FMT_INT8_G64) append_int8(a, st.x, st.codes, st.scales, D, st.is_v != 0, blockIdx.x);
   else if (st.fmt == KVQ_FMT_Q4_0_H256) append_q4h(a, st.x, st.codes, st.scales, st.is_v != 0, blockIdx.x);
+  else if (st.fmt == KVQ_FMT_F32) append_f32(a, st.x, st.codes, D, st.is_v != 0, blockIdx.x);
   else append_iso3(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
 }
 

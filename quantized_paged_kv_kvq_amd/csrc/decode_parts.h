@@ -1,12 +1,52 @@
-// Device pieces shared by the decode kernels whose V store is Hadamard-rotated q4_0 (strata PR #120,
-// "What"/"How": V rotated by H = H_256/16 and stored in q4_0; the attention output is rotated back):
-// the biased bf16 operand of 4 tokens' 4-bit codes, the hi / lo split of the softmax weights into
-// bf16 MFMA columns, and the back-rotation of a partial output row.
+// Device pieces shared by the decode kernels: exact MFMA operands of int8 codes (fp16 values; bf16
+// values biased by 128), the hi / lo split of the softmax weights into bf16 MFMA operands, and, for
+// Hadamard-rotated q4_0 stores (strata PR #120, "What"/"How": V rotated by H = H_256/16 and stored in
+// q4_0; the attention output is rotated back), the biased bf16 operand of 4 tokens' 4-bit codes and
+// the back-rotation of a partial output row.
 #pragma once
 
 #include "device_util.h"
 
 namespace kvq {
+
+// 8 int8 codes (two dwords, code e in byte e) -> 8 exact fp16 values.
+__device__ __forceinline__ f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;     // biased: code + 128
+  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u0, 0x05010400u)) - off;
+  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u0, 0x05030402u)) - off;
+  const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u1, 0x05010400u)) - off;
+  const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u1, 0x05030402u)) - off;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 4 int8 codes -> bf16 (code + 128), exact (integers below 256 have 8 significant bits).
+__device__ __forceinline__ s16x4 codes_to_bf16_biased(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const float f0 = (float)(u & 0xffu), f1 = (float)((u >> 8) & 0xffu), f2 = (float)((u >> 16) & 0xffu),
+              f3 = (float)(u >> 24);
+  const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+  return __builtin_bit_cast(s16x4, make_uint2(lo, hi));
+}
+
+// Split x into bf16 hi (truncated) + bf16 lo (rounded): hi + lo carries 16 significant bits.
+__device__ __forceinline__ void split_bf16(const float x[4], s16x4& hi, s16x4& lo) {
+  uint32_t hb[4];
+  float lf[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hb[e] = __float_as_uint(x[e]) & 0xffff0000u;
+    lf[e] = x[e] - __uint_as_float(hb[e]);
+  }
+  hi = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                                            __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)));
+  const uint32_t l0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[0]) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[1]) << 16);
+  const uint32_t l1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[2]) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lf[3]) << 16);
+  lo = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
+}
 
 // 4-bit codes of 4 tokens (one byte each; nibble picked by the caller) -> bf16 (128 + code), exact.
 __device__ __forceinline__ s16x4 nibbles_to_bf16_biased(uint32_t nib) {   // nib: 4 bytes, each 0..15

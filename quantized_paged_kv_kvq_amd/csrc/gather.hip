@@ -8,6 +8,7 @@
 //   Q4_0_H256  (code - 8) * d, rotated basis            (exact); with `unrotate`, H applied by
 //              binary32 butterflies of spans 1..128 and a final x 1/16
 //   ISO3       conj(q) * centroid group (left to right), then times the norm
+//   F32        the stored binary32 value
 #include "kvq_internal.h"
 #include "iso3_levels.h"
 
@@ -57,6 +58,29 @@ __global__ __launch_bounds__(256) void k_gather_int8(GatherArgs g, const uint8_t
     const int d = 4 * part + e;
     const size_t off = tile * KVQ_PAGE_SIZE * D + (is_v ? v_tile_offset(d, slot) : k_tile_offset(d, slot));
     v[e] = (float)(int8_t)codes[off] * s;
+  }
+  store4(out, ((size_t)i * g.hkv + head) * D + 4 * part, v, dtype);
+}
+
+// F32 (K or V tile order): one thread per 4 consecutive values of a cell.
+__global__ __launch_bounds__(256) void k_gather_f32(GatherArgs g, const uint8_t* __restrict__ codes, int D, int is_v,
+                                                    void* out, int dtype) {
+  const int tpc = D / 4;
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long cells = (long)g.count * g.hkv;
+  if (t >= cells * tpc) return;
+  const long cell = t / tpc;
+  const int part = (int)(t % tpc);
+  const int i = (int)(cell / g.hkv), head = (int)(cell % g.hkv);
+  int slot;
+  const size_t tile = tile_of(g, i, head, slot);
+  const uint8_t* base = codes + tile * KVQ_PAGE_SIZE * (4 * D);
+  float v[4];
+  if (!is_v) {
+    const float4 q = *reinterpret_cast<const float4*>(base + k_tile_offset(16 * part, slot));
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+    for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const float*>(base + vf32_tile_offset(4 * (4 * part + e), slot));
   }
   store4(out, ((size_t)i * g.hkv + head) * D + 4 * part, v, dtype);
 }
@@ -137,6 +161,10 @@ hipError_t launch_gather(int fmt, bool is_v, const uint8_t* codes, const uint16_
     const long threads = cells * (D / 4);
     k_gather_int8<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, is_v ? 1 : 0,
                                                                                out, out_dtype);
+  } else if (fmt == KVQ_FMT_F32) {
+    const long threads = cells * (D / 4);
+    k_gather_f32<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, D, is_v ? 1 : 0, out,
+                                                                              out_dtype);
   } else if (fmt == KVQ_FMT_Q4_0_H256) {
     k_gather_q4h<<<dim3((unsigned)((cells + 3) / 4)), dim3(256), 0, s>>>(g, codes, scales, is_v ? 1 : 0, out,
                                                                           out_dtype, unrotate ? 1 : 0);

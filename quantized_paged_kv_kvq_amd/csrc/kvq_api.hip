@@ -24,7 +24,9 @@ kvq_status fail(kvq_status st, const char* fmt, ...) {
   return st;
 }
 
-bool fmt_known(int f) { return f == KVQ_FMT_INT8_G64 || f == KVQ_FMT_Q4_0_H256 || f == KVQ_FMT_ISO3; }
+bool fmt_known(int f) {
+  return f == KVQ_FMT_INT8_G64 || f == KVQ_FMT_Q4_0_H256 || f == KVQ_FMT_ISO3 || f == KVQ_FMT_F32;
+}
 
 // Geometry rules of a store format (the pages validate head_dim at config time with a message).
 kvq_status check_store_fmt(int fmt, int D, bool is_v) {
@@ -35,6 +37,8 @@ kvq_status check_store_fmt(int fmt, int D, bool is_v) {
     return fail(KVQ_ERR_UNSUPPORTED, "Q4_0_H256 needs head_dim == 256 (got %d)", D);
   if (fmt == KVQ_FMT_ISO3 && (D % 128 != 0 || D > KVQ_MAX_HEAD_DIM))
     return fail(KVQ_ERR_UNSUPPORTED, "ISO3 needs head_dim %% 128 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
+  if (fmt == KVQ_FMT_F32 && (D % 64 != 0 || D > KVQ_MAX_HEAD_DIM))
+    return fail(KVQ_ERR_UNSUPPORTED, "F32 needs head_dim %% 64 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
   return KVQ_OK;
 }
 
@@ -50,8 +54,10 @@ kvq_status check_cache(const kvq_cache* c) {
 kvq_status check_store(const kvq_cache* c, const kvq_store& s, bool is_v) {
   kvq_status st = check_store_fmt(s.fmt, c->head_dim, is_v);
   if (st != KVQ_OK) return st;
-  if (!s.codes || !s.scales) return fail(KVQ_ERR_NULL, "%s store has a NULL codes or scales pointer", is_v ? "V" : "K");
-  if (((uintptr_t)s.codes & 15) || ((uintptr_t)s.scales & 15))
+  const bool scaled = s.fmt != KVQ_FMT_F32;          // an F32 store has no scales
+  if (!s.codes || (scaled && !s.scales))
+    return fail(KVQ_ERR_NULL, "%s store has a NULL codes or scales pointer", is_v ? "V" : "K");
+  if (((uintptr_t)s.codes & 15) || (scaled && ((uintptr_t)s.scales & 15)))
     return fail(KVQ_ERR_SHAPE, "%s store slabs must be 16-byte aligned", is_v ? "V" : "K");
   return KVQ_OK;
 }
@@ -144,6 +150,7 @@ int32_t kvq_cell_bytes(int32_t fmt, int32_t D, int32_t* code_bytes, int32_t* n_s
   if (fmt == KVQ_FMT_INT8_G64 && D > 0 && D % 64 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = D; ns = D / 64; }
   if (fmt == KVQ_FMT_Q4_0_H256 && D == 256) { cb = D / 2; ns = D / 32; }
   if (fmt == KVQ_FMT_ISO3 && D > 0 && D % 128 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = D / 128 * 48; ns = D / 128; }
+  if (fmt == KVQ_FMT_F32 && D > 0 && D % 64 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = 4 * D; ns = 0; }
   if (cb < 0) return -1;
   if (code_bytes) *code_bytes = cb;
   if (n_scales) *n_scales = ns;
@@ -204,10 +211,15 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if ((st = check_store_fmt(cache->v.fmt, cache->head_dim, true)) != KVQ_OK) return st;
   const bool iso = cache->k.fmt == KVQ_FMT_ISO3 && cache->v.fmt == KVQ_FMT_ISO3;
   const bool q4k = cache->k.fmt == KVQ_FMT_Q4_0_H256;
+  const bool kf = cache->k.fmt == KVQ_FMT_F32, vf = cache->v.fmt == KVQ_FMT_F32;
+  const bool f32 = kf || vf;      // single-store modes (and F32 for both)
+  if (f32 && ((!kf && cache->k.fmt != KVQ_FMT_INT8_G64) || (!vf && cache->v.fmt != KVQ_FMT_INT8_G64)))
+    return fail(KVQ_ERR_UNSUPPORTED, "decode with an F32 store needs the other store F32 or INT8_G64 (got formats %d / %d)",
+                cache->k.fmt, cache->v.fmt);
   if (q4k && cache->v.fmt != KVQ_FMT_Q4_0_H256)
     return fail(KVQ_ERR_UNSUPPORTED, "decode over a Q4_0_H256 K store needs a Q4_0_H256 V store (got %d)",
                 cache->v.fmt);
-  if (!iso && !q4k && cache->k.fmt != KVQ_FMT_INT8_G64)
+  if (!iso && !q4k && !f32 && cache->k.fmt != KVQ_FMT_INT8_G64)
     return fail(KVQ_ERR_UNSUPPORTED,
                 "decode needs an INT8_G64 or Q4_0_H256 K store, or ISO3 K and V stores (got formats %d / %d)",
                 cache->k.fmt, cache->v.fmt);
@@ -216,6 +228,8 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   const int D = cache->head_dim;
   if (iso && D != 128 && D != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "ISO3 decode supports head_dim 128 or 256 (got %d)", D);
+  if (f32 && D != 128 && D != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode with an F32 store supports head_dim 128 or 256 (got %d)", D);
   if (D != 64 && D != 128 && D != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "decode supports head_dim 64, 128 or 256 (got %d)", D);
   if (batch < 1 || batch > 65535) return fail(KVQ_ERR_SHAPE, "batch %d out of range", batch);
@@ -235,6 +249,7 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
                 kQ4DecodeMaxRows);
   *plan = iso   ? plan_decode_iso3(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
           : q4k ? plan_decode_q4(cache->n_kv_heads, batch, max_pages, n_q * max_g)
+          : f32 ? plan_decode_f32(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
                 : plan_decode(cache->v.fmt, D, cache->n_kv_heads, batch, max_pages, n_q * max_g);
   if (plan->n_splits > decode_max_splits())
     return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d needs %d context splits; decode supports %d", max_pages,
@@ -301,6 +316,10 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   if (cache->k.fmt == KVQ_FMT_ISO3)
     return hip_status(launch_decode_iso3(cache->head_dim, plan, a, hs), "decode launch");
   if (cache->k.fmt == KVQ_FMT_Q4_0_H256) return hip_status(launch_decode_q4(plan, a, hs), "decode launch");
+  if (cache->k.fmt == KVQ_FMT_F32 || cache->v.fmt == KVQ_FMT_F32)
+    return hip_status(launch_decode_f32(cache->k.fmt == KVQ_FMT_F32, cache->v.fmt == KVQ_FMT_F32, cache->head_dim,
+                                        plan, a, hs),
+                      "decode launch");
   return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, hs), "decode launch");
 }
 

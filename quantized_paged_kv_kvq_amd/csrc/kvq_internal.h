@@ -15,10 +15,13 @@ namespace kvq {
 //   Q4_0_H256 K stores: 16-byte units, unit (c/64, (c/4)%4, t) holds bytes 4w .. 4w+3 (w = (c/4)%4) of
 //     the four 32-value groups c/64*4 .. +3 of slot t -- one wave load covers a contiguous kilobyte
 //   ISO3 stores: token-major
+//   F32 K stores: as INT8_G64 K (a 16-byte chunk holds 4 values); F32 V stores: head_dim-major, the 16
+//     slots of one head_dim index are 64 contiguous bytes
 __host__ __device__ inline int k_tile_offset(int c, int t) { return ((c >> 4) * 16 + t) * 16 + (c & 15); }
 __host__ __device__ inline int k4_tile_offset(int c, int t) {
   return (((c >> 6) * 4 + ((c >> 2) & 3)) * 16 + t) * 16 + ((c >> 4) & 3) * 4 + (c & 3);
 }
+__host__ __device__ inline int vf32_tile_offset(int c, int t) { return ((c >> 2) * 16 + t) * 4 + (c & 3); }
 __host__ __device__ inline int v_tile_offset(int c, int t) {
   return ((((c >> 6) << 4) | (c & 15)) * 4 + (t >> 2)) * 16 + ((c >> 4) & 3) * 4 + (t & 3);
 }
@@ -127,6 +130,10 @@ hipError_t launch_decode_iso3(int head_dim, const DecodePlan& plan, const Decode
 constexpr int kQ4DecodeMaxRows = 16;
 DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode_q4(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
+// K and V stores each INT8_G64 or F32, at least one F32 (head_dim 128 or 256, up to 32 rows per KV head)
+DecodePlan plan_decode_f32(int head_dim, int hkv, int batch, int max_pages, int max_rows);
+hipError_t launch_decode_f32(bool k_f32, bool v_f32, int head_dim, const DecodePlan& plan, const DecodeArgs& a,
+                             hipStream_t s);
 
 // Extend over an ISO3 prefix: one row per (new token, query head); rows of KV head j use the query
 // heads head_list[head_off[j] .. head_off[j+1]).

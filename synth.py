@@ -63,7 +63,7 @@ class Workload:
     the step attends unquantised and packs afterwards.
     """
     name: str
-    fmt_k: str                      # 'int8' | 'q4h' | 'iso3'
+    fmt_k: str                      # 'int8' | 'q4h' | 'iso3' | 'f32'
     fmt_v: str
     batch: int
     n_q_heads: int
@@ -214,6 +214,30 @@ def moe_q4h_decode(ctx: int = 131072, seed: int = 8, n_q_heads: int = 16, n_kv_h
     q = normal_bf16(rng, (1, 1, n_q_heads, head_dim))
     w = Workload("moe_q4h_decode", "q4h", "q4h", 1, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
                  lens, table, npages, [k], [v], q)
+    w.meta["outlier_channels"] = [int(c) for c in outliers]
+    return w
+
+
+def moe_single_store_decode(fmt_k: str = "int8", fmt_v: str = "f32", ctx: int = 131072, seed: int = 9,
+                            n_q: int = 1, n_q_heads: int = 16, n_kv_heads: int = 2, head_dim: int = 256,
+                            n_outliers: int = 4) -> Workload:
+    """moe_int8_decode's layer (GQA 16:2, head_dim 256, K outlier channels x20) with one store
+    quantised and the other FP32 (strata PR #2698: `k8v32` / `k32v8`, measured there at 64K on a
+    Qwen3.6-35B-A3B model with a 2-token MTP draft); n_q > 1 makes a verify window of causal lengths
+    ctx - n_q + 1 .. ctx."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([ctx], np.int32)
+    table, npages = _page_table(rng, lens, PAGE_SIZE, identity=False)
+    outliers = np.sort(rng.choice(head_dim, size=n_outliers, replace=False)) if n_outliers else []
+    k = normal_bf16(rng, (ctx, n_kv_heads, head_dim), outlier_channels=outliers)
+    v = normal_bf16(rng, (ctx, n_kv_heads, head_dim))
+    q = normal_bf16(rng, (1, n_q, n_q_heads, head_dim))
+    name = {("int8", "f32"): "moe_k8v32_decode", ("f32", "int8"): "moe_k32v8_decode"}.get((fmt_k, fmt_v),
+                                                                                          "moe_f32_decode")
+    w = Workload(name, fmt_k, fmt_v, 1, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE, lens, table, npages, [k], [v],
+                 q, n_q=n_q, n_step=n_q)
+    if n_q > 1:
+        w.q_lens = (ctx - n_q + 1 + np.arange(n_q, dtype=np.int32))[None, :]
     w.meta["outlier_channels"] = [int(c) for c in outliers]
     return w
 

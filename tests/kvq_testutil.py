@@ -86,6 +86,8 @@ def tile_index(layout: str, cb: int) -> np.ndarray:
         return ((c >> 4) * 16 + t) * 16 + (c & 15)
     if layout == "v_quad":
         return ((((c >> 6) << 4) | (c & 15)) * 4 + (t >> 2)) * 16 + ((c >> 4) & 3) * 4 + (t & 3)
+    if layout == "v_f32":
+        return ((c >> 2) * 16 + t) * 4 + (c & 3)
     if layout == "k_q4":
         return (((c >> 6) * 4 + ((c >> 2) & 3)) * 16 + t) * 16 + ((c >> 4) & 3) * 4 + (c & 3)
     raise ValueError(layout)
@@ -96,6 +98,8 @@ def store_layout(fmt: str, which: str) -> str:
         return "token"
     if fmt == "q4h" and which == "k":
         return "k_q4"
+    if fmt == "f32" and which == "v":
+        return "v_f32"
     return "k_chunk" if which == "k" else "v_quad"
 
 

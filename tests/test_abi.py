@@ -32,14 +32,14 @@ def test_library_exports_every_declared_symbol():
 
 
 @pytest.mark.parametrize("fmt,D", [("int8", 64), ("int8", 128), ("int8", 256), ("int8", 512), ("q4h", 256),
-                                   ("iso3", 128), ("iso3", 256)])
+                                   ("iso3", 128), ("iso3", 256), ("f32", 64), ("f32", 256), ("f32", 512)])
 def test_cell_bytes_match_oracle(fmt, D):
     assert kvq.cell_bytes(fmt, D) == opaged.cell_bytes(fmt, D)
 
 
 def test_cell_bytes_refuses_bad_geometry():
     L = kvq.lib()
-    for fmt, D in ((1, 100), (2, 128), (3, 64), (9, 128), (1, 1024)):
+    for fmt, D in ((1, 100), (2, 128), (3, 64), (9, 128), (1, 1024), (4, 96), (4, 1024)):
         assert L.kvq_cell_bytes(fmt, D, None, None) == -1
 
 
@@ -95,6 +95,23 @@ def test_decode_validation_errors():
     assert decode(c, make_pages()) == 1
 
 
+def test_decode_validation_single_store_modes():
+    """k8v32 / k32v8 / F32 for both: head_dim 128 or 256, up to 32 rows, the other store int8; an
+    F32 store needs no scales pointer."""
+    assert decode(make_cache(fk=4, fv=2), make_pages()) == 3            # F32 K with q4_0 V
+    assert decode(make_cache(fk=3, fv=4, D=128), make_pages()) == 3     # ISO3 K with F32 V
+    assert decode(make_cache(fk=1, fv=4, D=64), make_pages(), hq=4) == 3    # head_dim 64
+    assert decode(make_cache(fk=4, fv=1, D=512), make_pages(), hq=4) == 3   # head_dim 512
+    assert decode(make_cache(fk=4, fv=1), make_pages(), n_q=5) == 3     # 40 rows > 32
+    c = make_cache(fk=4, fv=4)
+    c.k = kvq.KvqStore(4, FAKE, None)
+    c.v = kvq.KvqStore(4, FAKE, None)
+    assert decode(c, make_pages(), ws=None) == 4                        # reaches the workspace check
+    c = make_cache(fk=1, fv=4)
+    c.k = kvq.KvqStore(1, FAKE, None)                                   # int8 K still needs its scales
+    assert decode(c, make_pages()) == 1
+
+
 def decode_append(c, p, n_q=1, hq=16, k=FAKE, v=FAKE, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
     L = kvq.lib()
     return L.kvq_decode_attn_append(ctypes.byref(c) if c else None, ctypes.byref(p) if p else None, k, v, q, n_q, hq,
@@ -125,6 +142,12 @@ def test_decode_workspace_size_formula():
     assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (128 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 2, 16, None) == 2 * 128 * 16 * (128 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 3, 16, None) == 0
+    for fk, fv in ((1, 4), (4, 1), (4, 4)):
+        f = make_cache(fk=fk, fv=fv)
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 3, 16, None) == 2 * 128 * 24 * (256 + 2) * 4
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 4, 16, None) == 2 * 128 * 32 * (256 + 2) * 4
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 5, 16, None) == 0
     q4 = make_cache(fk=2, fv=2)
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 2, 16, None) == 2 * 128 * 16 * (256 + 2) * 4
@@ -141,6 +164,10 @@ def test_append_and_gather_validation_errors():
     assert A(c, p, FAKE, FAKE, 5, ts=None) == 1
     assert A(make_cache(fk=2, D=128), p, FAKE, None, 5) == 3   # q4_0 K store needs head_dim 256
     assert A(make_cache(page=32), p, FAKE, FAKE, 1) == 3
+    assert A(make_cache(fk=4, fv=4, D=96), p, FAKE, FAKE, 1) == 3   # F32 store: head_dim % 64
+    f = make_cache(fk=4, fv=4)
+    f.k = kvq.KvqStore(4, FAKE + 8, None)
+    assert A(f, p, FAKE, None, 1) == 2                 # misaligned codes
     G = lambda c, p, which, seq, start, count, dt=0, out=FAKE: L.kvq_dequant_gather(
         ctypes.byref(c), ctypes.byref(p), which, seq, start, count, dt, 0, out, None)
     assert G(c, p, 2, 0, 0, 1) == 2

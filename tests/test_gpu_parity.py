@@ -92,7 +92,8 @@ def test_append_special_values():
 
 
 @pytest.mark.parametrize("fmt,D,fk", [("int8", 128, None), ("int8", 256, None), ("q4h", 256, "int8"), ("q4h", 256, "q4h"),
-                                      ("iso3", 128, None), ("iso3", 256, None)])
+                                      ("iso3", 128, None), ("iso3", 256, None), ("f32", 256, None),
+                                      ("f32", 128, "int8"), ("int8", 256, "f32")])
 def test_gather_bitexact(fmt, D, fk):
     import torch
     import quantized_paged_kv_kvq_amd as kvq
