@@ -18,10 +18,10 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import f32, int8_g64, iso3, q4h
+from . import f32, int8_g64, iso3, iso4, q4h
 from .numerics import bf16_to_f32
 
-FORMATS = {"int8": int8_g64, "q4h": q4h, "iso3": iso3, "f32": f32}
+FORMATS = {"int8": int8_g64, "q4h": q4h, "iso3": iso3, "iso4": iso4, "f32": f32}
 
 
 def cell_bytes(fmt: str, head_dim: int):
@@ -59,6 +59,8 @@ def encode_cells(fmt: str, x_f32: np.ndarray, quat=None):
         return q4h.encode(x_f32)
     if fmt == "iso3":
         return iso3.encode(x_f32, quat)
+    if fmt == "iso4":
+        return iso4.encode(x_f32, quat)
     if fmt == "f32":
         return f32.encode(x_f32)
     raise ValueError(fmt)
@@ -73,6 +75,8 @@ def decode_cells(fmt: str, codes: np.ndarray, scales: np.ndarray, quat=None, rot
         return q4h.decode_rotated(codes, scales) if rotated else q4h.decode(codes, scales)
     if fmt == "iso3":
         return iso3.decode(codes, scales, quat)
+    if fmt == "iso4":
+        return iso4.decode(codes, scales, quat)
     if fmt == "f32":
         return f32.decode(codes, scales)
     raise ValueError(fmt)
