@@ -58,6 +58,8 @@ def make_workload(name: str):
         return synth.moe_iso3_decode(ctx=131072)
     if name == "moe_q4h_decode":
         return synth.moe_q4h_decode(ctx=131072)
+    if name == "moe_iso4_decode":
+        return synth.moe_iso3_decode(ctx=131072, fmt="iso4")
     if name == "moe_k8v32_decode":
         return synth.moe_single_store_decode("int8", "f32", ctx=131072)
     if name == "moe_k32v8_decode":
@@ -471,7 +473,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "/".join(dict.fromkeys({"int8": "int8", "q4h": "q4", "iso3": "iso3", "f32": "f32"}[f]
+        "dtype": "/".join(dict.fromkeys({"int8": "int8", "q4h": "q4", "iso3": "iso3", "iso4": "iso4", "f32": "f32"}[f]
                                           for f in (w.fmt_k, w.fmt_v))),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": int(w.seq_lens.max()), "n_q": w.n_q,

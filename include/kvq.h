@@ -50,7 +50,7 @@
  *                                 (attention contracts K over head_dim in 32-value scale groups:
  *                                 one 16-byte unit holds, for slot t, bytes 4w .. 4w+3 of four
  *                                 consecutive groups; a wave load covers a contiguous kilobyte);
- *     ISO3 store (K or V)         t * code_bytes + c   (token-major).
+ *     ISO3 / ISO4 store (K or V)  t * code_bytes + c   (token-major).
  *     F32 K store                 as INT8_G64 K (16-byte chunks of 4 values, chunk-major)
  *     F32 V store                 ((c / 4) * 16 + t) * 4 + c % 4
  *                                 (head_dim-major: the 16 slots' values of one head_dim
@@ -91,6 +91,14 @@
  *                     stream (code i in bits 3i..3i+2, 8 codes per 3 bytes).
  *                     Dequant: conj(iso_quat) * centroid group, times the norm.
  *                     D % 128 == 0, D <= 512.  ([FT398] "What".)
+ *   KVQ_FMT_ISO4      D/128*64 / 2*D/128.  ISO3's steps with the sixteen levels of the 16-level
+ *                     Lloyd-Max quantiser of a standard normal variable
+ *                     {+-0.1284, +-0.3880, +-0.6568, +-0.9423, +-1.2562, +-1.6180, +-2.0690,
+ *                     +-2.7326}/sqrt(128) (the page gives only the size: 4.25 bits per value,
+ *                     68 B per 128-value block); 4-bit codes, code i in bits 4i..4i+3 (byte j:
+ *                     code 2j in the low nibble); the corrected norm n / ||chosen centroids||
+ *                     is kept in binary32, its bytes in the block's two 16-bit scale slots
+ *                     (low half first).  D % 128 == 0, D <= 512.  ([FT398] "What".)
  *   KVQ_FMT_F32       4*D / 0.  Unquantised: value d of the cell as binary32 in code bytes
  *                     4d .. 4d+3 (little-endian); written from bf16 inputs, the bf16 value
  *                     exactly.  With an INT8_G64 store for the other side this is the
@@ -132,7 +140,8 @@ typedef enum {
   KVQ_FMT_INT8_G64 = 1,
   KVQ_FMT_Q4_0_H256 = 2,
   KVQ_FMT_ISO3 = 3,
-  KVQ_FMT_F32 = 4
+  KVQ_FMT_F32 = 4,
+  KVQ_FMT_ISO4 = 5
 } kvq_fmt;
 
 typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1, KVQ_OUT_BF16 = 2 } kvq_out_dtype;
@@ -197,7 +206,8 @@ kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages,
  * 128 or 256, and a K store of format INT8_G64 (the V store may be INT8_G64 or
  * Q4_0_H256); or ISO3 K and V stores ([FT398] "Pull request overview": the ISO backend's
  * decode attention over packed cells) with head_dim 128 or 256 and n_q * (largest number
- * of query heads of one KV head) <= 16.  ISO3 outputs are in the original basis.  A
+ * of query heads of one KV head) <= 16, or likewise ISO4 K and V stores (norms up to 65504).
+ * ISO3 / ISO4 outputs are in the original basis.  A
  * Q4_0_H256 K store needs a Q4_0_H256 V store and the same <= 16 rows ([ST2698] "Not in this
  * PR": q4_0 K and V, rotated, with the queries rotated).  K and V stores that are each
  * INT8_G64 or F32, at least one F32 ([ST2698] "What it does": k8v32 / k32v8, and the FP32

@@ -11,6 +11,8 @@
 //              (orthonormal FWHT-256 of V, then q4_0 blocks of 32 with d = signed max-abs / -8).
 //   ISO3       FreeToken PR #398, "What" (per 128 values: L2-normalise, rotate each 4-group by a
 //              unit quaternion, nearest 3-bit Lloyd-Max centroid, corrected norm).
+//   ISO4       FreeToken PR #398, "What" (the 4-bit sibling: sixteen levels, nibble codes, the
+//              corrected norm kept in binary32).
 //   F32        strata PR #2698, intro and "What it does" (the unquantised FP32 store of the
 //              single-store modes k8v32 / k32v8): the bf16 value widened to binary32, exact.
 #include "kvq_internal.h"
@@ -203,12 +205,16 @@ __device__ __forceinline__ float hamilton(int comp, float w, float x, float y, f
   return comp == 0 ? r0 : comp == 1 ? r1 : comp == 2 ? r2 : r3;
 }
 
+template <int BITS>
+__device__ __forceinline__ float iso_level(int k) { return BITS == 3 ? kIsoLevels[k] : kIso4Levels[k]; }
+
+template <int BITS>
 __device__ __forceinline__ int nearest_centroid(float r) {
   int best = 0;
-  float bd = fabsf(r - kIsoLevels[0]);
+  float bd = fabsf(r - iso_level<BITS>(0));
 #pragma unroll
-  for (int k = 1; k < 8; ++k) {
-    const float dk = fabsf(r - kIsoLevels[k]);
+  for (int k = 1; k < (1 << BITS); ++k) {
+    const float dk = fabsf(r - iso_level<BITS>(k));
     if (dk < bd) { bd = dk; best = k; }
   }
   return best;
@@ -220,9 +226,12 @@ __device__ __forceinline__ float rotate_component(float u, int lane, float w, fl
   return hamilton(lane & 3, w, x, y, z, a, b, c, d);
 }
 
-__device__ __forceinline__ void append_iso3(const AppendArgs& a, const uint16_t* __restrict__ x,
-                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ norms, int D,
-                                            const float quat[4], int block) {
+// ISO4 (FreeToken PR #398, "What": the 4-bit sibling) takes the same steps with sixteen levels,
+// packs the codes as nibbles and keeps the corrected norm in binary32 (two 16-bit scale slots).
+template <int BITS>
+__device__ __forceinline__ void append_iso(const AppendArgs& a, const uint16_t* __restrict__ x,
+                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ norms, int D,
+                                           const float quat[4], int block) {
   __shared__ uint8_t lds_codes[4][128];
   const float qw = quat[0], qx = quat[1], qy = quat[2], qz = quat[3];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -241,8 +250,8 @@ __device__ __forceinline__ void append_iso3(const AppendArgs& a, const uint16_t*
   const float u1 = n > 0.0f ? x1 / n : 0.0f;
   const float r0 = rotate_component(u0, lane, qw, qx, qy, qz);
   const float r1 = rotate_component(u1, lane, qw, qx, qy, qz);
-  const int c0 = nearest_centroid(r0), c1 = nearest_centroid(r1);
-  const float k0 = kIsoLevels[c0], k1 = kIsoLevels[c1];
+  const int c0 = nearest_centroid<BITS>(r0), c1 = nearest_centroid<BITS>(r1);
+  const float k0 = iso_level<BITS>(c0), k1 = iso_level<BITS>(c1);
   const float cn = sqrtf(halving_sum128(k0 * k0, k1 * k1));
   const float norm = n / cn;
 
@@ -253,15 +262,22 @@ __device__ __forceinline__ void append_iso3(const AppendArgs& a, const uint16_t*
   int page, slot;
   locate(a, tok, page, slot);
   const size_t tile = (size_t)page * a.hkv + head;
-  const int cb = nb * 48;
-  if (lane < 48) {
-    const int t = lane / 3;                          // 3 bytes hold codes 8t .. 8t+7
-    uint32_t word = 0;
+  if constexpr (BITS == 3) {
+    const int cb = nb * 48;
+    if (lane < 48) {
+      const int t = lane / 3;                          // 3 bytes hold codes 8t .. 8t+7
+      uint32_t word = 0;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) word |= (uint32_t)lds_codes[wv][8 * t + m] << (3 * m);
-    codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 48 + lane] = (uint8_t)(word >> (8 * (lane % 3)));
+      for (int m = 0; m < 8; ++m) word |= (uint32_t)lds_codes[wv][8 * t + m] << (3 * m);
+      codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 48 + lane] = (uint8_t)(word >> (8 * (lane % 3)));
+    }
+    if (lane == 0) norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = f32_to_f16_bits(norm);
+  } else {
+    const int cb = nb * 64;                            // byte j: code 2j (low nibble), 2j + 1 (high)
+    codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 64 + lane] =
+        (uint8_t)(lds_codes[wv][2 * lane] | (lds_codes[wv][2 * lane + 1] << 4));
+    if (lane == 0) reinterpret_cast<float*>(norms)[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = norm;
   }
-  if (lane == 0) norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = f32_to_f16_bits(norm);
 }
 
 // Blocks needed by one store's encoder for n_tok tokens (256 threads per block).
@@ -270,7 +286,7 @@ long blocks_for(int fmt, int D, long cells) {
     const int cpb = 256 / (D / 4);
     return (cells + cpb - 1) / cpb;
   }
-  if (fmt == KVQ_FMT_Q4_0_H256) return (cells + 3) / 4;
+  if (fmt == KVQ_FMT_Q4_0_H256) return (cells + 3) / 4;   // ISO3 / ISO4 below: one wave per block
   return (cells * (D / 128) + 3) / 4;
 }
 
@@ -292,7 +308,8 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, StoreArgs k, Store
   if (st.fmt == KVQ_FMT_INT8_G64) append_int8(a, st.x, st.codes, st.scales, D, st.is_v != 0, blockIdx.x);
   else if (st.fmt == KVQ_FMT_Q4_0_H256) append_q4h(a, st.x, st.codes, st.scales, st.is_v != 0, blockIdx.x);
   else if (st.fmt == KVQ_FMT_F32) append_f32(a, st.x, st.codes, D, st.is_v != 0, blockIdx.x);
-  else append_iso3(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
+  else if (st.fmt == KVQ_FMT_ISO4) append_iso<4>(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
+  else append_iso<3>(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
 }
 
 }  // namespace

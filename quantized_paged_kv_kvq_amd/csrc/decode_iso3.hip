@@ -30,6 +30,13 @@
 //   * Online softmax in base 2 with a lazily moved reference max; the waves merge (m, l, O) through
 //     LDS; the partial is rotated back by conj(r) and goes to the log-sum-exp combine shared with the
 //     other decode kernels.
+//
+// ISO4 (FreeToken PR #398, "What": the 4-bit sibling, 68 B per 128-value block) runs through the same
+// kernel with BITS = 4: sixteen levels, a 256-entry pair table indexed by one code byte (two
+// nibbles), 16 code bytes per lane and block for QK and one code word per token for PV, and binary32
+// norms.
+#include <type_traits>
+
 #include "kvq_internal.h"
 #include "device_util.h"
 #include "iso3_levels.h"
@@ -40,7 +47,10 @@ namespace {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
-constexpr int kBlockBytes = 48;                 // codes of one 128-value block
+template <int BITS>
+constexpr int kBlockBytes = BITS == 3 ? 48 : 64;   // codes of one 128-value block
+template <int BITS>
+constexpr float kLevelScale = BITS == 3 ? kIsoLevelScale : kIso4LevelScale;
 constexpr float kLazy = 8.0f;                   // weights stay below 2^8 between rescalings
 // weight x V norm enters fp16 as 2^-9 * p * n / S: with p < 2^8 and n <= 65504 it stays finite
 constexpr float kPScale = 1.0f / 512.0f;
@@ -78,14 +88,20 @@ __device__ __forceinline__ void quat_mul(const float a[4], const float u[4], flo
 }
 
 // One page of one KV head as a lane holds it (NB = head_dim / 128 blocks per cell).
-template <int NB>
+template <int BITS, int NB>
 struct IsoPage {
-  u32x3 k[NB];           // K: token lane % 16, codes 32 * (lane / 16) .. +31 of block b
-  u32x2 v[NB][4];        // V: token 4 * (lane / 16) + j, the 8 bytes holding codes 8 * (lane % 16) .. +7
-  uint32_t kn[2 * NB];   // fp16 norms of tokens 4 * (lane / 16) + j, block b: half j * NB + b
-  uint32_t vn[2 * NB];
-  __device__ __forceinline__ float knorm(int j, int b) const { return half_at(kn, j * NB + b); }
-  __device__ __forceinline__ float vnorm(int j, int b) const { return half_at(vn, j * NB + b); }
+  static constexpr int NW = BITS == 3 ? 2 * NB : 4 * NB;
+  std::conditional_t<BITS == 3, u32x3, u32x4> k[NB];   // K: token lane % 16, codes 32 * (lane / 16) .. +31 of block b
+  // V: token 4 * (lane / 16) + j: ISO3 the 8 bytes holding codes 8 * (lane % 16) .. +7, ISO4 the word of them
+  std::conditional_t<BITS == 3, u32x2, uint32_t> v[NB][4];
+  uint32_t kn[NW];       // norms of tokens 4 * (lane / 16) + j, block b: ISO3 fp16 half j * NB + b, ISO4 word
+  uint32_t vn[NW];
+  __device__ __forceinline__ float knorm(int j, int b) const {
+    return BITS == 3 ? half_at(kn, j * NB + b) : __uint_as_float(kn[j * NB + b]);
+  }
+  __device__ __forceinline__ float vnorm(int j, int b) const {
+    return BITS == 3 ? half_at(vn, j * NB + b) : __uint_as_float(vn[j * NB + b]);
+  }
   static __device__ __forceinline__ float half_at(const uint32_t* w, int i) {
     const uint32_t x = w[i >> 1];
     return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (x >> 16) : (x & 0xffffu))));
@@ -93,41 +109,60 @@ struct IsoPage {
 };
 
 // Loads of one (page, KV head) tile through buffer resources spanning just that tile, so that no
-// lane can read outside it.  v_off: byte offset, inside a block's 48 bytes, of the two words that
-// hold this lane's 24 V code bits.
-template <int NB>
-__device__ __forceinline__ void load_iso_page(IsoPage<NB>& pb, const DecodeArgs& a, int page, int kvh, int g, int n,
-                                              int v_off) {
-  constexpr int CB = NB * kBlockBytes;
+// lane can read outside it.  v_off: byte offset, inside a block's code bytes, of the two words (ISO3)
+// or the word (ISO4) that hold this lane's V code bits.
+template <int BITS, int NB>
+__device__ __forceinline__ void load_iso_page(IsoPage<BITS, NB>& pb, const DecodeArgs& a, int page, int kvh, int g,
+                                              int n, int v_off) {
+  constexpr int BB = kBlockBytes<BITS>;
+  constexpr int CB = NB * BB;
+  constexpr int NS = BITS == 3 ? NB : 2 * NB;       // 16-bit norm slots per (token, KV head)
   const size_t tile = (size_t)page * a.hkv + kvh;
   const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_codes + tile * (16 * CB)), (short)0,
                                                     16 * CB, kBufFlags);
   const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_codes + tile * (16 * CB)), (short)0,
                                                     16 * CB, kBufFlags);
-  const auto rkn = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k_scales + tile * (16 * NB)), (short)0,
-                                                     32 * NB, kBufFlags);
-  const auto rvn = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_scales + tile * (16 * NB)), (short)0,
-                                                     32 * NB, kBufFlags);
+  const auto rkn = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k_scales + tile * (16 * NS)), (short)0,
+                                                     32 * NS, kBufFlags);
+  const auto rvn = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v_scales + tile * (16 * NS)), (short)0,
+                                                     32 * NS, kBufFlags);
+  if constexpr (BITS == 3) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    pb.k[b] = __builtin_amdgcn_raw_buffer_load_b96(rk, n * CB + kBlockBytes * b + 12 * g, 0, kNonTemporal);
+    for (int b = 0; b < NB; ++b)
+      pb.k[b] = __builtin_amdgcn_raw_buffer_load_b96(rk, n * CB + BB * b + 12 * g, 0, kNonTemporal);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pb.v[b][j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (4 * g + j) * CB + kBlockBytes * b + v_off, 0,
-                                                        kNonTemporal);
-  if constexpr (NB == 1) {
-    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rkn, 8 * g, 0, kNonTemporal);
-    const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(rvn, 8 * g, 0, kNonTemporal);
-    pb.kn[0] = x[0]; pb.kn[1] = x[1];
-    pb.vn[0] = y[0]; pb.vn[1] = y[1];
-  } else {
-    static_assert(NB == 2, "head_dim 128 or 256");
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rkn, 16 * g, 0, kNonTemporal);
-    const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rvn, 16 * g, 0, kNonTemporal);
+      for (int j = 0; j < 4; ++j)
+        pb.v[b][j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (4 * g + j) * CB + BB * b + v_off, 0, kNonTemporal);
+    if constexpr (NB == 1) {
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rkn, 8 * g, 0, kNonTemporal);
+      const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(rvn, 8 * g, 0, kNonTemporal);
+      pb.kn[0] = x[0]; pb.kn[1] = x[1];
+      pb.vn[0] = y[0]; pb.vn[1] = y[1];
+    } else {
+      static_assert(NB == 2, "head_dim 128 or 256");
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rkn, 16 * g, 0, kNonTemporal);
+      const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rvn, 16 * g, 0, kNonTemporal);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { pb.kn[e] = x[e]; pb.vn[e] = y[e]; }
+      for (int e = 0; e < 4; ++e) { pb.kn[e] = x[e]; pb.vn[e] = y[e]; }
+    }
+  } else {                          // ISO4: 16 code bytes per lane and block, binary32 norms
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      pb.k[b] = __builtin_amdgcn_raw_buffer_load_b128(rk, n * CB + BB * b + 16 * g, 0, kNonTemporal);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pb.v[b][j] = __builtin_amdgcn_raw_buffer_load_b32(rv, (4 * g + j) * CB + BB * b + v_off, 0, kNonTemporal);
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {  // words j * NB + b of tokens 4g .. 4g+3: 16 NB contiguous bytes
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rkn, 16 * NB * g + 16 * h, 0, kNonTemporal);
+      const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rvn, 16 * NB * g + 16 * h, 0, kNonTemporal);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { pb.kn[4 * h + e] = x[e]; pb.vn[4 * h + e] = y[e]; }
+    }
   }
 }
 
@@ -141,8 +176,8 @@ __device__ __forceinline__ void split_f16(const float x[4], f16x4& hi, f16x4& lo
 }
 
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
-template <int D, bool DUP>
-__device__ __forceinline__ void iso_page_step(const IsoPage<D / 128>& pb, int p, int g, bool lo_col, int Lrow,
+template <int BITS, int D, bool DUP>
+__device__ __forceinline__ void iso_page_step(const IsoPage<BITS, D / 128>& pb, int p, int g, bool lo_col, int Lrow,
                                               const f16x8 (&qb)[D / 128][4][DUP ? 1 : 2], float qmul, int v_shift,
                                               const uint32_t* lut, float& m_run, float& l_run, f32x4 (&O)[D / 16]) {
   constexpr int NB = D / 128;
@@ -150,14 +185,23 @@ __device__ __forceinline__ void iso_page_step(const IsoPage<D / 128>& pb, int p,
   f32x4 acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const u32x3 w = pb.k[b];
-    // the 32 codes as four 24-bit groups of 8 (code i of the group in bits 3i .. 3i+2)
-    const uint32_t x[4] = {w[0], __builtin_amdgcn_alignbit(w[1], w[0], 24), __builtin_amdgcn_alignbit(w[2], w[1], 16),
-                           w[2] >> 8};
+    const auto w = pb.k[b];
+    // the 32 codes as four groups of 8: ISO3 24-bit groups (code i of the group in bits 3i .. 3i+2),
+    // ISO4 words (code i in bits 4i .. 4i+3)
+    uint32_t x[4];
+    if constexpr (BITS == 3) {
+      x[0] = w[0]; x[1] = __builtin_amdgcn_alignbit(w[1], w[0], 24); x[2] = __builtin_amdgcn_alignbit(w[2], w[1], 16);
+      x[3] = w[2] >> 8;
+    } else {
+      x[0] = w[0]; x[1] = w[1]; x[2] = w[2]; x[3] = w[3];
+    }
     acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 pairs = {lut[x[c] & 63u], lut[(x[c] >> 6) & 63u], lut[(x[c] >> 12) & 63u], lut[(x[c] >> 18) & 63u]};
+      constexpr int PB = 2 * BITS;                // bits of a code pair = the table index
+      constexpr uint32_t PM = (1u << PB) - 1;
+      const u32x4 pairs = {lut[x[c] & PM], lut[(x[c] >> PB) & PM], lut[(x[c] >> (2 * PB)) & PM],
+                           lut[(x[c] >> (3 * PB)) & PM]};
       const f16x8 av = __builtin_bit_cast(f16x8, pairs);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[b][c][0], acc[b], 0, 0, 0);
       if constexpr (!DUP) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[b][c][1], acc[b], 0, 0, 0);
@@ -199,21 +243,27 @@ __device__ __forceinline__ void iso_page_step(const IsoPage<D / 128>& pb, int p,
   for (int b = 0; b < NB; ++b) {
     float w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = pk[k] * (pb.vnorm(k, b) * (kPScale / kIsoLevelScale));
+    for (int k = 0; k < 4; ++k) w[k] = pk[k] * (pb.vnorm(k, b) * (kPScale / kLevelScale<BITS>));
     f16x4 bh, bl;
     split_f16(w, bh, bl);
     const f16x4 bp = lo_col ? bl : bh;
-    uint32_t xv[4];               // 24 code bits of token 4g + j: head_dim 8n .. 8n+7 of block b
+    uint32_t xv[4];               // code bits of token 4g + j: head_dim 8n .. 8n+7 of block b
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint64_t pair = ((uint64_t)pb.v[b][j][1] << 32) | pb.v[b][j][0];
-      xv[j] = (uint32_t)(pair >> v_shift);
+      if constexpr (BITS == 3) {
+        const uint64_t pair = ((uint64_t)pb.v[b][j][1] << 32) | pb.v[b][j][0];
+        xv[j] = (uint32_t)(pair >> v_shift);
+      } else {
+        xv[j] = pb.v[b][j];
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {   // dims 8n + 2kk (tile 2kk) and 8n + 2kk + 1 (tile 2kk + 1)
+      constexpr int PB = 2 * BITS;
+      constexpr uint32_t PM = (1u << PB) - 1;
       uint32_t L[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L[j] = lut[(xv[j] >> (6 * kk)) & 63u];
+      for (int j = 0; j < 4; ++j) L[j] = lut[(xv[j] >> (PB * kk)) & PM];
       const f16x4 a0 = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(L[1], L[0], 0x05040100u),
                                                        __builtin_amdgcn_perm(L[3], L[2], 0x05040100u)});
       const f16x4 a1 = __builtin_bit_cast(f16x4, u32x2{__builtin_amdgcn_perm(L[1], L[0], 0x07060302u),
@@ -233,21 +283,30 @@ __device__ __forceinline__ void iso_page_step(const IsoPage<D / 128>& pb, int p,
   }
 }
 
-template <int D, bool DUP, int NW, int PPW, int PD, int OCC>
-__global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a) {
+template <int BITS, int D, bool DUP, int NW, int PPW, int PD, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a) {
   constexpr int NB = D / 128;
   constexpr int NT = D / 16;                        // PV tiles of 16 head_dim rows
   constexpr int NTG = NT / 4;                       // groups of 4 tiles: 4 consecutive head_dim per lane
-  __shared__ uint32_t lut[64];
+  constexpr int NL = 1 << (2 * BITS);               // pair-table entries
+  __shared__ uint32_t lut[NL];
   __shared__ __align__(16) float mrg[NW * (NT * 64 * 4 + 2 * 64)];
 
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  if (threadIdx.x < 64) {
-    const _Float16 lo = (_Float16)(kIsoLevelScale * kIsoLevels[threadIdx.x & 7]);
-    const _Float16 hi = (_Float16)(kIsoLevelScale * kIsoLevels[threadIdx.x >> 3]);
-    lut[threadIdx.x] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  if constexpr (BITS == 3) {
+    if (threadIdx.x < 64) {
+      const _Float16 lo = (_Float16)(kIsoLevelScale * kIsoLevels[threadIdx.x & 7]);
+      const _Float16 hi = (_Float16)(kIsoLevelScale * kIsoLevels[threadIdx.x >> 3]);
+      lut[threadIdx.x] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+  } else {
+    for (int i = (int)threadIdx.x; i < NL; i += NW * 64) {
+      const _Float16 lo = (_Float16)(kIso4LevelScale * kIso4Levels[i & 15]);
+      const _Float16 hi = (_Float16)(kIso4LevelScale * kIso4Levels[i >> 4]);
+      lut[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
   }
 
   // ---- rows of this KV head: row r is (query token r / G, query head r % G of the head's list)
@@ -283,12 +342,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a
 #pragma unroll
       for (int c = 0; c < 4; ++c) qraw[bb][c] = *reinterpret_cast<const uint4*>(qp + 128 * bb + 8 * c);
   }
-  const int v_e = min((24 * n) >> 5, 10);           // first of the two words holding V bits 24n .. 24n+23
-  const int v_off = 4 * v_e, v_shift = 24 * n - 32 * v_e;
-  IsoPage<NB> buf[PD + 1];
+  // ISO3: first of the two words holding V bits 24n .. 24n+23; ISO4: the word of bits 32n .. 32n+31
+  const int v_e = BITS == 3 ? min((24 * n) >> 5, 10) : n;
+  const int v_off = 4 * v_e, v_shift = BITS == 3 ? 24 * n - 32 * v_e : 0;
+  IsoPage<BITS, NB> buf[PD + 1];
 #pragma unroll
   for (int i = 0; i < PD && i < PPW; ++i)
-    load_iso_page<NB>(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, g, n, v_off);
+    load_iso_page<BITS, NB>(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, g, n, v_off);
 
   int Lmax = 0;
   for (int t = 0; t < a.n_q; ++t)
@@ -356,7 +416,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a
             qb[bb][c][1][j] = lo;
           }
         }
-    qmul = ldexpf(a.scale_log2 * (1.0f / kIsoLevelScale), -ex);
+    qmul = ldexpf(a.scale_log2 * (1.0f / kLevelScale<BITS>), -ex);
   }
 
   float m_run = kNegInf, l_run = 0.0f;
@@ -376,9 +436,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a
     for (int i = 0; i < PPW; ++i) {
       const int pc = p0 + i * NW;
       if (i + PD < PPW)
-        load_iso_page<NB>(buf[(i + PD) % (PD + 1)], a, clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1),
-                          kvh, g, n, v_off);
-      iso_page_step<D, DUP>(buf[i % (PD + 1)], pc, g, lo_col, Lrow, qb, qmul, v_shift, lut, m_run, l_run, O);
+        load_iso_page<BITS, NB>(buf[(i + PD) % (PD + 1)], a,
+                                clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1), kvh, g, n, v_off);
+      iso_page_step<BITS, D, DUP>(buf[i % (PD + 1)], pc, g, lo_col, Lrow, qb, qmul, v_shift, lut, m_run, l_run, O);
       if (i + 1 >= n_mine) break;
     }
   }
@@ -447,22 +507,32 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso3(const DecodeArgs a
   }
 }
 
-template <int D, bool DUP, int SH>
+template <int BITS, int D, bool DUP, int SH>
 hipError_t launch_iso3_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   constexpr IsoShape sh = kIsoShapes[SH];
   constexpr int pd = D == 128 ? sh.pd : (sh.pd + 1) / 2;
-  k_decode_iso3<D, DUP, sh.nw, sh.ppw, pd, sh.occ>
+  k_decode_iso<BITS, D, DUP, sh.nw, sh.ppw, pd, sh.occ>
       <<<dim3((unsigned)plan.n_splits, a.hkv, a.batch), dim3(sh.nw * 64), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return plan.n_splits > 1 ? launch_decode_combine(D, plan, a, s) : hipSuccess;   // one split wrote the output
 }
 
-template <int D, bool DUP, int SH = 0>
+template <int BITS, int D, bool DUP, int SH = 0>
 hipError_t launch_iso3_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   if constexpr (SH + 1 < kNumIsoShapes)
-    if (plan.shape != SH) return launch_iso3_shape<D, DUP, SH + 1>(plan, a, s);
-  return launch_iso3_t<D, DUP, SH>(plan, a, s);
+    if (plan.shape != SH) return launch_iso3_shape<BITS, D, DUP, SH + 1>(plan, a, s);
+  return launch_iso3_t<BITS, D, DUP, SH>(plan, a, s);
+}
+
+template <int BITS>
+hipError_t launch_iso_bits(int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+  const bool dup = plan.rows <= 8;
+  switch (D) {
+    case 128: return dup ? launch_iso3_shape<BITS, 128, true>(plan, a, s) : launch_iso3_shape<BITS, 128, false>(plan, a, s);
+    case 256: return dup ? launch_iso3_shape<BITS, 256, true>(plan, a, s) : launch_iso3_shape<BITS, 256, false>(plan, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -486,13 +556,8 @@ DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int
   return p;
 }
 
-hipError_t launch_decode_iso3(int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
-  const bool dup = plan.rows <= 8;
-  switch (D) {
-    case 128: return dup ? launch_iso3_shape<128, true>(plan, a, s) : launch_iso3_shape<128, false>(plan, a, s);
-    case 256: return dup ? launch_iso3_shape<256, true>(plan, a, s) : launch_iso3_shape<256, false>(plan, a, s);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_decode_iso(int bits, int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+  return bits == 4 ? launch_iso_bits<4>(D, plan, a, s) : launch_iso_bits<3>(D, plan, a, s);
 }
 
 }  // namespace kvq

@@ -7,7 +7,7 @@
 //   INT8_G64   code * scale                            (exact in binary32)
 //   Q4_0_H256  (code - 8) * d, rotated basis            (exact); with `unrotate`, H applied by
 //              binary32 butterflies of spans 1..128 and a final x 1/16
-//   ISO3       conj(q) * centroid group (left to right), then times the norm
+//   ISO3/ISO4  conj(q) * centroid group (left to right), then times the norm
 //   F32        the stored binary32 value
 #include "kvq_internal.h"
 #include "iso3_levels.h"
@@ -118,10 +118,12 @@ __global__ __launch_bounds__(256) void k_gather_q4h(GatherArgs g, const uint8_t*
 }
 
 
-// ISO3: one thread per 4-value group; the group's 12 code bits start at bit 12*g of its block.
-__global__ __launch_bounds__(256) void k_gather_iso3(GatherArgs g, const uint8_t* __restrict__ codes,
-                                                     const uint16_t* __restrict__ norms, int D, float qw, float qx,
-                                                     float qy, float qz, void* out, int dtype) {
+// ISO3 / ISO4: one thread per 4-value group; the group's 12 (16) code bits start at bit 12*g (16*g)
+// of its block.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_gather_iso(GatherArgs g, const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ norms, int D, float qw, float qx,
+                                                    float qy, float qz, void* out, int dtype) {
   const int gpc = D / 4;                          // groups per cell
   const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long cells = (long)g.count * g.hkv;
@@ -133,19 +135,28 @@ __global__ __launch_bounds__(256) void k_gather_iso3(GatherArgs g, const uint8_t
   int slot;
   const size_t tile = tile_of(g, i, head, slot);
   const int nb = D / 128;
-  const uint8_t* cb = codes + (tile * KVQ_PAGE_SIZE + slot) * (nb * 48) + blk * 48;
-  const int bit = 12 * gi;
-  const uint32_t w16 = (uint32_t)cb[bit >> 3] | ((uint32_t)cb[(bit >> 3) + 1] << 8);
-  const uint32_t bits = w16 >> (bit & 7);
-  const float a = kIsoLevels[bits & 7], b = kIsoLevels[(bits >> 3) & 7], c = kIsoLevels[(bits >> 6) & 7],
-              d = kIsoLevels[(bits >> 9) & 7];
+  float a, b, c, d, nrm;
+  if constexpr (BITS == 3) {
+    const uint8_t* cb = codes + (tile * KVQ_PAGE_SIZE + slot) * (nb * 48) + blk * 48;
+    const int bit = 12 * gi;
+    const uint32_t w16 = (uint32_t)cb[bit >> 3] | ((uint32_t)cb[(bit >> 3) + 1] << 8);
+    const uint32_t bits = w16 >> (bit & 7);
+    a = kIsoLevels[bits & 7]; b = kIsoLevels[(bits >> 3) & 7]; c = kIsoLevels[(bits >> 6) & 7];
+    d = kIsoLevels[(bits >> 9) & 7];
+    nrm = f16_bits_to_f32(norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk]);
+  } else {
+    const uint8_t* cb = codes + (tile * KVQ_PAGE_SIZE + slot) * (nb * 64) + blk * 64 + 2 * gi;
+    const uint32_t bits = (uint32_t)cb[0] | ((uint32_t)cb[1] << 8);
+    a = kIso4Levels[bits & 15]; b = kIso4Levels[(bits >> 4) & 15]; c = kIso4Levels[(bits >> 8) & 15];
+    d = kIso4Levels[bits >> 12];
+    nrm = reinterpret_cast<const float*>(norms)[(tile * KVQ_PAGE_SIZE + slot) * nb + blk];
+  }
   // conjugate quaternion (w, -x, -y, -z), same evaluation order as the encoder's product
   const float w = qw, x = -qx, y = -qy, z = -qz;
   const float r0 = ((w * a - x * b) - y * c) - z * d;
   const float r1 = ((w * b + x * a) + y * d) - z * c;
   const float r2 = ((w * c - x * d) + y * a) + z * b;
   const float r3 = ((w * d + x * c) - y * b) + z * a;
-  const float nrm = f16_bits_to_f32(norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk]);
   const float v[4] = {r0 * nrm, r1 * nrm, r2 * nrm, r3 * nrm};
   store4(out, ((size_t)i * g.hkv + head) * D + 4 * grp, v, dtype);
 }
@@ -168,10 +179,16 @@ hipError_t launch_gather(int fmt, bool is_v, const uint8_t* codes, const uint16_
   } else if (fmt == KVQ_FMT_Q4_0_H256) {
     k_gather_q4h<<<dim3((unsigned)((cells + 3) / 4)), dim3(256), 0, s>>>(g, codes, scales, is_v ? 1 : 0, out,
                                                                           out_dtype, unrotate ? 1 : 0);
+  } else if (fmt == KVQ_FMT_ISO4) {
+    const long threads = cells * (D / 4);
+    k_gather_iso<4><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, quat[0],
+                                                                                 quat[1], quat[2], quat[3], out,
+                                                                                 out_dtype);
   } else {
     const long threads = cells * (D / 4);
-    k_gather_iso3<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, quat[0], quat[1],
-                                                                               quat[2], quat[3], out, out_dtype);
+    k_gather_iso<3><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(g, codes, scales, D, quat[0],
+                                                                                 quat[1], quat[2], quat[3], out,
+                                                                                 out_dtype);
   }
   return hipGetLastError();
 }

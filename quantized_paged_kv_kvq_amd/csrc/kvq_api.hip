@@ -25,7 +25,8 @@ kvq_status fail(kvq_status st, const char* fmt, ...) {
 }
 
 bool fmt_known(int f) {
-  return f == KVQ_FMT_INT8_G64 || f == KVQ_FMT_Q4_0_H256 || f == KVQ_FMT_ISO3 || f == KVQ_FMT_F32;
+  return f == KVQ_FMT_INT8_G64 || f == KVQ_FMT_Q4_0_H256 || f == KVQ_FMT_ISO3 || f == KVQ_FMT_F32 ||
+         f == KVQ_FMT_ISO4;
 }
 
 // Geometry rules of a store format (the pages validate head_dim at config time with a message).
@@ -37,6 +38,8 @@ kvq_status check_store_fmt(int fmt, int D, bool is_v) {
     return fail(KVQ_ERR_UNSUPPORTED, "Q4_0_H256 needs head_dim == 256 (got %d)", D);
   if (fmt == KVQ_FMT_ISO3 && (D % 128 != 0 || D > KVQ_MAX_HEAD_DIM))
     return fail(KVQ_ERR_UNSUPPORTED, "ISO3 needs head_dim %% 128 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
+  if (fmt == KVQ_FMT_ISO4 && (D % 128 != 0 || D > KVQ_MAX_HEAD_DIM))
+    return fail(KVQ_ERR_UNSUPPORTED, "ISO4 needs head_dim %% 128 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
   if (fmt == KVQ_FMT_F32 && (D % 64 != 0 || D > KVQ_MAX_HEAD_DIM))
     return fail(KVQ_ERR_UNSUPPORTED, "F32 needs head_dim %% 64 == 0 and <= %d (got %d)", KVQ_MAX_HEAD_DIM, D);
   return KVQ_OK;
@@ -151,6 +154,7 @@ int32_t kvq_cell_bytes(int32_t fmt, int32_t D, int32_t* code_bytes, int32_t* n_s
   if (fmt == KVQ_FMT_Q4_0_H256 && D == 256) { cb = D / 2; ns = D / 32; }
   if (fmt == KVQ_FMT_ISO3 && D > 0 && D % 128 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = D / 128 * 48; ns = D / 128; }
   if (fmt == KVQ_FMT_F32 && D > 0 && D % 64 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = 4 * D; ns = 0; }
+  if (fmt == KVQ_FMT_ISO4 && D > 0 && D % 128 == 0 && D <= KVQ_MAX_HEAD_DIM) { cb = D / 128 * 64; ns = D / 64; }
   if (cb < 0) return -1;
   if (code_bytes) *code_bytes = cb;
   if (n_scales) *n_scales = ns;
@@ -209,7 +213,8 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->k.fmt, cache->head_dim, false)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->v.fmt, cache->head_dim, true)) != KVQ_OK) return st;
-  const bool iso = cache->k.fmt == KVQ_FMT_ISO3 && cache->v.fmt == KVQ_FMT_ISO3;
+  const bool iso = (cache->k.fmt == KVQ_FMT_ISO3 && cache->v.fmt == KVQ_FMT_ISO3) ||
+                   (cache->k.fmt == KVQ_FMT_ISO4 && cache->v.fmt == KVQ_FMT_ISO4);
   const bool q4k = cache->k.fmt == KVQ_FMT_Q4_0_H256;
   const bool kf = cache->k.fmt == KVQ_FMT_F32, vf = cache->v.fmt == KVQ_FMT_F32;
   const bool f32 = kf || vf;      // single-store modes (and F32 for both)
@@ -221,13 +226,15 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
                 cache->v.fmt);
   if (!iso && !q4k && !f32 && cache->k.fmt != KVQ_FMT_INT8_G64)
     return fail(KVQ_ERR_UNSUPPORTED,
-                "decode needs an INT8_G64 or Q4_0_H256 K store, or ISO3 K and V stores (got formats %d / %d)",
+                "decode needs an INT8_G64 or Q4_0_H256 K store, or ISO3 / ISO4 K and V stores (got formats %d / %d)",
                 cache->k.fmt, cache->v.fmt);
-  if (!iso && cache->v.fmt == KVQ_FMT_ISO3)
-    return fail(KVQ_ERR_UNSUPPORTED, "decode over an ISO3 V store needs an ISO3 K store");
+  if (!iso && (cache->k.fmt == KVQ_FMT_ISO3 || cache->k.fmt == KVQ_FMT_ISO4 || cache->v.fmt == KVQ_FMT_ISO3 ||
+               cache->v.fmt == KVQ_FMT_ISO4))
+    return fail(KVQ_ERR_UNSUPPORTED, "decode over ISO3 / ISO4 stores needs K and V of the same ISO format (got %d / %d)",
+                cache->k.fmt, cache->v.fmt);
   const int D = cache->head_dim;
   if (iso && D != 128 && D != 256)
-    return fail(KVQ_ERR_UNSUPPORTED, "ISO3 decode supports head_dim 128 or 256 (got %d)", D);
+    return fail(KVQ_ERR_UNSUPPORTED, "ISO3 / ISO4 decode supports head_dim 128 or 256 (got %d)", D);
   if (f32 && D != 128 && D != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "decode with an F32 store supports head_dim 128 or 256 (got %d)", D);
   if (D != 64 && D != 128 && D != 256)
@@ -242,7 +249,7 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
     return fail(KVQ_ERR_UNSUPPORTED, "n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
                 KVQ_MAX_ROWS_PER_KV_HEAD);
   if (iso && (long)n_q * max_g > kIsoDecodeMaxRows)
-    return fail(KVQ_ERR_UNSUPPORTED, "ISO3 decode: n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
+    return fail(KVQ_ERR_UNSUPPORTED, "ISO3 / ISO4 decode: n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
                 kIsoDecodeMaxRows);
   if (q4k && (long)n_q * max_g > kQ4DecodeMaxRows)
     return fail(KVQ_ERR_UNSUPPORTED, "q4_0 K decode: n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
@@ -313,8 +320,9 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   for (int h = 0; h < n_q_heads && a.g_uniform; ++h)
     if (a.head_list[h] != h || (h % a.g_uniform == 0 && a.head_off[h / a.g_uniform] != h)) a.g_uniform = 0;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (cache->k.fmt == KVQ_FMT_ISO3)
-    return hip_status(launch_decode_iso3(cache->head_dim, plan, a, hs), "decode launch");
+  if (cache->k.fmt == KVQ_FMT_ISO3 || cache->k.fmt == KVQ_FMT_ISO4)
+    return hip_status(launch_decode_iso(cache->k.fmt == KVQ_FMT_ISO4 ? 4 : 3, cache->head_dim, plan, a, hs),
+                      "decode launch");
   if (cache->k.fmt == KVQ_FMT_Q4_0_H256) return hip_status(launch_decode_q4(plan, a, hs), "decode launch");
   if (cache->k.fmt == KVQ_FMT_F32 || cache->v.fmt == KVQ_FMT_F32)
     return hip_status(launch_decode_f32(cache->k.fmt == KVQ_FMT_F32, cache->v.fmt == KVQ_FMT_F32, cache->head_dim,

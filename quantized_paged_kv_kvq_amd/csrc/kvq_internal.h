@@ -14,7 +14,7 @@ namespace kvq {
 //     words of code bytes c, c+16, c+32, c+48 (c % 64 < 16) form a 16-byte unit
 //   Q4_0_H256 K stores: 16-byte units, unit (c/64, (c/4)%4, t) holds bytes 4w .. 4w+3 (w = (c/4)%4) of
 //     the four 32-value groups c/64*4 .. +3 of slot t -- one wave load covers a contiguous kilobyte
-//   ISO3 stores: token-major
+//   ISO3 / ISO4 stores: token-major
 //   F32 K stores: as INT8_G64 K (a 16-byte chunk holds 4 values); F32 V stores: head_dim-major, the 16
 //     slots of one head_dim index are 64 contiguous bytes
 __host__ __device__ inline int k_tile_offset(int c, int t) { return ((c >> 4) * 16 + t) * 16 + (c & 15); }
@@ -123,9 +123,10 @@ hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const 
                          hipStream_t s);
 // the log-sum-exp combine of the split partials (every decode kernel writes the same layout)
 hipError_t launch_decode_combine(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
-// ISO3 K and V stores (head_dim 128 or 256, at most kIsoDecodeMaxRows rows per KV head)
+// ISO3 or ISO4 K and V stores (bits 3 or 4; head_dim 128 or 256, at most kIsoDecodeMaxRows rows per
+// KV head)
 DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int max_rows);
-hipError_t launch_decode_iso3(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_iso(int bits, int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 // Q4_0_H256 K and V stores (head_dim 256, at most kQ4DecodeMaxRows rows per KV head)
 constexpr int kQ4DecodeMaxRows = 16;
 DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows);

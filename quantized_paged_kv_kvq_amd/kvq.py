@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-FMT = {"int8": 1, "q4h": 2, "iso3": 3, "f32": 4}
+FMT = {"int8": 1, "q4h": 2, "iso3": 3, "f32": 4, "iso4": 5}
 OUT_DTYPE = {"f32": (0, torch.float32), "f16": (1, torch.float16), "bf16": (2, torch.bfloat16)}
 PAGE_SIZE = 16
 

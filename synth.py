@@ -185,8 +185,9 @@ def batched_iso3_decode(seed: int = 6, n_seqs: int = 32, len_lo: int = 4096, len
 
 
 def moe_iso3_decode(ctx: int = 131072, seed: int = 7, n_q_heads: int = 16, n_kv_heads: int = 2,
-                    head_dim: int = 256, n_outliers: int = 4) -> Workload:
-    """moe_int8_decode's layer (GQA 16:2, head_dim 256, K outlier channels x20) over ISO3 K and V."""
+                    head_dim: int = 256, n_outliers: int = 4, fmt: str = "iso3") -> Workload:
+    """moe_int8_decode's layer (GQA 16:2, head_dim 256, K outlier channels x20) over ISO3 (or, with
+    fmt="iso4", ISO4) K and V."""
     rng = np.random.default_rng(seed)
     lens = np.array([ctx], np.int32)
     table, npages = _page_table(rng, lens, PAGE_SIZE, identity=False)
@@ -195,7 +196,7 @@ def moe_iso3_decode(ctx: int = 131072, seed: int = 7, n_q_heads: int = 16, n_kv_
     v = normal_bf16(rng, (ctx, n_kv_heads, head_dim))
     q = normal_bf16(rng, (1, 1, n_q_heads, head_dim))
     quat = random_quaternion(seed + 1000)
-    w = Workload("moe_iso3_decode", "iso3", "iso3", 1, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
+    w = Workload(f"moe_{fmt}_decode", fmt, fmt, 1, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
                  lens, table, npages, [k], [v], q, quat=quat)
     w.meta["outlier_channels"] = [int(c) for c in outliers]
     return w

@@ -94,7 +94,7 @@ def tile_index(layout: str, cb: int) -> np.ndarray:
 
 
 def store_layout(fmt: str, which: str) -> str:
-    if fmt == "iso3":
+    if fmt in ("iso3", "iso4"):
         return "token"
     if fmt == "q4h" and which == "k":
         return "k_q4"

@@ -32,14 +32,15 @@ def test_library_exports_every_declared_symbol():
 
 
 @pytest.mark.parametrize("fmt,D", [("int8", 64), ("int8", 128), ("int8", 256), ("int8", 512), ("q4h", 256),
-                                   ("iso3", 128), ("iso3", 256), ("f32", 64), ("f32", 256), ("f32", 512)])
+                                   ("iso3", 128), ("iso3", 256), ("f32", 64), ("f32", 256), ("f32", 512),
+                                   ("iso4", 128), ("iso4", 512)])
 def test_cell_bytes_match_oracle(fmt, D):
     assert kvq.cell_bytes(fmt, D) == opaged.cell_bytes(fmt, D)
 
 
 def test_cell_bytes_refuses_bad_geometry():
     L = kvq.lib()
-    for fmt, D in ((1, 100), (2, 128), (3, 64), (9, 128), (1, 1024), (4, 96), (4, 1024)):
+    for fmt, D in ((1, 100), (2, 128), (3, 64), (9, 128), (1, 1024), (4, 96), (4, 1024), (5, 64), (5, 640)):
         assert L.kvq_cell_bytes(fmt, D, None, None) == -1
 
 
@@ -93,6 +94,19 @@ def test_decode_validation_errors():
     c = make_cache()
     c.v = kvq.KvqStore(1, None, FAKE)
     assert decode(c, make_pages()) == 1
+
+
+def test_decode_validation_iso4():
+    """ISO4 K and V: head_dim 128 or 256, up to 16 rows; no mixing with ISO3 or other stores."""
+    assert decode(make_cache(fk=5, fv=3, D=128), make_pages()) == 3
+    assert decode(make_cache(fk=3, fv=5, D=128), make_pages()) == 3
+    assert decode(make_cache(fk=1, fv=5, D=128), make_pages()) == 3
+    assert decode(make_cache(fk=5, fv=5, D=384), make_pages()) == 3
+    assert decode(make_cache(fk=5, fv=5, D=128), make_pages(), n_q=3) == 3    # 24 rows > 16
+    assert decode(make_cache(fk=5, fv=5, D=128), make_pages(), ws=None) == 4  # valid up to the workspace
+    L = kvq.lib()
+    c = make_cache(fk=5, fv=5, D=128)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (128 + 2) * 4
 
 
 def test_decode_validation_single_store_modes():
