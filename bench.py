@@ -52,6 +52,8 @@ def make_workload(name: str):
         return synth.tiny_int8_decode()
     if name == "iso3_extend":
         return synth.iso3_extend()
+    if name == "int8_extend":
+        return synth.iso3_extend(fmt="int8")
     if name == "batched_iso3_decode":
         return synth.batched_iso3_decode()
     if name == "moe_iso3_decode":
@@ -158,8 +160,8 @@ def extend_cpu_baseline(w, budget_s: float = 15.0):
         threads = 1
     pre, new = w.prefix_lens(), w.new_lens()
     P, N = int(pre[0]), int(new[0])
-    sk = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
-    sv = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sv = opaged.Store.empty(w.fmt_v, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
     opaged.append(sk, w.block_table, np.zeros(P, int), np.arange(P), w.k[0][:P], w.page_size, quat=w.quat)
     opaged.append(sv, w.block_table, np.zeros(P, int), np.arange(P), w.v[0][:P], w.page_size, quat=w.quat)
     cu = np.array([0, N], np.int32)
@@ -174,7 +176,7 @@ def extend_cpu_baseline(w, budget_s: float = 15.0):
             break
     t_rows = (time.perf_counter() - t0) / n_calls
     t1 = time.perf_counter()
-    sk2 = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sk2 = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
     opaged.append(sk2, w.block_table, np.zeros(N, int), np.arange(P, P + N), w.k[0][P:], w.page_size, quat=w.quat)
     opaged.append(sk2, w.block_table, np.zeros(N, int), np.arange(P, P + N), w.v[0][P:], w.page_size, quat=w.quat)
     t_pack = time.perf_counter() - t1
@@ -192,7 +194,7 @@ def bench_extend(args):
     w = make_workload(args.workload)
     pre, new = w.prefix_lens(), w.new_lens()
     P, N = int(pre[0]), int(new[0])
-    cache = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, "iso3", "iso3", quat=w.quat)
+    cache = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, w.fmt_k, w.fmt_v, quat=w.quat)
     pages = kvq.Pages(dev_i32(w.block_table), dev_i32(pre))
     kvq.kvq_append(cache, pages, dev_bf16(w.k[0][:P]), dev_bf16(w.v[0][:P]), dev_i32(np.zeros(P, np.int32)),
                    dev_i32(np.arange(P, dtype=np.int32)))
@@ -247,18 +249,21 @@ def bench_extend(args):
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cpu = extend_cpu_baseline(w)
     line = {
-        "metric": EXTEND_METRIC, "value": round(ms_per_step * 1e3, 3), "unit": "us/step", "n_gpus": 1,
+        "metric": EXTEND_METRIC.replace("ISO3", w.fmt_k.upper()), "value": round(ms_per_step * 1e3, 3),
+        "unit": "us/step", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16/bf16 mfma, iso3 cells",
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"f16/bf16 mfma, {w.fmt_k} cells",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "prefix": P, "n_new": N, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
-                   "k_format": "iso3", "v_format": "iso3",
+                   "k_format": w.fmt_k, "v_format": w.fmt_v,
                    "step": "extend attention over the packed prefix + causal new tokens, then pack the new tokens",
                    "launch": mode},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_extend_iso3", "launch_us": round(att_us, 3), "algorithmic_flops": flops},
+                     "kernel": "extend launch (k_extend_stage + k_extend_attn)", "launch_us": round(att_us, 3),
+                     "algorithmic_flops": flops},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
@@ -332,7 +337,7 @@ def main():
     if args.read_probe:
         return read_probe(args.read_probe)
     kvq.lib()
-    if args.workload == "iso3_extend":
+    if args.workload in ("iso3_extend", "int8_extend"):
         return bench_extend(args)
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
     w = make_workload(args.workload)

@@ -259,8 +259,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
  *   workspace    : device, >= kvq_extend_workspace_bytes(...) bytes, 256-byte aligned:
  *                  every 64-cell tile of every prefix and chunk is staged there once as
  *                  the attention kernel's tile image (about 33 KB per tile and KV head)
- * Requires ISO3 K and V stores and head_dim 128.  Prefix attention runs in the
- * quaternion-rotated basis (the query rotated once, the accumulator rotated back once);
+ * Requires ISO3 K and V stores, or INT8_G64 K and V stores ([ST2698] "What it does": the
+ * prompt chunk reads the int8 cache dequantised), and head_dim 128.  ISO3 prefix attention
+ * runs in the quaternion-rotated basis (the query rotated once, the accumulator rotated back
+ * once); int8 prefix attention weights each 64-value group's partial sums by its scale;
  * the cells of a chunk's pages must not be written by pack_after of another sequence
  * in the same call. */
 kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages,

@@ -1,4 +1,4 @@
-// Extend (prefill chunk) attention over an ISO3-packed prefix plus the chunk's own bf16 tokens.
+// Extend (prefill chunk) attention over an ISO3- or int8-packed prefix plus the chunk's own bf16 tokens.
 //
 // FreeToken PR #398, "What": a prefill chunk attends the cached prefix, which is held packed,
 // and its own new tokens, which are packed only after the chunk's attention (deferred packing);
@@ -35,6 +35,15 @@
 //
 // Online softmax in base 2 per row across both phases; the row max is shared by the 4 lanes that
 // hold a row's keys, the running sums stay per lane until the end.
+//
+// INT8_G64 prefix (strata PR #2698, "What it does": a prompt chunk reads the int8 cache range
+// dequantised, there by a dequantise-to-f16 kernel feeding a GEMM).  Here the stage writes the exact
+// codes as fp16 (|code| <= 127) and the fp32 scales of both 64-value groups of every key; the
+// attention forms each key's score from its two group partials weighted by the group scales (the
+// query enters unscaled and exact in one fp16 part), and splits
+// the weights times the key's V group scale into fp16 hi + lo parts per group.  Rounding the
+// dequantised values to fp16 instead (code x scale has up to 18 significant bits) measured up to
+// 1.8e-3 off on the CPU for short prefixes.  No rotation; head_dim 128 as ISO3.
 #include "kvq_internal.h"
 #include "iso3_levels.h"
 #include "device_util.h"
@@ -51,6 +60,8 @@ constexpr int kImgK = kKeys * kKRow;                       // K image bytes: [ke
 constexpr int kImgV = kD * kVRow;                          // V image bytes: [d][key position]
 constexpr int kNormOff = kImgK + kImgV;                    // fp32 K norms [64], then V norms / S [64]
 static_assert(kNormOff + 2 * kKeys * 4 <= kExtendTileBytes, "tile image layout");
+// int8 prefix tiles: fp32 [K s0 / s1, K s1, V s0, V s1][64] (s_g: group scales) instead
+static_assert(kNormOff + 4 * kKeys * 4 <= kExtendTileBytes, "int8 tile image layout");
 static_assert(kExtendTileBytes % 1024 == 0, "a tile image is whole kilobytes");
 
 // Byte offsets inside a tile image: 16-byte chunk c (head_dim 8c .. 8c+7) of key k, and 16-byte
@@ -85,7 +96,10 @@ __device__ __forceinline__ uint8_t* chunk_image(const ExtendArgs& a, int b, int 
 
 // ============================== staging ==============================
 struct StageLds {
-  uint32_t raw[2][kKeys * 12 + 4];                          // ISO3 codes of the tile's keys (K, V), 48 B each
+  union {
+    uint32_t raw[2][kKeys * 12 + 4];                        // ISO3 codes of the tile's keys (K, V), 48 B each
+    uint4 raw8[2][4 * KVQ_PAGE_SIZE * kD / 16];             // int8: the 4 pages' K and V code tiles
+  };
   uint16_t level[8];                                         // S * c as fp16
   __attribute__((aligned(16))) uint8_t img[kExtendTileBytes];
 };
@@ -104,7 +118,73 @@ __global__ __launch_bounds__(256) void k_extend_stage(const ExtendArgs a) {
   const int n_b = clampi(a.cu_new[b + 1], s0, a.n_new) - s0;
   const int P = clampi(a.prefix_lens[b], 0, a.max_pages * KVQ_PAGE_SIZE);
 
-  if ((int)blockIdx.x < a.pt_max) {
+  if ((int)blockIdx.x < a.pt_max && a.int8) {
+    // INT8_G64 prefix tile (4 whole pages): images of the exact codes in fp16 and the fp32 scales of
+    // both 64-value groups of every key; the attention weights each group's partial sums by them.
+    const int t = blockIdx.x;
+    if (t * kKeys >= P) return;
+    const int* bt_row = a.bt + (size_t)b * a.max_pages;
+    for (int i = tid; i < 2 * 4 * 128; i += 256) {          // 16-byte units: store, page j, unit u
+      const int st = i >> 9, j = (i >> 7) & 3, u = i & 127;
+      const int pos = min(t * kKeys + 16 * j, P - 1);
+      const int page = clampi(bt_row[pos >> 4], 0, a.num_pages - 1);
+      const uint8_t* src = (st ? a.v_codes : a.k_codes) + ((size_t)page * a.hkv + kvh) * (KVQ_PAGE_SIZE * kD);
+      s.raw8[st][j * 128 + u] = reinterpret_cast<const uint4*>(src)[u];
+    }
+    if (tid < kKeys) {
+      const int pos = t * kKeys + tid;
+      const bool live = pos < P;
+      const int pc = min(pos, P - 1);
+      const int page = clampi(bt_row[pc >> 4], 0, a.num_pages - 1);
+      const size_t cell = ((size_t)page * a.hkv + kvh) * KVQ_PAGE_SIZE + (pc & 15);
+      // K: the factors of (S0 * s0 / s1 + S1) * s1 (S0 * s0 when s1 = 0); V: the group scales
+      float* sc = reinterpret_cast<float*>(s.img + kNormOff);
+      const float k0 = live ? h2f(a.k_norms[cell * 2]) : 0.0f, k1 = live ? h2f(a.k_norms[cell * 2 + 1]) : 0.0f;
+      sc[tid] = k1 > 0.0f ? k0 / k1 : k0;
+      sc[kKeys + tid] = k1 > 0.0f ? k1 : 1.0f;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) sc[(2 + g) * kKeys + tid] = live ? h2f(a.v_norms[cell * 2 + g]) : 0.0f;
+    }
+    __syncthreads();
+    {   // K image: thread = (key, 32 head_dim values = chunks 2q, 2q + 1 of the key's slot)
+      const int key = tid >> 2, q = tid & 3;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 ch = s.raw8[0][(key >> 4) * 128 + (2 * q + (c >> 1)) * 16 + (key & 15)];
+        const uint32_t w0 = (c & 1) ? ch.z : ch.x, w1 = (c & 1) ? ch.w : ch.y;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t src = e < 2 ? w0 : w1;
+          const int sh = 16 * (e & 1);
+          const _Float16 lo = (_Float16)(float)(int8_t)(src >> sh), hi = (_Float16)(float)(int8_t)(src >> (sh + 8));
+          w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *reinterpret_cast<uint4*>(s.img + k_img_off(key, 4 * q + c)) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    {   // V image: thread = (head_dim row, 32 key positions)
+      const int d = tid >> 1, h = tid & 1;
+      const uint8_t* vr = reinterpret_cast<const uint8_t*>(s.raw8[1]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = 32 * h + 8 * c + 2 * e;
+          const int k0 = key_at(p), k1 = key_at(p + 1);
+          const _Float16 lo = (_Float16)(float)(int8_t)vr[(k0 >> 4) * 2048 + v_tile_offset(d, k0 & 15)];
+          const _Float16 hi = (_Float16)(float)(int8_t)vr[(k1 >> 4) * 2048 + v_tile_offset(d, k1 & 15)];
+          w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *reinterpret_cast<uint4*>(s.img + v_img_off(d, 4 * h + c)) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(prefix_image(a, b, kvh, t));
+    const uint4* src = reinterpret_cast<const uint4*>(s.img);
+    for (int i = tid; i < kExtendTileBytes / 16; i += 256) dst[i] = src[i];
+  } else if ((int)blockIdx.x < a.pt_max) {
     const int t = blockIdx.x;
     if (t * kKeys >= P) return;
     const int* bt_row = a.bt + (size_t)b * a.max_pages;
@@ -262,20 +342,22 @@ struct TileOps<bf16x8, NQ> {
   }
 };
 
-// S^T for the tile's 64 keys (two 32-key blocks) against this wave's 32 rows; q is given as NQ
-// parts (hi, lo) whose products accumulate.
-template <typename V8, int NQ>
+// S^T for the tile's 64 keys (two 32-key blocks) against this wave's 32 rows over the head_dim steps
+// KS0 .. KS1 - 1 (16 values each); q is given as NQ parts (hi, lo) whose products accumulate.
+template <typename V8, int NQ, int KS0 = 0, int KS1 = 8, bool ACC = false>
 __device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, const V8 (&q)[NQ][8], f32x16 (&S)[2]) {
   using Ops = TileOps<V8, NQ>;
-  S[0] = f32x16{};
-  S[1] = f32x16{};
+  if constexpr (!ACC) {
+    S[0] = f32x16{};
+    S[1] = f32x16{};
+  }
   V8 ka[2][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) ka[0][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, h));
+  for (int kb = 0; kb < 2; ++kb) ka[0][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, 2 * KS0 + h));
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const int cb = ks & 1;
-    if (ks + 1 < 8) {
+  for (int ks = KS0; ks < KS1; ++ks) {
+    const int cb = (ks - KS0) & 1;
+    if (ks + 1 < KS1) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         ka[cb ^ 1][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, 2 * (ks + 1) + h));
@@ -284,15 +366,22 @@ __device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, cons
     for (int part = 0; part < NQ; ++part)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) S[kb] = Ops::mma(ka[cb][kb], q[part][ks], S[kb]);
-    if (ks + 1 < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    if (ks + 1 < KS1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NQ, 0);
   }
 }
 
-// O^T += V^T P^T for the tile: per 16-key step st, the weights' hi and lo parts P[st][0..1] (as MFMA
-// B operands) against the 4 head_dim blocks of V.
-template <typename V8>
-__device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, const u32x4 (&P)[4][2], f32x16 (&O)[4]) {
+template <typename V8, int NQ, int KS0, int KS1>
+__device__ __forceinline__ void qk_tile_acc(const uint8_t* buf, int l32, int h, const V8 (&q)[NQ][8], f32x16 (&S)[2]) {
+  qk_tile<V8, NQ, KS0, KS1, true>(buf, l32, h, q, S);
+}
+
+// O^T += V^T P^T for the tile: per 16-key step st, the weights' hi and lo parts (as MFMA B operands)
+// against the 4 head_dim blocks of V; head_dim block t takes the weights P[t * NPG / 4] (NPG = 1: one
+// set for all; NPG = 2: one set per 64-value group).
+template <typename V8, int NPG = 1>
+__device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, const u32x4 (&P)[NPG][4][2],
+                                        f32x16 (&O)[4]) {
   using Ops = TileOps<V8, 1>;
   V8 va[2][4];
 #pragma unroll
@@ -305,11 +394,10 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, cons
       for (int t = 0; t < 4; ++t)
         va[cb ^ 1][t] = *reinterpret_cast<const V8*>(buf + v_img_off(32 * t + l32, 2 * (st + 1) + h));
     }
-    const V8 ph = __builtin_bit_cast(V8, P[st][0]), pl = __builtin_bit_cast(V8, P[st][1]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) O[t] = Ops::mma(va[cb][t], ph, O[t]);
+    for (int t = 0; t < 4; ++t) O[t] = Ops::mma(va[cb][t], __builtin_bit_cast(V8, P[t * NPG / 4][st][0]), O[t]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) O[t] = Ops::mma(va[cb][t], pl, O[t]);
+    for (int t = 0; t < 4; ++t) O[t] = Ops::mma(va[cb][t], __builtin_bit_cast(V8, P[t * NPG / 4][st][1]), O[t]);
     if (st + 1 < 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
   }
@@ -317,6 +405,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, cons
 
 // Prefix tiles: rotated basis, fp16 MFMAs, per-key norms.
 struct PrefixTiles {
+  using Weights = u32x4[1][4][2];
   const ExtendArgs& a;
   int b, kvh, P;
   const f16x8 (&q)[2][8];
@@ -345,7 +434,7 @@ struct PrefixTiles {
     }
     return rs;
   }
-  __device__ __forceinline__ void weights(const uint8_t* buf, int h, const float (&u)[32], u32x4 (&Pw)[4][2]) const {
+  __device__ __forceinline__ void weights(const uint8_t* buf, int h, const float (&u)[32], Weights& Pw) const {
     const float* nv = reinterpret_cast<const float*>(buf + kNormOff) + kKeys;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -360,17 +449,93 @@ struct PrefixTiles {
       }
       f16x8 ph, pl;
       split_f16x8(x, ph, pl);
-      Pw[st][0] = __builtin_bit_cast(u32x4, ph);
-      Pw[st][1] = __builtin_bit_cast(u32x4, pl);
+      Pw[0][st][0] = __builtin_bit_cast(u32x4, ph);
+      Pw[0][st][1] = __builtin_bit_cast(u32x4, pl);
     }
   }
-  __device__ __forceinline__ void pv(const uint8_t* buf, int l32, int h, const u32x4 (&Pw)[4][2], f32x16 (&O)[4]) const {
+  __device__ __forceinline__ void pv(const uint8_t* buf, int l32, int h, const Weights& Pw, f32x16 (&O)[4]) const {
     pv_tile<f16x8>(buf, l32, h, Pw, O);
+  }
+};
+
+// INT8_G64 prefix tiles: exact fp16 codes, one partial sum per 64-value group weighted by the key's
+// group scale (QK), and per group the weights times the key's V group scale (PV); no rotation.
+struct PrefixTilesI8 {
+  using Weights = u32x4[2][4][2];
+  const ExtendArgs& a;
+  int b, kvh, P;
+  const f16x8 (&q)[2][8];
+  float rs;
+  __device__ __forceinline__ const uint8_t* image(int t) const { return prefix_image(a, b, kvh, t); }
+  __device__ __forceinline__ bool active(int) const { return true; }
+  // The query is bf16 and unscaled, so its fp16 image (times a power of two) is exact in one part.
+  // Per key, S = s0 * S0 + s1 * S1 (S_g: the partial over group g) is formed as (S0 * s0 / s1 + S1) * s1
+  // in one accumulator (as S0 * s0 when s1 = 0: that group's codes are all zero), with both factors
+  // from the stage.
+  __device__ __forceinline__ void qk(const uint8_t* buf, int l32, int h, f32x16 (&S)[2]) const {
+    const f16x8 (&qh)[1][8] = reinterpret_cast<const f16x8 (&)[1][8]>(q[0]);
+    const float* sk = reinterpret_cast<const float*>(buf + kNormOff);
+    qk_tile<f16x8, 1, 0, 4>(buf, l32, h, qh, S);             // head_dim 0 .. 63
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const int key = 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h;   // keys key .. key+3
+      const float4 s0 = *reinterpret_cast<const float4*>(sk + key);
+      const float4 s1 = *reinterpret_cast<const float4*>(sk + kKeys + key);
+      const float a0[4] = {s0.x, s0.y, s0.z, s0.w}, a1[4] = {s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i >> 4][(i & 15) + j] *= a0[j];
+    }
+    qk_tile_acc<f16x8, 1, 4, 8>(buf, l32, h, qh, S);         // head_dim 64 .. 127, accumulated
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const int key = 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h;
+      const float4 s1 = *reinterpret_cast<const float4*>(sk + kKeys + key);
+      const float a1[4] = {s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i >> 4][(i & 15) + j] *= a1[j];
+    }
+  }
+  __device__ __forceinline__ float scores(const uint8_t*, int t, int h, const f32x16 (&S)[2], float (&u)[32]) const {
+    const int limit = P - t * kKeys;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) u[i] = S[i >> 4][i & 15];
+    if (limit < kKeys) {                                     // the prefix ends inside this tile
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h + (i & 3) >= limit) u[i] = kNegInf;
+    }
+    return rs * a.scale_log2;                                // the query entered unscaled
+  }
+  __device__ __forceinline__ void weights(const uint8_t* buf, int h, const float (&u)[32], Weights& Pw) const {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float* nv = reinterpret_cast<const float*>(buf + kNormOff) + (2 + g) * kKeys;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float x[8];
+#pragma unroll
+        for (int e4 = 0; e4 < 2; ++e4) {
+          const float4 n4 = *reinterpret_cast<const float4*>(nv + 16 * st + 8 * e4 + 4 * h);
+          x[4 * e4 + 0] = u[8 * st + 4 * e4 + 0] * n4.x;
+          x[4 * e4 + 1] = u[8 * st + 4 * e4 + 1] * n4.y;
+          x[4 * e4 + 2] = u[8 * st + 4 * e4 + 2] * n4.z;
+          x[4 * e4 + 3] = u[8 * st + 4 * e4 + 3] * n4.w;
+        }
+        f16x8 ph, pl;
+        split_f16x8(x, ph, pl);
+        Pw[g][st][0] = __builtin_bit_cast(u32x4, ph);
+        Pw[g][st][1] = __builtin_bit_cast(u32x4, pl);
+      }
+    }
+  }
+  __device__ __forceinline__ void pv(const uint8_t* buf, int l32, int h, const Weights& Pw, f32x16 (&O)[4]) const {
+    pv_tile<f16x8, 2>(buf, l32, h, Pw, O);
   }
 };
 
 // Chunk tiles: original basis, bf16 MFMAs, causal mask; tiles past a wave's last token are skipped.
 struct ChunkTiles {
+  using Weights = u32x4[1][4][2];
   const ExtendArgs& a;
   int b, kvh, tok, wave_first, wave_last;
   const bf16x8 (&q)[1][8];
@@ -389,16 +554,16 @@ struct ChunkTiles {
     }
     return a.scale_log2;
   }
-  __device__ __forceinline__ void weights(const uint8_t*, int, const float (&u)[32], u32x4 (&Pw)[4][2]) const {
+  __device__ __forceinline__ void weights(const uint8_t*, int, const float (&u)[32], Weights& Pw) const {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       bf16x8 ph, pl;
       split_bf16x8(u + 8 * st, ph, pl);
-      Pw[st][0] = __builtin_bit_cast(u32x4, ph);
-      Pw[st][1] = __builtin_bit_cast(u32x4, pl);
+      Pw[0][st][0] = __builtin_bit_cast(u32x4, ph);
+      Pw[0][st][1] = __builtin_bit_cast(u32x4, pl);
     }
   }
-  __device__ __forceinline__ void pv(const uint8_t* buf, int l32, int h, const u32x4 (&Pw)[4][2], f32x16 (&O)[4]) const {
+  __device__ __forceinline__ void pv(const uint8_t* buf, int l32, int h, const Weights& Pw, f32x16 (&O)[4]) const {
     pv_tile<bf16x8>(buf, l32, h, Pw, O);
   }
 };
@@ -412,9 +577,12 @@ __device__ __forceinline__ void issue_tile(const uint8_t* src, uint8_t* dst, int
 }
 
 // Register values that must exist at this point of the instruction stream.
-__device__ __forceinline__ void pin(u32x4 (&P)[4][2], f32x16 (&O)[4]) {
+template <int NPG>
+__device__ __forceinline__ void pin(u32x4 (&P)[NPG][4][2], f32x16 (&O)[4]) {
 #pragma unroll
-  for (int st = 0; st < 4; ++st) asm volatile("" : "+v"(P[st][0]), "+v"(P[st][1]));
+  for (int g = 0; g < NPG; ++g)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) asm volatile("" : "+v"(P[g][st][0]), "+v"(P[g][st][1]));
   asm volatile("" : "+v"(O[0]), "+v"(O[1]), "+v"(O[2]), "+v"(O[3]));
 }
 __device__ __forceinline__ void pin(f32x16 (&S)[2], f32x16 (&O)[4]) {
@@ -447,7 +615,7 @@ __device__ __forceinline__ void run_tiles(const Tiles& k, int n, uint8_t* ring, 
   f32x16 S[2];
   if (k.active(0)) k.qk(buf(0), l32, h, S);
   sync_tiles(false);
-  u32x4 Pw[4][2];
+  typename Tiles::Weights Pw;
   for (int it = 0; it < n; ++it) {
     // ---- VALU cluster: softmax of tile it
     if (group_b && it + 2 < n) issue_tile(k.image(it + 2), buf(it + 2), wv, lane);
@@ -472,6 +640,7 @@ __device__ __forceinline__ void run_tiles(const Tiles& k, int n, uint8_t* ring, 
   if (!group_b) sync_tiles(true);
 }
 
+template <bool I8>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_extend_attn(const ExtendArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[3 * kExtendTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -520,7 +689,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_extend_attn(const ExtendArgs
           const float u[4] = {bf16f(w[2 * grp] & 0xffffu), bf16f(w[2 * grp] >> 16), bf16f(w[2 * grp + 1] & 0xffffu),
                               bf16f(w[2 * grp + 1] >> 16)};
           float t[4];
-          qmul(rw, rx, ry, rz, u, t);
+          if constexpr (I8) {                               // int8 prefix: original basis
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = u[e];
+          } else {
+            qmul(rw, rx, ry, rz, u, t);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[ks][4 * grp + e] = t[e] * a.q_scale;
@@ -540,11 +714,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_extend_attn(const ExtendArgs
         split_f16x8(x, qs[0][ks], qs[1][ks]);
       }
     }
-    const PrefixTiles pk{a, b, kvh, P, qs, rs};
-    run_tiles(pk, n_pt, ring, group_b, wv, lane, l32, h, m_run, l_run, O);
+    if constexpr (I8) {
+      const PrefixTilesI8 pk{a, b, kvh, P, qs, rs};
+      run_tiles(pk, n_pt, ring, group_b, wv, lane, l32, h, m_run, l_run, O);
+    } else {
+      const PrefixTiles pk{a, b, kvh, P, qs, rs};
+      run_tiles(pk, n_pt, ring, group_b, wv, lane, l32, h, m_run, l_run, O);
+    }
     // back to the original basis: O[t][4g .. 4g+3] is head_dim 32t + 8g + 4h .. +3, one group
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4 && !I8; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float u[4] = {O[t][4 * g], O[t][4 * g + 1], O[t][4 * g + 2], O[t][4 * g + 3]};
@@ -590,7 +769,10 @@ float extend_level_scale() { return kIsoLevelScale; }
 
 hipError_t launch_extend(const ExtendArgs& a, int tiles_per_seq, hipStream_t s) {
   k_extend_stage<<<dim3((unsigned)(a.pt_max + a.nt_max), (unsigned)a.hkv, (unsigned)a.batch), dim3(256), 0, s>>>(a);
-  k_extend_attn<<<dim3((unsigned)(a.hkv * tiles_per_seq), (unsigned)a.batch), dim3(kWaves * 64), 0, s>>>(a);
+  if (a.int8)
+    k_extend_attn<true><<<dim3((unsigned)(a.hkv * tiles_per_seq), (unsigned)a.batch), dim3(kWaves * 64), 0, s>>>(a);
+  else
+    k_extend_attn<false><<<dim3((unsigned)(a.hkv * tiles_per_seq), (unsigned)a.batch), dim3(kWaves * 64), 0, s>>>(a);
   return hipGetLastError();
 }
 

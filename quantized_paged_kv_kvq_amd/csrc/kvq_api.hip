@@ -364,9 +364,12 @@ static kvq_status extend_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->k.fmt, cache->head_dim, false)) != KVQ_OK) return st;
   if ((st = check_store_fmt(cache->v.fmt, cache->head_dim, true)) != KVQ_OK) return st;
-  if (cache->k.fmt != KVQ_FMT_ISO3 || cache->v.fmt != KVQ_FMT_ISO3)
-    return fail(KVQ_ERR_UNSUPPORTED, "extend attention needs ISO3 K and V stores (got formats %d / %d)",
+  const bool iso3 = cache->k.fmt == KVQ_FMT_ISO3 && cache->v.fmt == KVQ_FMT_ISO3;
+  const bool int8 = cache->k.fmt == KVQ_FMT_INT8_G64 && cache->v.fmt == KVQ_FMT_INT8_G64;
+  if (!iso3 && !int8)
+    return fail(KVQ_ERR_UNSUPPORTED, "extend attention needs ISO3 or INT8_G64 K and V stores (got formats %d / %d)",
                 cache->k.fmt, cache->v.fmt);
+  a->int8 = int8 ? 1 : 0;
   if (cache->head_dim != 128)
     return fail(KVQ_ERR_UNSUPPORTED, "extend attention supports head_dim 128 (got %d)", cache->head_dim);
   if (batch < 1 || batch > 65535) return fail(KVQ_ERR_SHAPE, "batch %d out of range", batch);
@@ -397,7 +400,9 @@ size_t kvq_extend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
                                   int32_t max_new, int32_t n_q_heads) {
   (void)n_q_heads;   // the tile images depend on the KV heads only
   if (check_cache(cache) != KVQ_OK) return 0;
-  if (cache->k.fmt != KVQ_FMT_ISO3 || cache->v.fmt != KVQ_FMT_ISO3 || cache->head_dim != 128) return 0;
+  const bool iso3 = cache->k.fmt == KVQ_FMT_ISO3 && cache->v.fmt == KVQ_FMT_ISO3;
+  const bool int8 = cache->k.fmt == KVQ_FMT_INT8_G64 && cache->v.fmt == KVQ_FMT_INT8_G64;
+  if ((!iso3 && !int8) || cache->head_dim != 128) return 0;
   if (batch < 1 || batch > 65535 || max_pages < 1 || n_new < 0 || max_new < 0 || max_new > n_new) return 0;
   const int pt_max = (int)(((long)max_pages * KVQ_PAGE_SIZE + 63) / 64), nt_max = (max_new + 63) / 64;
   return extend_workspace_bytes(batch, cache->n_kv_heads, pt_max, nt_max);
@@ -447,9 +452,9 @@ kvq_status kvq_extend_attn(const kvq_cache* cache, const kvq_pages* pages, const
   a.batch = pages->batch;
   a.n_new = n_new;
   a.n_q_heads = n_q_heads;
-  for (int i = 0; i < 4; ++i) a.quat[i] = cache->iso_quat[i];
+  for (int i = 0; i < 4; ++i) a.quat[i] = a.int8 ? (i == 0 ? 1.0f : 0.0f) : cache->iso_quat[i];
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
-  a.q_scale = a.scale_log2 / extend_level_scale();
+  a.q_scale = a.int8 ? 1.0f : a.scale_log2 / extend_level_scale();   // int8: the scale goes to the scores
   a.g_uniform = n_q_heads % cache->n_kv_heads == 0 ? n_q_heads / cache->n_kv_heads : 0;
   for (int h = 0; h < n_q_heads && a.g_uniform; ++h)
     if (a.head_list[h] != h || (h % a.g_uniform == 0 && a.head_off[h / a.g_uniform] != h)) a.g_uniform = 0;

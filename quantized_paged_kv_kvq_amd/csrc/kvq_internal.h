@@ -136,11 +136,11 @@ DecodePlan plan_decode_f32(int head_dim, int hkv, int batch, int max_pages, int 
 hipError_t launch_decode_f32(bool k_f32, bool v_f32, int head_dim, const DecodePlan& plan, const DecodeArgs& a,
                              hipStream_t s);
 
-// Extend over an ISO3 prefix: one row per (new token, query head); rows of KV head j use the query
-// heads head_list[head_off[j] .. head_off[j+1]).
+// Extend over an ISO3 or INT8_G64 prefix: one row per (new token, query head); rows of KV head j use
+// the query heads head_list[head_off[j] .. head_off[j+1]).
 struct ExtendArgs {
   const uint8_t* k_codes;
-  const uint16_t* k_norms;
+  const uint16_t* k_norms;    // the scales slabs: ISO3 norms, or INT8_G64 group scales
   const uint8_t* v_codes;
   const uint16_t* v_norms;
   const uint16_t* q;          // bf16 [n_new][n_q_heads][head_dim]
@@ -161,7 +161,8 @@ struct ExtendArgs {
   int n_q_heads;
   int g_pad;                  // power of two >= the largest group; a wave holds 32 / g_pad tokens
   float quat[4];
-  float q_scale;              // sm_scale * log2(e) / S (rotated prefix phase)
+  float q_scale;              // sm_scale * log2(e) / S (rotated prefix phase); 1 for int8 (applied to the scores)
+  int int8;                   // INT8_G64 K and V stores instead of ISO3
   float scale_log2;           // sm_scale * log2(e)
   int g_uniform;
   int16_t head_off[KVQ_MAX_Q_HEADS + 1];

@@ -259,9 +259,9 @@ def k8v4_verify(ctx: int = 118750, seed: int = 4, n_q: int = 3, n_q_heads: int =
 
 
 def iso3_extend(prefix: int = 30000, n_new: int = 2048, seed: int = 5, n_q_heads: int = 32,
-                n_kv_heads: int = 8, head_dim: int = 128, batch: int = 1) -> Workload:
-    """Prefill chunk over an ISO3-packed prefix: ``n_new`` bf16 tokens per sequence attend
-    the packed prefix plus themselves causally, and are packed after the attention."""
+                n_kv_heads: int = 8, head_dim: int = 128, batch: int = 1, fmt: str = "iso3") -> Workload:
+    """Prefill chunk over an ISO3-packed (fmt="int8": int8-g64) prefix: ``n_new`` bf16 tokens per
+    sequence attend the packed prefix plus themselves causally, and are packed after the attention."""
     rng = np.random.default_rng(seed)
     lens = np.full(batch, prefix + n_new, np.int32)
     table, npages = _page_table(rng, lens, PAGE_SIZE, identity=False)
@@ -269,7 +269,7 @@ def iso3_extend(prefix: int = 30000, n_new: int = 2048, seed: int = 5, n_q_heads
     vs = [normal_bf16(rng, (prefix + n_new, n_kv_heads, head_dim)) for _ in range(batch)]
     q = normal_bf16(rng, (batch * n_new, n_q_heads, head_dim))
     quat = random_quaternion(seed + 1000)
-    return Workload("iso3_extend", "iso3", "iso3", batch, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
+    return Workload(f"{fmt}_extend", fmt, fmt, batch, n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
                     lens, table, npages, ks, vs, q, n_q=n_new, n_step=n_new, quat=quat, kind="extend")
 
 
@@ -295,7 +295,7 @@ def ragged_decode(fmt_k: str, fmt_v: str, lens, seed: int = 11, n_q: int = 1, n_
 
 
 def ragged_extend(prefix_lens, new_lens, seed: int = 21, n_q_heads: int = 8, n_kv_heads: int = 2,
-                  head_dim: int = 128, identity: bool = False) -> Workload:
+                  head_dim: int = 128, identity: bool = False, fmt: str = "iso3") -> Workload:
     """Prefill chunks over ISO3 prefixes of any lengths, for parity tests: sequence b holds
     ``prefix_lens[b]`` packed cells and ``new_lens[b]`` new bf16 tokens; the q rows of all
     sequences' new tokens are concatenated in sequence order."""
@@ -308,6 +308,6 @@ def ragged_extend(prefix_lens, new_lens, seed: int = 21, n_q_heads: int = 8, n_k
     vs = [normal_bf16(rng, (int(L), n_kv_heads, head_dim)) for L in lens]
     q = normal_bf16(rng, (int(new.sum()), n_q_heads, head_dim))
     quat = random_quaternion(seed + 1000)
-    return Workload("ragged_extend", "iso3", "iso3", len(lens), n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
+    return Workload("ragged_extend", fmt, fmt, len(lens), n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
                     lens, table, npages, ks, vs, q, n_q=int(new.max()) if len(new) else 0, n_step=0, quat=quat,
                     kind="extend", meta={"new": new})

@@ -210,7 +210,10 @@ def test_extend_validation_errors():
     iso = lambda **kw: make_cache(fk=3, fv=3, D=128, **kw)
     assert extend(None, make_pages()) == 1
     assert extend(iso(), None) == 1
-    assert extend(make_cache(), make_pages()) == 3                      # int8 stores: no extend path
+    assert extend(make_cache(), make_pages()) == 3                      # int8 stores: head_dim 128 only
+    assert extend(make_cache(D=128), make_pages(), cu=None) == 1        # int8 K and V at 128: accepted
+    assert extend(make_cache(fk=1, fv=3, D=128), make_pages()) == 3     # mixed int8 / ISO3
+    assert extend(make_cache(fk=4, fv=4, D=128), make_pages()) == 3     # F32 stores: no extend path
     assert extend(make_cache(fk=3, fv=3, D=256), make_pages()) == 3     # head_dim 128 only
     assert extend(iso(), make_pages(), max_new=65) == 2                 # max_new > n_new
     assert extend(iso(), make_pages(), n_new=-1, max_new=0) == 2
@@ -224,3 +227,5 @@ def test_extend_validation_errors():
     c = iso()
     assert L.kvq_extend_workspace_bytes(ctypes.byref(c), 1, 64, 64, 64, 16) == 2 * (16 + 1) * 36864
     assert L.kvq_extend_workspace_bytes(ctypes.byref(make_cache()), 1, 64, 64, 64, 16) == 0
+    i8 = make_cache(D=128)
+    assert L.kvq_extend_workspace_bytes(ctypes.byref(i8), 1, 64, 64, 64, 16) == 2 * (16 + 1) * 36864

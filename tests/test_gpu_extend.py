@@ -1,4 +1,4 @@
-"""GPU parity of extend (prefill chunk) attention over ISO3-packed prefixes, through the C ABI.
+"""GPU parity of extend (prefill chunk) attention over ISO3- and int8-packed prefixes, through the C ABI.
 
 Each case fills the cache with the prefix through kvq_append, runs kvq_extend_attn on the chunk's
 bf16 tokens (deferred packing on), and compares with the oracle: attention element by element
@@ -29,8 +29,8 @@ def chunk_inputs(w):
 
 def oracle_prefix_stores(w):
     pre = w.prefix_lens()
-    sk = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
-    sv = opaged.Store.empty("iso3", w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sv = opaged.Store.empty(w.fmt_v, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
     for b in range(w.batch):
         P = int(pre[b])
         if P:
@@ -44,7 +44,7 @@ def run_extend(w, head_map=None, pack_after=True):
     import torch
     import quantized_paged_kv_kvq_amd as kvq
     pre, cu, kn, vn = chunk_inputs(w)
-    cache = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, "iso3", "iso3", quat=w.quat)
+    cache = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, w.fmt_k, w.fmt_v, quat=w.quat)
     pages = kvq.Pages(dev_i32(w.block_table), dev_i32(pre))
     seqs = [np.full(int(pre[b]), b, np.int32) for b in range(w.batch)]
     if int(pre.sum()):
@@ -68,7 +68,7 @@ def oracle_extend(w, head_map=None, rows=None):
 
 
 def check(w, head_map=None):
-    print(f"extend case {w.name}: prefix {w.prefix_lens().tolist()} new {w.new_lens().tolist()} "
+    print(f"extend case {w.name} {w.fmt_k}: prefix {w.prefix_lens().tolist()} new {w.new_lens().tolist()} "
           f"Hq {w.n_q_heads} Hkv {w.n_kv_heads}", flush=True)
     cache, got = run_extend(w, head_map=head_map)
     ref = oracle_extend(w, head_map=head_map)
@@ -82,24 +82,49 @@ def test_extend_iso3_scaled():
     check(synth.ragged_extend([300], [200], seed=5, n_q_heads=32, n_kv_heads=8))
 
 
-def test_extend_ragged_batch():
+@pytest.mark.parametrize("fmt", ["iso3", "int8"])
+def test_extend_ragged_batch(fmt):
     """Empty, 1-cell, ragged and tile-boundary prefixes; chunks of 1, 63, 64, 65, 130 tokens."""
-    check(synth.ragged_extend([0, 1, 17, 64, 200], [1, 63, 64, 65, 130], seed=22))
+    check(synth.ragged_extend([0, 1, 17, 64, 200], [1, 63, 64, 65, 130], seed=22, fmt=fmt))
 
 
-def test_extend_sequence_without_new_tokens():
-    check(synth.ragged_extend([10, 40, 0], [0, 33, 5], seed=23))
+@pytest.mark.parametrize("fmt", ["iso3", "int8"])
+def test_extend_sequence_without_new_tokens(fmt):
+    check(synth.ragged_extend([10, 40, 0], [0, 33, 5], seed=23, fmt=fmt))
 
 
-def test_extend_uneven_head_map():
-    w = synth.ragged_extend([70, 5], [40, 21], seed=24, n_q_heads=6, n_kv_heads=2)
+@pytest.mark.parametrize("fmt", ["iso3", "int8"])
+def test_extend_uneven_head_map(fmt):
+    w = synth.ragged_extend([70, 5], [40, 21], seed=24, n_q_heads=6, n_kv_heads=2, fmt=fmt)
     check(w, head_map=[1, 0, 1, 1, 0, 1])
 
 
+@pytest.mark.parametrize("fmt", ["iso3", "int8"])
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 1), (32, 1)])
-def test_extend_group_widths(hq, hkv):
+def test_extend_group_widths(hq, hkv, fmt):
     """MHA (32 tokens per wave), MQA 16:1 and 32:1 (one token per wave)."""
-    check(synth.ragged_extend([100, 37], [150, 20], seed=25 + hq, n_q_heads=hq, n_kv_heads=hkv))
+    check(synth.ragged_extend([100, 37], [150, 20], seed=25 + hq, n_q_heads=hq, n_kv_heads=hkv, fmt=fmt))
+
+
+def test_extend_int8_groups_of_different_scale():
+    """int8 prefix whose two 64-value groups differ in scale by up to 2^12 per key (K and V), short
+    and long prefixes: each group's partial sums take their own scale.  Compared relative to the
+    output's magnitude (max-abs 1e-3 at unit scale)."""
+    from oracle.numerics import bf16_to_f32
+    w = synth.ragged_extend([1, 5, 17, 300], [3, 40, 64, 20], seed=28, fmt="int8")
+    rng = np.random.default_rng(29)
+    for b in range(w.batch):
+        L = len(w.k[b])
+        for x in (w.k, w.v):
+            f = bf16_to_f32(x[b]).copy()
+            f[:, :, 64:] *= (2.0 ** rng.integers(-6, 7, size=(L, w.n_kv_heads, 1))).astype(np.float32)
+            x[b] = synth.bf16_bits(f)
+    cache, got = run_extend(w)
+    ref = oracle_extend(w)
+    scale = float(np.max(np.abs(ref)))          # outputs up to 2^6 x unit scale: the bound is relative
+    assert_attention_close(got / scale, ref / scale)
+    sk, sv = oracle_stores(w)
+    assert_slabs_equal(cache, sk, sv)
 
 
 def test_extend_without_packing_leaves_prefix_only():
@@ -117,10 +142,11 @@ def test_extend_deterministic():
     assert np.array_equal(a, b)
 
 
-def test_extend_iso3_full_size_sampled():
-    """30,000-cell ISO3 prefix + 2,048 new tokens, 32 / 8 heads: every output element of sampled
+@pytest.mark.parametrize("fmt", ["iso3", "int8"])
+def test_extend_full_size_sampled(fmt):
+    """30,000-cell ISO3 (int8) prefix + 2,048 new tokens, 32 / 8 heads: every output element of sampled
     query tokens (first, tile edges, middle, last) against the oracle."""
-    w = synth.iso3_extend()
+    w = synth.iso3_extend(fmt=fmt)
     rows = np.array([0, 1, 31, 32, 63, 64, 127, 128, 1000, 1500, 2046, 2047])
     cache, got = run_extend(w)
     ref = oracle_extend(w, rows=rows)
