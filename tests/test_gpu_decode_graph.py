@@ -1,6 +1,7 @@
-"""GPU parity of decode with sequences that leave whole context splits empty, and of append +
-decode captured in a HIP graph: the graph is replayed several times, with eager work between the
-replays, and every replay must reproduce the eager result exactly.
+"""GPU parity of decode with sequences that leave whole context splits empty, and of append + decode
+(every store format mix the decode supports) and extend (ISO3 and int8 prefixes) captured in a HIP
+graph: the graph is replayed several times, with eager work between the replays, and every replay
+must reproduce the eager result exactly.
 """
 import numpy as np
 import pytest
@@ -38,10 +39,12 @@ def test_verify_k8v4_ragged_windows():
     assert_attention_close(_decode(w), oracle_decode(w, sk, sv))
 
 
-def test_decode_graph_replays():
+@pytest.mark.parametrize("fk,fv", [("int8", "int8"), ("int8", "f32"), ("f32", "int8"), ("iso4", "iso4"),
+                                   ("q4h", "q4h"), ("iso3", "iso3")])
+def test_decode_graph_replays(fk, fv):
     import torch
     import quantized_paged_kv_kvq_amd as kvq
-    w = synth.ragged_decode("int8", "int8", [4096, 300], seed=43, n_q_heads=16, n_kv_heads=2, head_dim=256)
+    w = synth.ragged_decode(fk, fv, [4096, 300], seed=43, n_q_heads=16, n_kv_heads=2, head_dim=256)
     cache, pages = gpu_cache(w)
     gpu_append(w, cache, pages, "prefix")
     step = [x for x in __import__("kvq_testutil").token_lists(w, "step")]
@@ -72,6 +75,55 @@ def test_decode_graph_replays():
     for i in range(4):
         out.zero_()
         junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager.cpu().numpy()), f"replay {i} differs from the eager run"
+        del junk
+
+
+@pytest.mark.parametrize("fmt", ["int8", "iso3"])
+def test_extend_graph_replays(fmt):
+    """Extend (stage + attention + deferred packing) captured once and replayed with eager work between
+    the replays: every replay reproduces the eager output."""
+    import torch
+    import quantized_paged_kv_kvq_amd as kvq
+    w = synth.ragged_extend([300, 70], [100, 45], seed=44, fmt=fmt)
+    pre, new = w.prefix_lens(), w.new_lens()
+    cache = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, w.fmt_k, w.fmt_v, quat=w.quat)
+    pages = kvq.Pages(dev_i32(w.block_table), dev_i32(pre))
+    tok_seq = np.concatenate([np.full(int(pre[b]), b, np.int32) for b in range(w.batch)])
+    tok_pos = np.concatenate([np.arange(int(pre[b]), dtype=np.int32) for b in range(w.batch)])
+    kvq.kvq_append(cache, pages, dev_bf16(np.concatenate([w.k[b][:int(pre[b])] for b in range(w.batch)])),
+                   dev_bf16(np.concatenate([w.v[b][:int(pre[b])] for b in range(w.batch)])), dev_i32(tok_seq),
+                   dev_i32(tok_pos))
+    kn = dev_bf16(np.concatenate([w.k[b][int(pre[b]):] for b in range(w.batch)]))
+    vn = dev_bf16(np.concatenate([w.v[b][int(pre[b]):] for b in range(w.batch)]))
+    cu = dev_i32(np.concatenate([[0], np.cumsum(new)]).astype(np.int32))
+    q = dev_bf16(w.q)
+    out = torch.empty((int(new.sum()), w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    nbytes = kvq.kvq_extend_workspace_bytes(cache, pages.batch, pages.max_pages, int(new.sum()), int(new.max()),
+                                            w.n_q_heads)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step_fn():
+        kvq.kvq_extend_attn(cache, pages, q, kn, vn, cu, int(new.max()), sm_scale=w.sm_scale, out=out,
+                            pack_after=True, workspace=ws)
+
+    step_fn()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step_fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_fn()
+    for i in range(4):
+        out.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager.cpu().numpy()), f"replay {i} differs from the eager run"
