@@ -31,7 +31,7 @@ UNITS = {
     "append.hip": ["-ffp-contract=off"],
     "gather.hip": ["-ffp-contract=off"],
     "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "decode_iso3.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+    "decode_iso.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
     "decode_q4.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode_f32.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "extend.hip": [],

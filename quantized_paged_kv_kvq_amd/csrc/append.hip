@@ -16,7 +16,7 @@
 //   F32        strata PR #2698, intro and "What it does" (the unquantised FP32 store of the
 //              single-store modes k8v32 / k32v8): the bf16 value widened to binary32, exact.
 #include "kvq_internal.h"
-#include "iso3_levels.h"
+#include "iso_levels.h"
 #include "int8_cell.h"
 
 namespace kvq {

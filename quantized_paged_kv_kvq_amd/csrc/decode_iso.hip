@@ -1,4 +1,4 @@
-// Split-K decode / verify attention over ISO3 K and V stores.
+// Split-K decode / verify attention over ISO3 (or ISO4) K and V stores.
 //
 // FreeToken PR #398, "Pull request overview": the ISO backend attends decode tokens over the packed
 // cells with its own kernel ("What": decode tokens are quantised as they are written), checked
@@ -39,7 +39,7 @@
 
 #include "kvq_internal.h"
 #include "device_util.h"
-#include "iso3_levels.h"
+#include "iso_levels.h"
 
 namespace kvq {
 namespace {
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a)
 }
 
 template <int BITS, int D, bool DUP, int SH>
-hipError_t launch_iso3_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_iso_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   constexpr IsoShape sh = kIsoShapes[SH];
   constexpr int pd = D == 128 ? sh.pd : (sh.pd + 1) / 2;
   k_decode_iso<BITS, D, DUP, sh.nw, sh.ppw, pd, sh.occ>
@@ -519,25 +519,25 @@ hipError_t launch_iso3_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_
 }
 
 template <int BITS, int D, bool DUP, int SH = 0>
-hipError_t launch_iso3_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_iso_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   if constexpr (SH + 1 < kNumIsoShapes)
-    if (plan.shape != SH) return launch_iso3_shape<BITS, D, DUP, SH + 1>(plan, a, s);
-  return launch_iso3_t<BITS, D, DUP, SH>(plan, a, s);
+    if (plan.shape != SH) return launch_iso_shape<BITS, D, DUP, SH + 1>(plan, a, s);
+  return launch_iso_t<BITS, D, DUP, SH>(plan, a, s);
 }
 
 template <int BITS>
 hipError_t launch_iso_bits(int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   const bool dup = plan.rows <= 8;
   switch (D) {
-    case 128: return dup ? launch_iso3_shape<BITS, 128, true>(plan, a, s) : launch_iso3_shape<BITS, 128, false>(plan, a, s);
-    case 256: return dup ? launch_iso3_shape<BITS, 256, true>(plan, a, s) : launch_iso3_shape<BITS, 256, false>(plan, a, s);
+    case 128: return dup ? launch_iso_shape<BITS, 128, true>(plan, a, s) : launch_iso_shape<BITS, 128, false>(plan, a, s);
+    case 256: return dup ? launch_iso_shape<BITS, 256, true>(plan, a, s) : launch_iso_shape<BITS, 256, false>(plan, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int max_rows) {
+DecodePlan plan_decode_iso(int head_dim, int hkv, int batch, int max_pages, int max_rows) {
   DecodePlan p{};
   p.rows = max_rows;
   p.row_groups = max(1, (max_rows + 7) / 8);        // partial rows: 8 (one MFMA half) or 16

@@ -45,7 +45,7 @@
 // dequantised values to fp16 instead (code x scale has up to 18 significant bits) measured up to
 // 1.8e-3 off on the CPU for short prefixes.  No rotation; head_dim 128 as ISO3.
 #include "kvq_internal.h"
-#include "iso3_levels.h"
+#include "iso_levels.h"
 #include "device_util.h"
 
 namespace kvq {

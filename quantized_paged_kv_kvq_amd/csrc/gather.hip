@@ -10,7 +10,7 @@
 //   ISO3/ISO4  conj(q) * centroid group (left to right), then times the norm
 //   F32        the stored binary32 value
 #include "kvq_internal.h"
-#include "iso3_levels.h"
+#include "iso_levels.h"
 
 namespace kvq {
 namespace {

@@ -254,7 +254,7 @@ static kvq_status decode_setup(const kvq_cache* cache, int32_t batch, int32_t ma
   if (q4k && (long)n_q * max_g > kQ4DecodeMaxRows)
     return fail(KVQ_ERR_UNSUPPORTED, "q4_0 K decode: n_q * (query heads per KV head) = %d exceeds %d", n_q * max_g,
                 kQ4DecodeMaxRows);
-  *plan = iso   ? plan_decode_iso3(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
+  *plan = iso   ? plan_decode_iso(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
           : q4k ? plan_decode_q4(cache->n_kv_heads, batch, max_pages, n_q * max_g)
           : f32 ? plan_decode_f32(D, cache->n_kv_heads, batch, max_pages, n_q * max_g)
                 : plan_decode(cache->v.fmt, D, cache->n_kv_heads, batch, max_pages, n_q * max_g);

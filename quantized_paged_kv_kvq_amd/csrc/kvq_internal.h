@@ -125,7 +125,7 @@ hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const 
 hipError_t launch_decode_combine(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 // ISO3 or ISO4 K and V stores (bits 3 or 4; head_dim 128 or 256, at most kIsoDecodeMaxRows rows per
 // KV head)
-DecodePlan plan_decode_iso3(int head_dim, int hkv, int batch, int max_pages, int max_rows);
+DecodePlan plan_decode_iso(int head_dim, int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode_iso(int bits, int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 // Q4_0_H256 K and V stores (head_dim 256, at most kQ4DecodeMaxRows rows per KV head)
 constexpr int kQ4DecodeMaxRows = 16;
