@@ -542,13 +542,14 @@ DecodePlan plan_decode_iso(int head_dim, int hkv, int batch, int max_pages, int 
   p.rows = max_rows;
   p.row_groups = max(1, (max_rows + 7) / 8);        // partial rows: 8 (one MFMA half) or 16
   p.row_tiles = 0;
-  // 64-page splits unless they would fill at most about half of the CUs; then 32-page splits
+  // 64-page splits unless they would give at most one workgroup per CU; then 32-page splits, two
+  // waves per SIMD (measured on one sequence at 131,072 tokens, 2 KV heads: 6% faster launches)
   auto splits_of = [&](int sh) {
     const int pps = kIsoShapes[sh].nw * kIsoShapes[sh].ppw;
     return (max_pages + pps - 1) / pps;
   };
   p.shape = iso_shape_override();
-  if (p.shape < 0) p.shape = ((long)splits_of(0) * hkv * batch * 20 <= (long)device_cu_count() * 11) ? 1 : 0;
+  if (p.shape < 0) p.shape = ((long)splits_of(0) * hkv * batch <= (long)device_cu_count()) ? 1 : 0;
   p.waves = kIsoShapes[p.shape].nw;
   p.pages_per_split = kIsoShapes[p.shape].nw * kIsoShapes[p.shape].ppw;
   p.n_splits = splits_of(p.shape);
