@@ -137,3 +137,34 @@ def test_fused_moe_full_size_131072():
     """The benchmark's workload and launch configuration at full size."""
     m = check_fused(synth.moe_int8_decode(ctx=131072))
     print(f"[fused 131072] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
+
+
+def test_fused_batched_full_size_sampled_sequences():
+    """The 32-sequence batched workload (4,096-32,768 tokens each, 32 / 8 heads, head_dim 128) at full
+    size in the benchmark's launch configuration (fused quantize-on-write + decode).  The oracle encodes
+    and attends a sample of sequences (shortest, longest, first, last); their step cells are compared
+    byte for byte and their outputs to the tolerance; the fused output equals append + decode bit for
+    bit over the whole batch."""
+    from oracle import paged as opaged
+    w = synth.batched_int8_decode()
+    lens = np.asarray(w.seq_lens)
+    seqs = sorted({0, w.batch - 1, int(np.argmin(lens)), int(np.argmax(lens))})
+    print(f"[fused batched] sampled sequences {seqs} of {w.batch}, lengths {[int(lens[b]) for b in seqs]}", flush=True)
+    cache, got = run_fused(w)
+    sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    sv = opaged.Store.empty(w.fmt_v, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    for b in seqs:
+        L = int(lens[b])
+        opaged.append(sk, w.block_table, np.full(L, b), np.arange(L), w.k[b], w.page_size)
+        opaged.append(sv, w.block_table, np.full(L, b), np.arange(L), w.v[b], w.page_size)
+    ref = oracle_decode(w, sk, sv, seqs=seqs)
+    assert_attention_close(got[seqs], ref[seqs])
+    kc, ks = (cache.k_codes.cpu().numpy(), cache.k_scales.cpu().numpy())
+    for b in seqs:                                   # the step's cell (last position) of each sampled sequence
+        pos = int(lens[b]) - 1
+        page, slot = int(w.block_table[b, pos // 16]), pos % 16
+        from kvq_testutil import tile_index
+        idx = tile_index("k_chunk", w.head_dim)[slot]
+        assert np.array_equal(kc[page][:, idx], sk.codes[page, :, slot, :]), f"K cell of sequence {b}"
+        assert np.array_equal(ks[page][:, slot].view(np.uint16), sk.scales[page, :, slot].view(np.uint16))
+    assert np.array_equal(got.view(np.uint32), run_unfused(w).view(np.uint32)), "fused and unfused outputs differ"
