@@ -310,7 +310,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="moe_int8_decode")
+    ap.add_argument("--workload", default="moe_int8_decode",
+                    help="moe_int8_decode (default), moe_int8_decode_64k, tiny_int8_decode, batched_int8_decode, k8v4_verify, "
+                         "iso3_extend, "
+                         "int8_extend, moe_q4h_decode, moe_iso3_decode, batched_iso3_decode, moe_iso4_decode, "
+                         "moe_k8v32_decode, moe_k32v8_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--unfused", action="store_true",
@@ -322,8 +326,8 @@ def main():
                     help="time only a plain streaming read and a plain copy of BYTES (context for the roofline)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the hot path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the hot path runs on one GPU "
+              f"per process, with no collectives)", file=sys.stderr)
         sys.exit(2)
 
     import torch
