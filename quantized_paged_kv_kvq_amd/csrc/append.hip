@@ -18,6 +18,7 @@
 #include "kvq_internal.h"
 #include "iso_levels.h"
 #include "int8_cell.h"
+#include "q4h_cell.h"
 
 namespace kvq {
 namespace {
@@ -116,27 +117,7 @@ __device__ __forceinline__ void append_f32(const AppendArgs& a, const uint16_t* 
 
 // ---------------------------------------------------------------------------------------------
 // Q4_0_H256 (K or V; their tiles differ in byte order).  One wave per cell; lane l holds elements
-// 4l .. 4l+3.
-// FWHT butterflies run in the order of spans 1, 2, 4, ..., 128: spans 1 and 2 inside a lane,
-// spans 4..128 between lanes l and l ^ (span / 4).  Each butterfly maps (a, b) -> (a + b, a - b)
-// for the pair (i, i + span), exactly as the definition, so the result is bit-identical to any
-// other evaluation of the same sequence of stages.
-__device__ __forceinline__ void fwht256_lane(float y[4], int lane) {
-  float a0 = y[0] + y[1], a1 = y[0] - y[1], a2 = y[2] + y[3], a3 = y[2] - y[3];   // span 1
-  y[0] = a0 + a2; y[2] = a0 - a2; y[1] = a1 + a3; y[3] = a1 - a3;                   // span 2
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {                                                // spans 4..128
-    const bool upper = (lane & o) != 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float other = __shfl_xor(y[e], o);
-      y[e] = upper ? (other - y[e]) : (y[e] + other);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) y[e] = y[e] * 0.0625f;
-}
-
+// 4l .. 4l+3 (the encoder is q4h_encode_x4).
 __device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* __restrict__ x,
                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, bool is_v,
                                            int block) {
@@ -149,27 +130,7 @@ __device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* 
   const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * 256 + 4 * lane);
   float y[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
                 bf16_to_f32(raw.y >> 16)};
-  fwht256_lane(y, lane);
-
-  // Signed max-abs of each block of 32 (= 8 lanes): the first index with the largest magnitude.
-  float best = y[0];
-  int bidx = 4 * lane;
-#pragma unroll
-  for (int e = 1; e < 4; ++e)
-    if (fabsf(y[e]) > fabsf(best)) { best = y[e]; bidx = 4 * lane + e; }
-#pragma unroll
-  for (int o = 4; o >= 1; o >>= 1) {
-    const float ob = __shfl_xor(best, o);
-    const int oi = __shfl_xor(bidx, o);
-    if (fabsf(ob) > fabsf(best) || (fabsf(ob) == fabsf(best) && oi < bidx)) { best = ob; bidx = oi; }
-  }
-  const float d = best / -8.0f;
-  uint32_t q[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    q[e] = 8;
-    if (best != 0.0f) q[e] = (uint32_t)fminf(fmaxf(rintf(y[e] / d) + 8.0f, 0.0f), 15.0f);
-  }
+  const Q4x4 e = q4h_encode_x4(y, lane);
   if (!active) return;
   int page, slot;
   locate(a, tok, page, slot);
@@ -177,10 +138,9 @@ __device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* 
   uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128;
   const int o0 = is_v ? v_tile_offset(2 * lane, slot) : k4_tile_offset(2 * lane, slot);
   const int o1 = is_v ? v_tile_offset(2 * lane + 1, slot) : k4_tile_offset(2 * lane + 1, slot);
-  base[o0] = (uint8_t)(q[0] | (q[1] << 4));
-  base[o1] = (uint8_t)(q[2] | (q[3] << 4));
-  if ((lane & 7) == 0)
-    scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)] = f32_to_f16_bits(best != 0.0f ? d : 0.0f);
+  base[o0] = e.b0;
+  base[o1] = e.b1;
+  if ((lane & 7) == 0) scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)] = e.d_bits;
 }
 
 // ---------------------------------------------------------------------------------------------

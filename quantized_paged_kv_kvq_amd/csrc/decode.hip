@@ -34,6 +34,7 @@
 #include "device_util.h"
 #include "int8_cell.h"
 #include "decode_parts.h"
+#include "q4h_cell.h"
 
 namespace kvq {
 namespace {
@@ -163,6 +164,34 @@ __device__ __forceinline__ void load_page_dev(PageBuf<D, 1>& pb, const DecodeArg
     pb.ks[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4, 0, 0x10);
     pb.vs[0] = __builtin_amdgcn_raw_buffer_load_b32(rv, 0, 0, 0x10);
     pb.vs[1] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4, 0, 0x10);
+  }
+}
+
+// The same for an int8 K + Hadamard-rotated q4_0 V page (head_dim 256).
+template <int D>
+__device__ __forceinline__ void load_page_dev(PageBuf<D, 2>& pb, const DecodeArgs& a, int page, int kvh, int lane) {
+  constexpr int NG = D / 64, NVG = D / 32;
+  const int i16 = lane & 15, j4 = lane >> 4;
+  const size_t tile = (size_t)page * a.hkv + kvh;
+  const uint8_t* kb = a.k_codes + tile * (16 * D);
+  const uint8_t* vb = a.v_codes + tile * (16 * (D / 2));
+#pragma unroll
+  for (int g = 0; g < NG; ++g) pb.k[g] = load_dev16(kb, 16 * (64 * g + lane));
+#pragma unroll
+  for (int G = 0; G < PageBuf<D, 2>::NVQ; ++G) pb.v[G] = load_dev16(vb, 16 * (64 * G + 4 * i16 + j4));
+  // scales of tokens 4 j4 .. 4 j4 + 3: (tile * 16 + 4 j4) * N halves from the (uniform) tile start
+  const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scales + tile * 16 * NG);
+  const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_scales + tile * 16 * NVG);
+  static_assert((2 * NG) % 4 == 0 && (2 * NVG) % 4 == 0, "scale words in 16-byte units");
+#pragma unroll
+  for (int c = 0; c < 2 * NG; c += 4) {
+    const uint4 x = load_dev16(ks, 8 * j4 * NG + 4 * c);
+    pb.ks[c] = x.x; pb.ks[c + 1] = x.y; pb.ks[c + 2] = x.z; pb.ks[c + 3] = x.w;
+  }
+#pragma unroll
+  for (int c = 0; c < 2 * NVG; c += 4) {
+    const uint4 x = load_dev16(vs, 8 * j4 * NVG + 4 * c);
+    pb.vs[c] = x.x; pb.vs[c + 1] = x.y; pb.vs[c + 2] = x.z; pb.vs[c + 3] = x.w;
   }
 }
 
@@ -444,7 +473,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     if constexpr (VF == 1) return __builtin_amdgcn_readlane(my_ids, i);
     else return clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1);
   };
-  // Fused quantize-on-write (int8 V only): new token t of this sequence goes to position
+  // Fused quantize-on-write (int8 K; int8 or, at head_dim 256, Hadamard-rotated q4_0 V): new token t
+  // of this sequence goes to position
   // seq_len - n_q + t.  The wave whose page list holds that cell loads the token now, encodes and
   // stores it before the page loop and waits for the stores, so the loop's load of that page
   // returns the cell; a page the prologue already loaded is loaded again (device scope, past the
@@ -457,7 +487,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   for (int t = 0; t < kDecodeMaxFused; ++t) {
     fz_idx[t] = -1;
     fz_slot[t] = 0;
-    if (VF == 1 && a.k_new && t < a.n_q) {
+    if (a.k_new && t < a.n_q) {
       const int pos = clampi(seq_len - a.n_q + t, 0, cap - 1);
       const int pl = pos / KVQ_PAGE_SIZE - p_begin;
       if (pl >= 0 && pl < a.pages_per_split && pl % NW == wv) {
@@ -501,13 +531,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   // ---- encode this wave's new cells into the cache; pages of the prologue that hold one are
   // loaded again once the stores have completed
-  if (VF == 1 && fz_mask) {
+  bool fz_small = false;                                   // a new q4_0 V cell has a d below 2^-10
+  if (fz_mask) {
 #pragma unroll
     for (int t = 0; t < kDecodeMaxFused; ++t) {
       if (fz_idx[t] < 0) continue;
-      const size_t tile = (size_t)__builtin_amdgcn_readlane(my_ids, fz_idx[t]) * a.hkv + kvh;
+      const size_t tile = (size_t)page_id(fz_idx[t]) * a.hkv + kvh;
+      if constexpr (VF == 2) {                              // q4_0 V: the whole wave encodes one cell
+        static_assert(VF != 2 || D == 256, "Hadamard-rotated q4_0 needs head_dim 256");
+        float y[4] = {bf16f(fz_x[t][1].x & 0xffffu), bf16f(fz_x[t][1].x >> 16), bf16f(fz_x[t][1].y & 0xffffu),
+                      bf16f(fz_x[t][1].y >> 16)};
+        const Q4x4 e = q4h_encode_x4(y, lane);
+        uint8_t* codes = const_cast<uint8_t*>(a.v_codes) + tile * (KVQ_PAGE_SIZE * (D / 2));
+        codes[v_tile_offset(2 * lane, fz_slot[t])] = e.b0;
+        codes[v_tile_offset(2 * lane + 1, fz_slot[t])] = e.b1;
+        if ((lane & 7) == 0)
+          const_cast<uint16_t*>(a.v_scales)[(tile * KVQ_PAGE_SIZE + fz_slot[t]) * (D / 32) + (lane >> 3)] = e.d_bits;
+        fz_small = fz_small || (uint16_t)((e.d_bits & 0x7fffu) - 1u) < 0x13ffu;
+      }
 #pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
+      for (int kv = 0; kv < (VF == 1 ? 2 : 1); ++kv) {
         const float x[4] = {bf16f(fz_x[t][kv].x & 0xffffu), bf16f(fz_x[t][kv].x >> 16),
                             bf16f(fz_x[t][kv].y & 0xffffu), bf16f(fz_x[t][kv].y >> 16)};
         const Int8x4 e = int8_encode_x4(x);
@@ -526,12 +569,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     }
     // the stores complete before any later load of this wave (the page loop's loads of these pages)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (VF == 1) {
 #pragma unroll
-      for (int i = 0; i < PD && i < PPW; ++i)
-        if ((fz_mask >> i) & 1)
-          load_page_dev<D>(buf[i], a, __builtin_amdgcn_readlane(my_ids, i), kvh, lane);
-    }
+    for (int i = 0; i < PD && i < PPW; ++i)
+      if ((fz_mask >> i) & 1) load_page_dev<D>(buf[i], a, page_id(i), kvh, lane);
   }
 
   if (R == 0) return;
@@ -639,7 +679,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
         for (int e = 0; e < 4; ++e)
           mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, wd[e] & 0x7fff7fffu) - u16x2{1, 1});
       }
-      if (__any(mn[0] < 0x13ffu || mn[1] < 0x13ffu)) run(std::false_type{});
+      // (the scan's plain loads may return a fused cell's slot as it was before this wave's store,
+      // from the CU's L1; the encoder's own check covers the new d)
+      if (__any(mn[0] < 0x13ffu || mn[1] < 0x13ffu || fz_small)) run(std::false_type{});
       else run(std::true_type{});
     } else {
 #pragma unroll

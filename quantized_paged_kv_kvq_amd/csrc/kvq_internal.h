@@ -89,7 +89,7 @@ struct DecodeArgs {
   int row_alloc;            // rows of the partials per (sequence, KV head): 8 * row_groups
   int16_t head_off[KVQ_MAX_Q_HEADS + 1];
   int16_t head_list[KVQ_MAX_Q_HEADS];
-  // fused quantize-on-write (INT8_G64 K and V): new token t of sequence b, bf16
+  // fused quantize-on-write (INT8_G64 K; INT8_G64 or Q4_0_H256 V): new token t of sequence b, bf16
   // [batch][n_q][hkv][head_dim], is encoded into position seq_lens[b] - n_q + t before the
   // attention reads it; nullptr: plain decode
   const uint16_t* k_new;

@@ -168,3 +168,34 @@ def test_fused_batched_full_size_sampled_sequences():
         assert np.array_equal(kc[page][:, idx], sk.codes[page, :, slot, :]), f"K cell of sequence {b}"
         assert np.array_equal(ks[page][:, slot].view(np.uint16), sk.scales[page, :, slot].view(np.uint16))
     assert np.array_equal(got.view(np.uint32), run_unfused(w).view(np.uint32)), "fused and unfused outputs differ"
+
+@pytest.mark.parametrize("lens", [[33, 2500], [16, 17, 1000]])
+def test_fused_k8v4_single_query(lens):
+    """int8 K + Hadamard-rotated q4_0 V, one query token, 8 rows per KV head (duplicated columns)."""
+    check_fused(synth.ragged_decode("int8", "q4h", lens, seed=55 + len(lens), n_q_heads=16, n_kv_heads=2,
+                                    head_dim=256))
+
+
+@pytest.mark.parametrize("ctx", [3, 17, 2500])
+def test_fused_k8v4_verify_windows(ctx):
+    """k8v4 MTP verify (3 tokens, 24 rows in two row tiles) with the window's cells written by the launch,
+    on and across page edges."""
+    check_fused(synth.k8v4_verify(ctx=ctx, seed=56 + ctx))
+
+
+def test_fused_k8v4_small_new_v_scale():
+    """The row-tile kernel's fp16 V parts need every V d of a wave's pages >= 2^-10: a window whose new
+    V tokens are tiny (d far below that) while the cache holds ordinary values must take the bf16
+    parts, decided from the encoder's d (the scale scan may read the slot as it was before the store)."""
+    from oracle.numerics import bf16_to_f32
+    w = synth.k8v4_verify(ctx=700, seed=57)
+    v = bf16_to_f32(w.v[0]).copy()
+    v[-3:] *= np.float32(1e-5)
+    w.v[0] = synth.bf16_bits(v)
+    check_fused(w)
+
+
+def test_fused_k8v4_full_size_118750():
+    """The k8v4 verify workload at full size in the fused launch configuration."""
+    m = check_fused(synth.k8v4_verify())
+    print(f"[fused k8v4 118750] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
