@@ -84,8 +84,9 @@ def algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v, fused=False):
 
 def fusable(w):
     """The step can run as one fused quantize-on-write + decode launch sequence."""
-    v_ok = w.fmt_v == "int8" or (w.fmt_v == "q4h" and w.head_dim == 256)
-    return w.fmt_k == "int8" and v_ok and w.n_step == w.n_q and 1 <= w.n_q <= 4
+    plain = w.fmt_k in ("int8", "f32") and w.fmt_v in ("int8", "f32")
+    k8v4 = w.fmt_k == "int8" and w.fmt_v == "q4h" and w.head_dim == 256
+    return (plain or k8v4) and w.n_step == w.n_q and 1 <= w.n_q <= 4
 
 
 def recorded_traffic(workload: str):

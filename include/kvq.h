@@ -228,8 +228,8 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
  *                  of sequence b goes to position seq_lens[b] - n_q + t
  *   seq_lens     : already counts the new tokens (seq_lens[b] >= n_q)
  * Other arguments, workspace and limits as for kvq_decode_attn (same workspace size).
- * Requires an INT8_G64 K store, an INT8_G64 V store or a Q4_0_H256 V store at head_dim 256
- * (k8v4: [ST120] "How"), and 1 <= n_q <= 4.  A page holding new cells must not
+ * Requires INT8_G64 or F32 K and V stores (the single-store modes included), or an INT8_G64
+ * K store with a Q4_0_H256 V store at head_dim 256 (k8v4: [ST120] "How"), and 1 <= n_q <= 4.  A page holding new cells must not
  * be read by another sequence of the batch in the same call (pages written by a step are
  * owned by their sequence). */
 kvq_status kvq_decode_attn_append(const kvq_cache* cache, const kvq_pages* pages,

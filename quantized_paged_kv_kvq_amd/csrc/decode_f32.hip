@@ -29,6 +29,7 @@
 #include "kvq_internal.h"
 #include "device_util.h"
 #include "decode_parts.h"
+#include "int8_cell.h"
 
 namespace kvq {
 namespace {
@@ -94,6 +95,45 @@ __device__ __forceinline__ void load_fpage(FPage<D, KF, VF>& pb, const DecodeArg
 #pragma unroll
   for (int u = 0; u < P::NV; ++u) pb.v[u] = stream_load(vb + 64 * u);
   if constexpr (!VF) load_scale_words(pb.vs, a.v_scales + (tile * 16 + 4 * j4) * P::NG);
+}
+
+// Device-scope 16-byte load at a byte offset from a wave-uniform base: it misses the CU's L1 and reads
+// L2, so a page this wave loaded, then wrote a cell into (and waited for), comes back with it.
+__device__ __forceinline__ uint4 load_dev(const void* base, uint32_t off) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0x10 /* sc1: device scope */);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int D, bool KF, bool VF>
+__device__ __forceinline__ void load_fpage_dev(FPage<D, KF, VF>& pb, const DecodeArgs& a, int page, int kvh,
+                                               int lane) {
+  using P = FPage<D, KF, VF>;
+  const int i16 = lane & 15, j4 = lane >> 4;
+  const size_t tile = (size_t)page * a.hkv + kvh;
+  const uint8_t* kb = a.k_codes + tile * (16 * (KF ? 4 * D : D));
+#pragma unroll
+  for (int u = 0; u < P::NK; ++u) pb.k[u] = load_dev(kb, 16 * (64 * u + lane));
+  const uint8_t* vb = a.v_codes + tile * (16 * (VF ? 4 * D : D));
+#pragma unroll
+  for (int u = 0; u < P::NV; ++u) pb.v[u] = load_dev(vb, 16 * (64 * u + 4 * i16 + j4));
+  // scales of tokens 4 j4 .. 4 j4 + 3 (NG halves each) from the tile's first scale
+  if constexpr (!KF) {
+    const uint16_t* ks = a.k_scales + tile * 16 * P::NG;
+#pragma unroll
+    for (int c = 0; c < P::NG / 2; ++c) {
+      const uint4 x = load_dev(ks, 8 * j4 * P::NG + 16 * c);
+      pb.ks[4 * c] = x.x; pb.ks[4 * c + 1] = x.y; pb.ks[4 * c + 2] = x.z; pb.ks[4 * c + 3] = x.w;
+    }
+  }
+  if constexpr (!VF) {
+    const uint16_t* vs = a.v_scales + tile * 16 * P::NG;
+#pragma unroll
+    for (int c = 0; c < P::NG / 2; ++c) {
+      const uint4 x = load_dev(vs, 8 * j4 * P::NG + 16 * c);
+      pb.vs[4 * c] = x.x; pb.vs[4 * c + 1] = x.y; pb.vs[4 * c + 2] = x.z; pb.vs[4 * c + 3] = x.w;
+    }
+  }
 }
 
 // 8 binary32 values (two 16-byte chunks) -> bf16 hi (truncated) and bf16 lo (the exact remainder,
@@ -279,6 +319,58 @@ __global__ __launch_bounds__(NW * 64, 1) void k_decode_f32(const DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < PD && i < PPW; ++i)
     load_fpage(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, lane);
+
+  // Fused quantize-on-write (kvq_decode_attn_append): new token t goes to position seq_len - n_q + t.
+  // The wave whose page list holds that cell encodes it (int8 store) or writes its values (FP32
+  // store) before its page loop and waits for the stores; a page the prologue already loaded is
+  // loaded again with device-scope loads, past the CU's L1.
+  if (a.k_new) {
+    int fz_mask = 0;
+    for (int t = 0; t < a.n_q && t < kDecodeMaxFused; ++t) {
+      const int pos = clampi(seq_len - a.n_q + t, 0, cap - 1);
+      const int pl = pos / KVQ_PAGE_SIZE - p_begin;
+      if (pl < 0 || pl >= a.pages_per_split || pl % NW != wv) continue;
+      const int i = pl / NW, slot = pos % KVQ_PAGE_SIZE;
+      const size_t tile = (size_t)clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1) * a.hkv + kvh;
+      const size_t off = ((size_t)(b * a.n_q + t) * a.hkv + kvh) * D + 4 * min(lane, D / 4 - 1);
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const uint2 raw = *reinterpret_cast<const uint2*>((kv ? a.v_new : a.k_new) + off);
+        const float x[4] = {bf16f(raw.x & 0xffffu), bf16f(raw.x >> 16), bf16f(raw.y & 0xffffu), bf16f(raw.y >> 16)};
+        if (kv ? VF : KF) {                                 // FP32 store: the bf16 values widened
+          uint8_t* codes = const_cast<uint8_t*>(kv ? a.v_codes : a.k_codes) + tile * (KVQ_PAGE_SIZE * 4 * D);
+          if (lane < D / 4) {
+            if (kv == 0) {
+              *reinterpret_cast<float4*>(codes + k_tile_offset(16 * lane, slot)) = make_float4(x[0], x[1], x[2], x[3]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(codes + vf32_tile_offset(4 * (4 * lane + e), slot)) = x[e];
+            }
+          }
+        } else {                                            // int8 store: the append kernel's encoder
+          const Int8x4 en = int8_encode_x4(x);
+          uint8_t* codes = const_cast<uint8_t*>(kv ? a.v_codes : a.k_codes) + tile * (KVQ_PAGE_SIZE * D);
+          if (lane < D / 4) {
+            if (kv == 0) {
+              *reinterpret_cast<uint32_t*>(codes + k_tile_offset(4 * lane, slot)) = en.packed;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) codes[v_tile_offset(4 * lane + q, slot)] = (uint8_t)(en.packed >> (8 * q));
+            }
+            if ((lane & 15) == 0)
+              const_cast<uint16_t*>(kv ? a.v_scales : a.k_scales)[(tile * KVQ_PAGE_SIZE + slot) * NG + (lane >> 4)] =
+                  en.scale_bits;
+          }
+        }
+      }
+      if (i < PD) fz_mask |= 1 << i;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores complete before later loads
+#pragma unroll
+    for (int i = 0; i < PD && i < PPW; ++i)
+      if ((fz_mask >> i) & 1)
+        load_fpage_dev(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, lane);
+  }
 
   int Lmax = 0;
   for (int t = 0; t < a.n_q; ++t)

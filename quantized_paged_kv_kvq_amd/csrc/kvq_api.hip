@@ -344,13 +344,14 @@ kvq_status kvq_decode_attn_append(const kvq_cache* cache, const kvq_pages* pages
                                   void* workspace, size_t workspace_bytes, void* stream) {
   kvq_status st;
   if ((st = check_cache(cache)) != KVQ_OK) return st;
-  const bool k8v8 = cache->k.fmt == KVQ_FMT_INT8_G64 && cache->v.fmt == KVQ_FMT_INT8_G64;
-  const bool k8v4 = cache->k.fmt == KVQ_FMT_INT8_G64 && cache->v.fmt == KVQ_FMT_Q4_0_H256 && cache->head_dim == 256;
-  if (!k8v8 && !k8v4)
+  const int fk = cache->k.fmt, fv = cache->v.fmt;
+  const bool i8f32 = (fk == KVQ_FMT_INT8_G64 || fk == KVQ_FMT_F32) && (fv == KVQ_FMT_INT8_G64 || fv == KVQ_FMT_F32);
+  const bool k8v4 = fk == KVQ_FMT_INT8_G64 && fv == KVQ_FMT_Q4_0_H256 && cache->head_dim == 256;
+  if (!i8f32 && !k8v4)
     return fail(KVQ_ERR_UNSUPPORTED,
-                "fused append + decode needs INT8_G64 K and an INT8_G64 or (head_dim 256) Q4_0_H256 V store "
-                "(got formats %d / %d)",
-                cache->k.fmt, cache->v.fmt);
+                "fused append + decode needs INT8_G64 or F32 K and V stores, or INT8_G64 K with a (head_dim 256) "
+                "Q4_0_H256 V store (got formats %d / %d)",
+                fk, fv);
   if (n_q < 1 || n_q > kDecodeMaxFused)
     return fail(KVQ_ERR_UNSUPPORTED, "fused append + decode takes 1..%d new tokens per sequence (got %d)",
                 kDecodeMaxFused, n_q);

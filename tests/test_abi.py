@@ -138,6 +138,8 @@ def test_decode_append_validation_errors():
     assert decode_append(None, make_pages()) == 1
     assert decode_append(make_cache(fv=2, D=128), make_pages()) == 3    # q4_0 V: head_dim 256 only
     assert decode_append(make_cache(fk=2, fv=2), make_pages()) == 3     # fused path: int8 K only
+    assert decode_append(make_cache(fk=3, fv=3, D=128), make_pages()) == 3   # no fused ISO3 step
+    assert decode_append(make_cache(fk=4, fv=2), make_pages()) == 3     # F32 K with q4_0 V
     assert decode_append(make_cache(fk=3, fv=3, D=128), make_pages()) == 3
     assert decode_append(make_cache(), make_pages(), n_q=5, hq=4) == 3  # at most 4 new tokens per sequence
     assert decode_append(make_cache(), make_pages(), n_q=0) == 3

@@ -199,3 +199,22 @@ def test_fused_k8v4_full_size_118750():
     """The k8v4 verify workload at full size in the fused launch configuration."""
     m = check_fused(synth.k8v4_verify())
     print(f"[fused k8v4 118750] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
+
+
+@pytest.mark.parametrize("fk,fv", [("int8", "f32"), ("f32", "int8"), ("f32", "f32")])
+@pytest.mark.parametrize("D", [128, 256])
+def test_fused_single_store_modes(fk, fv, D):
+    """k8v32 / k32v8 / FP32: the step's cells written by the decode launch (int8 encoded or FP32 values),
+    one query token and a verify window across page edges; a KV head without queries still appends."""
+    check_fused(synth.ragged_decode(fk, fv, [1, 17, 300, 2100], seed=60 + D, n_q_heads=8, n_kv_heads=2,
+                                    head_dim=D))
+    check_fused(synth.ragged_decode(fk, fv, [3, 16, 18, 1000], seed=61 + D, n_q=3, q_len_back=[2, 1, 0],
+                                    n_q_heads=16, n_kv_heads=2, head_dim=D))
+    w = synth.ragged_decode(fk, fv, [40, 300], seed=62 + D, n_q_heads=4, n_kv_heads=3, head_dim=D)
+    check_fused(w, head_map=[0, 2, 0, 2])
+
+
+def test_fused_k8v32_full_size_131072():
+    """The k8v32 workload at full size in the fused launch configuration."""
+    m = check_fused(synth.moe_single_store_decode("int8", "f32", ctx=131072))
+    print(f"[fused k8v32 131072] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
