@@ -1,5 +1,6 @@
 """GPU parity of the fused decode step (kvq_decode_attn_append: quantize-on-write of the step's
-tokens and decode attention in one launch sequence), through the C ABI.
+tokens and decode attention in one launch sequence), through the C ABI, for int8 K and V, the k8v4
+hybrid (q4_0 V encoded by one wave per cell) and the single-store modes (int8 / FP32 stores).
 
 Every case checks the slabs byte for byte against the oracle's encoding of every token (prefix
 and step), the attention against the oracle (max-abs 1e-3, cosine > 0.9999 over the tensor and
