@@ -107,40 +107,109 @@ def recorded_traffic(workload: str):
     return int(m.group(4))
 
 
-def cpu_baseline(w, budget_s: float = 15.0):
-    """Time the oracle's step (encode the step's tokens, then fp64 attention over the dequantised
-    cache) on the host cores; the oracle's cache is filled first, outside the timing."""
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from oracle import attention as oatt
-    from oracle import paged as opaged
+def host_info():
+    """CPU model, the machine's physical cores and the threads this process may run on."""
+    model, cores, phys, core = None, set(), None, None
+    try:
+        for line in open("/proc/cpuinfo"):
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "model name" and model is None:
+                model = val
+            elif key == "physical id":
+                phys = val
+            elif key == "core id":
+                core = val
+            elif not key and phys is not None:
+                cores.add((phys, core))
+                phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "usable_threads": usable}
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        threads = 1
+        return 1
+
+
+def cpu_baseline(w, budget_s: float = 15.0, gpu_out=None, gpu_cache=None):
+    """Time the oracle's step (encode the step's tokens, then fp64 attention over the dequantised
+    cache) on the host cores -- all the threads its BLAS pool has, then one thread -- with the
+    oracle's cache filled first, outside the timing.  Returns (baseline, parity): the parity verdict
+    of the GPU step's output and cache slabs against the oracle's (when they are passed in)."""
+    from oracle import attention as oatt
+    from oracle import paged as opaged
+    threads = blas_threads()
     sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
     sv = opaged.Store.empty(w.fmt_v, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
     for b in range(w.batch):
         P = int(w.seq_lens[b]) - w.n_step
         opaged.append(sk, w.block_table, np.full(P, b), np.arange(P), w.k[b][:P], w.page_size, quat=w.quat)
         opaged.append(sv, w.block_table, np.full(P, b), np.arange(P), w.v[b][:P], w.page_size, quat=w.quat)
-    times = []
-    t_all = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
+
+    def step():
         for b in range(w.batch):
             L = int(w.seq_lens[b])
             pos = np.arange(L - w.n_step, L)
             opaged.append(sk, w.block_table, np.full(w.n_step, b), pos, w.k[b][L - w.n_step:], w.page_size, quat=w.quat)
             opaged.append(sv, w.block_table, np.full(w.n_step, b), pos, w.v[b][L - w.n_step:], w.page_size, quat=w.quat)
-        oatt.decode(sk, sv, w.block_table, w.seq_lens, w.q, w.page_size, w.sm_scale, q_lens=w.q_lens, quat=w.quat)
+        return oatt.decode(sk, sv, w.block_table, w.seq_lens, w.q, w.page_size, w.sm_scale, q_lens=w.q_lens,
+                           quat=w.quat)
+
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        ref = step()
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_all > budget_s or len(times) >= 20:
             break
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            step()
+            one = time.perf_counter() - t0
+    except ImportError:
+        pass
     per_step = float(np.median(times))
-    return {"value": per_step * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
+    base = {"value": per_step * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(times)} full steps of the same workload (median); numpy fp32 encode of the "
-                      f"step's tokens + fp64 attention over all {int(np.sum(w.seq_lens))} cells"}
+                      f"step's tokens + fp64 attention over all {int(np.sum(w.seq_lens))} cells",
+            "value_1thread": round(one * 1e6, 1) if one is not None else None, **host_info()}
+    parity = None
+    if gpu_out is not None:
+        parity = parity_verdict(w, sk, sv, ref, gpu_out, gpu_cache)
+    return base, parity
+
+
+def parity_verdict(w, sk, sv, ref, gpu_out, gpu_cache):
+    """The benched step against the oracle, computed outside the timed region: attention errors over
+    every output element and row, and byte mismatches of every cell of both stores (codes and scales)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from kvq_testutil import attention_errors, gpu_slabs_token_major
+    maxabs, cos, row_cos = attention_errors(gpu_out, ref)
+    code_bad = scale_bad = 0
+    for which, st in (("k", sk), ("v", sv)):
+        codes, scales = gpu_slabs_token_major(gpu_cache, which)
+        code_bad += int(np.count_nonzero(codes != st.codes))
+        scale_bad += int(np.count_nonzero(scales.view(np.uint16) != st.scales.view(np.uint16)))
+    ok = maxabs <= 1e-3 and cos > 0.9999 and row_cos > 0.9999 and code_bad == 0 and scale_bad == 0
+    return {"max_abs": float(f"{maxabs:.3e}"), "cosine": round(cos, 9), "min_row_cosine": round(row_cos, 9),
+            "code_byte_mismatches": code_bad, "scale_mismatches": scale_bad,
+            "cells_checked": int(np.sum(w.seq_lens)) * w.n_kv_heads * 2, "pass": bool(ok),
+            "bar": "max-abs <= 1e-3, cosine and min row cosine > 0.9999, codes and scales byte-identical"}
 
 
 def extend_flops(w):
@@ -155,11 +224,7 @@ def extend_cpu_baseline(w, budget_s: float = 15.0):
     the chunk's tokens (deferred packing); the oracle's prefix is encoded first, outside the timing."""
     from oracle import attention as oatt
     from oracle import paged as opaged
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    threads = blas_threads()
     pre, new = w.prefix_lens(), w.new_lens()
     P, N = int(pre[0]), int(new[0])
     sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
@@ -185,13 +250,14 @@ def extend_cpu_baseline(w, budget_s: float = 15.0):
     per_step = t_rows * N / len(rows) + t_pack
     return {"value": per_step * 1e6, "unit": "us/step", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 attention of {len(rows)} of {N} query tokens (all {w.n_q_heads} heads, "
-                      f"{n_calls} runs) scaled by {N}/{len(rows)}, plus the numpy encode of the {N} new tokens"}
+                      f"{n_calls} runs) scaled by {N}/{len(rows)}, plus the numpy encode of the {N} new tokens",
+            **host_info()}
 
 
 def bench_extend(args):
     import torch
     import quantized_paged_kv_kvq_amd as kvq
-    from kvq_testutil import dev_bf16, dev_i32
+    from synth import dev_bf16, dev_i32
 
     w = make_workload(args.workload)
     pre, new = w.prefix_lens(), w.new_lens()
@@ -271,6 +337,22 @@ def bench_extend(args):
     print(json.dumps(line))
 
 
+def time_batches(stream, n_batches, per_batch, graph, eager):
+    """Per-launch µs of each of n_batches batches of per_batch launches (a graph replay, or the eager
+    launches), from HIP events recorded on the launch stream around each batch."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_batches)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            eager()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 / per_batch for a, b in evs]
+
+
 def copy_probe(nbytes: int):
     """A plain copy of a known number of bytes (torch's elementwise copy kernel), five times: the
     per-dispatch FETCH_SIZE / WRITE_SIZE counters of this kernel calibrate those of the others."""
@@ -334,8 +416,7 @@ def main():
 
     import torch
     import quantized_paged_kv_kvq_amd as kvq
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from kvq_testutil import dev_bf16, dev_i32, token_lists
+    from synth import dev_bf16, dev_i32, token_lists
 
     torch.cuda.set_device(0)
     if args.copy_probe:
@@ -365,6 +446,9 @@ def main():
             kvq.kvq_append(c, pages, dev_bf16(pre[2]), dev_bf16(pre[3]), dev_i32(pre[0]), dev_i32(pre[1]))
         caches.append(c)
     s_seq, s_pos, s_k, s_v = (dev_i32(step[0]), dev_i32(step[1]), dev_bf16(step[2]), dev_bf16(step[3]))
+    # the fused call takes the step's tokens as [batch][n_q][n_kv_heads][head_dim] (sequence, then position)
+    f_k = s_k.view(w.batch, w.n_step, w.n_kv_heads, w.head_dim) if fusable(w) else None
+    f_v = s_v.view(w.batch, w.n_step, w.n_kv_heads, w.head_dim) if fusable(w) else None
     q = dev_bf16(w.q)
     q_lens = dev_i32(w.q_lens) if w.q_lens is not None else None
     out = torch.empty((w.batch, w.n_q, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
@@ -382,20 +466,23 @@ def main():
     def one_step(i, stream):
         c = caches[i % R]
         if fused:
-            kvq.kvq_decode_attn_append(c, pages, s_k, s_v, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out,
+            kvq.kvq_decode_attn_append(c, pages, f_k, f_v, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out,
                                        workspace=ws, stream=stream)
             return
         kvq.kvq_append(c, pages, s_k, s_v, s_seq, s_pos, stream=stream)
         kvq.kvq_decode_attn(c, pages, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out, workspace=ws, stream=stream)
 
+    def decode_one(i, stream):
+        if fused:
+            kvq.kvq_decode_attn_append(caches[i], pages, f_k, f_v, q, q_lens=q_lens, sm_scale=w.sm_scale,
+                                       out=out, workspace=ws, stream=stream)
+        else:
+            kvq.kvq_decode_attn(caches[i], pages, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out,
+                                workspace=ws, stream=stream)
+
     def decode_batch(stream):
         for i in range(R):
-            if fused:
-                kvq.kvq_decode_attn_append(caches[i], pages, s_k, s_v, q, q_lens=q_lens, sm_scale=w.sm_scale,
-                                           out=out, workspace=ws, stream=stream)
-            else:
-                kvq.kvq_decode_attn(caches[i], pages, q, q_lens=q_lens, sm_scale=w.sm_scale, out=out,
-                                    workspace=ws, stream=stream)
+            decode_one(i, stream)
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -450,28 +537,41 @@ def main():
 
     # Roofline of the decode attention launch: HIP events on the launch stream around batches of
     # back-to-back decode launches, one per cache copy in turn (so each reads HBM, not cache), so
-    # the events' own fixed cost is spread over the batch.
-    n_batches, per_batch = max(1, args.steps // R), R
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_batches)]
-    for j in range(n_batches):
-        evs[j][0].record(stream)
-        if dec_graph is not None:
-            dec_graph.replay()
-        else:
-            decode_batch(stream)
-        evs[j][1].record(stream)
-    torch.cuda.synchronize()
-    dec_us = [a.elapsed_time(b) * 1e3 / per_batch for a, b in evs]
+    # the events' own fixed cost is spread over the batch.  At least 20 batches whatever --steps is.
+    # At least 100 batches whatever --steps is (a few milliseconds of GPU time): their spread gives the
+    # percentiles.  (Events around single one-launch graph replays would add each replay's own launch
+    # cost, about 7 us here, to every sample.)
+    n_batches, per_batch = max(100, args.steps // R), R
+    dec_us = time_batches(stream, n_batches, per_batch, dec_graph, lambda: decode_batch(stream))
     dec_avg = float(np.mean(dec_us))
     algo = algorithmic_bytes(w, cb_k, ns_k, cb_v, ns_v, fused)
     achieved = algo / (dec_avg * 1e-6) / 1e9
-    print(f"[bench] {mode}: decode launch avg {dec_avg:.2f} us over {n_batches} x {per_batch} launches, step "
-          f"{ms_per_step * 1e3:.2f} us, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    # Warm: the same launches all on one cache copy, which then stays in the 256 MB Infinity Cache
+    # (when it fits): context for the MALL-defeated figures above, not a headline.
+    warm_us = None
+    if R > 1:
+        warm_graph = None
+        if graphs:
+            warm_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(warm_graph):
+                for _ in range(R):
+                    decode_one(0, torch.cuda.current_stream())
+            warm_graph.replay()
+            torch.cuda.synchronize()
+        warm_us = float(np.mean(time_batches(stream, 20, R, warm_graph,
+                                             lambda: [decode_one(0, stream) for _ in range(R)])))
+    pct = {k: round(float(np.percentile(dec_us, q)), 3) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+    print(f"[bench] {mode}: decode launch avg {dec_avg:.2f} us over {n_batches} x {per_batch} launches "
+          f"(p10/p50/p90 {pct['p10']}/{pct['p50']}/{pct['p90']}), step {ms_per_step * 1e3:.2f} us, "
+          f"{achieved:.0f} GB/s; warm {warm_us if warm_us is None else round(warm_us, 2)} us",
+          file=sys.stderr, flush=True)
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w)
+        print("[bench] timing the CPU oracle on a bounded sample; parity of the benched step", file=sys.stderr,
+              flush=True)
+        torch.cuda.synchronize()
+        cpu, parity = cpu_baseline(w, gpu_out=out.cpu().numpy(), gpu_cache=caches[0])
 
     line = {
         "metric": METRIC,
@@ -498,7 +598,15 @@ def main():
                      "kernel": ("fused quantize-on-write + decode attention launch (split-K kernel encoding "
                                 "the step's cells + log-sum-exp combine kernel)" if fused else
                                 "decode attention launch (split-K kernel + log-sum-exp combine kernel)"),
-                     "launch_us": round(dec_avg, 3), "algorithmic_bytes": int(algo)},
+                     "launch_us": round(dec_avg, 3), "algorithmic_bytes": int(algo),
+                     "timing": f"HIP events around {n_batches} batches of {per_batch} back-to-back launches, "
+                               f"one per cache copy"},
+        "launch_us_percentiles": {**pct, "n": n_batches,
+                                  "what": f"per-launch mean of each batch of {per_batch} back-to-back launches"},
+        "warm": None if warm_us is None else {
+            "launch_us": round(warm_us, 3), "GB/s": round(algo / (warm_us * 1e-6) / 1e9, 1),
+            "what": "the same launches on one cache copy (resident in the 256 MB Infinity Cache when it fits)"},
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -174,8 +174,8 @@ typedef struct {
   int32_t max_pages;
 } kvq_pages;
 
-/* Quantize-on-write ([FT398] "What": decode tokens are quantised as they are written;
- * [ST2698] "What it does").  Encodes n_tok bf16 vectors per store and writes each into
+/* Quantize-on-write ([FT398] section What: a decode step stores each new token already
+ * quantised; [ST2698] section What it does).  Encodes n_tok bf16 vectors per store and writes each into
  * the cell of (tok_seq[i], tok_pos[i]) through pages->block_table.  seq_lens is not read
  * or changed: the caller advances it.
  *   k_new, v_new : device bf16 [n_tok][n_kv_heads][head_dim]; either may be NULL to skip
@@ -204,8 +204,9 @@ kvq_status kvq_append(const kvq_cache* cache, const kvq_pages* pages,
  *   workspace: device, >= kvq_decode_workspace_bytes(...) bytes, 256-byte aligned.
  * Requires n_q * (largest number of query heads of one KV head) <= 32, head_dim 64,
  * 128 or 256, and a K store of format INT8_G64 (the V store may be INT8_G64 or
- * Q4_0_H256); or ISO3 K and V stores ([FT398] "Pull request overview": the ISO backend's
- * decode attention over packed cells) with head_dim 128 or 256 and n_q * (largest number
+ * Q4_0_H256); or ISO3 K and V stores ([FT398] section What: the ISO attention backend runs its
+ * own kernels over the packed cells, which its file table lists as the ISO attention source) with
+ * head_dim 128 or 256 and n_q * (largest number
  * of query heads of one KV head) <= 16, or likewise ISO4 K and V stores (norms up to 65504).
  * ISO3 / ISO4 outputs are in the original basis.  A
  * Q4_0_H256 K store needs a Q4_0_H256 V store and the same <= 16 rows ([ST2698] "Not in this
@@ -218,15 +219,16 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages,
                            float sm_scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* A decode step in one launch: quantize-on-write of the step's tokens ([FT398] "What":
- * decode tokens are quantised as they are written) and decode attention over the cache that
+/* A decode step in one launch: quantize-on-write of the step's tokens ([FT398] section What:
+ * a decode step stores each new token already quantised) and decode attention over the cache that
  * includes them ([ST2698] "What it does").  Same result as kvq_append of the n_q new tokens
  * of every sequence into cells seq_lens[b] - n_q .. seq_lens[b] - 1 followed by
  * kvq_decode_attn with the same arguments: the cells are encoded exactly as kvq_append
  * encodes them, written to the cache, and the attention reads them as stored.
  *   k_new, v_new : device bf16 [batch][n_q][n_kv_heads][head_dim], 16-byte aligned; token t
  *                  of sequence b goes to position seq_lens[b] - n_q + t
- *   seq_lens     : already counts the new tokens (seq_lens[b] >= n_q)
+ *   seq_lens     : already counts the new tokens; a sequence with seq_lens[b] < n_q has no cell
+ *                  for its tokens t < n_q - seq_lens[b], which are skipped (never written)
  * Other arguments, workspace and limits as for kvq_decode_attn (same workspace size).
  * Requires INT8_G64 or F32 K and V stores (the single-store modes included), or an INT8_G64
  * K store with a Q4_0_H256 V store at head_dim 256 (k8v4: [ST120] "How"), and 1 <= n_q <= 4.  A page holding new cells must not

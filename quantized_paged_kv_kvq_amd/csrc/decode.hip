@@ -462,16 +462,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   const int p_begin = split * a.pages_per_split;
   const int p0 = p_begin + wv;
   const int p_cap = min(p_begin + a.pages_per_split, a.max_pages) - 1;
-  // Page id of this wave's i-th page (clamped to the split and the table).  The int8 kernel,
-  // which may store new cells, reads the ids of all its pages in one vector load at entry and
-  // takes them with lane reads: once a kernel stores to global memory the compiler can no longer
-  // prove the table unchanged, and scalar loads of it would become vector loads each waited for
-  // with vmcnt(0).  The k8v4 kernel stores nothing and loads each id with a scalar load.
-  int my_ids = 0;
-  if constexpr (VF == 1) my_ids = clampi(bt_row[min(p0 + min(lane, PPW - 1) * NW, p_cap)], 0, a.num_pages - 1);
+  // Page id of this wave's i-th page (clamped to the split and the table).  The kernel may store
+  // the step's new cells, so the compiler cannot prove the table unchanged by those stores: scalar
+  // loads of it would become vector loads, each waited for with vmcnt(0).  Instead lane l reads the
+  // id of the wave's page l in one vector load at entry, and the page loop takes the ids with lane
+  // reads.
+  const int my_ids = clampi(bt_row[min(p0 + min(lane, PPW - 1) * NW, p_cap)], 0, a.num_pages - 1);
   auto page_id = [&](int i) -> int {          // i: index in this wave's page list, uniform
-    if constexpr (VF == 1) return __builtin_amdgcn_readlane(my_ids, i);
-    else return clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1);
+    return __builtin_amdgcn_readlane(my_ids, i);
   };
   // Fused quantize-on-write (int8 K; int8 or, at head_dim 256, Hadamard-rotated q4_0 V): new token t
   // of this sequence goes to position
@@ -487,8 +485,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   for (int t = 0; t < kDecodeMaxFused; ++t) {
     fz_idx[t] = -1;
     fz_slot[t] = 0;
-    if (a.k_new && t < a.n_q) {
-      const int pos = clampi(seq_len - a.n_q + t, 0, cap - 1);
+    // a sequence shorter than the window (an idle slot of length 0, say) has no cell for the
+    // tokens that would sit before position 0: they are skipped, never written elsewhere
+    if (a.k_new && t < a.n_q && seq_len - a.n_q + t >= 0) {
+      const int pos = seq_len - a.n_q + t;                  // <= seq_len - 1 <= cap - 1
       const int pl = pos / KVQ_PAGE_SIZE - p_begin;
       if (pl >= 0 && pl < a.pages_per_split && pl % NW == wv) {
         fz_idx[t] = pl / NW;
@@ -646,17 +646,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   __syncthreads();                                          // q fragments written by wave 0
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;          // pages of this wave, >= 1
-    const int p_last = p0 + (n_mine - 1) * NW;
     // page i of the wave sits in ring slot i % (PD + 1)
     auto run = [&](auto v16_tag) {
       constexpr bool V16 = decltype(v16_tag)::value;
 #pragma unroll
       for (int i = 0; i < PPW; ++i) {
         const int pc = p0 + i * NW;
-        if (i + PD < PPW) {
-          const int page = clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1);
-          load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page, kvh, lane);
-        }
+        if (i + PD < PPW) load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page_id(min(i + PD, n_mine - 1)), kvh, lane);
         page_step<D, RT, VF, DUP, V16>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
         if (i + 1 >= n_mine) break;
       }
@@ -668,7 +664,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
       // page loops.
       static_assert(PPW <= 16, "the scale scan covers 16 pages");
       const int pl = min(lane >> 2, n_mine - 1);
-      const int pid = clampi(bt_row[p0 + pl * NW], 0, a.num_pages - 1);
+      const int pid = __shfl(my_ids, pl);
       const uint4* vsp = reinterpret_cast<const uint4*>(a.v_scales + (((size_t)pid * a.hkv + kvh) * 16 + 4 * (lane & 3)) * NVG);
       u16x2 mn = {0xffff, 0xffff};
 #pragma unroll
@@ -687,12 +683,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
 #pragma unroll
       for (int i = 0; i < PPW; ++i) {
         const int pc = p0 + i * NW;
-        if (i + PD < PPW) {
-          int page;
-          if constexpr (VF == 1) page = page_id(min(i + PD, n_mine - 1));
-          else page = clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1);
-          load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page, kvh, lane);
-        }
+        if (i + PD < PPW) load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page_id(min(i + PD, n_mine - 1)), kvh, lane);
         page_step<D, RT, VF, DUP, false>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
         if (i + 1 >= n_mine) break;
       }

@@ -327,7 +327,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_decode_f32(const DecodeArgs a) {
   if (a.k_new) {
     int fz_mask = 0;
     for (int t = 0; t < a.n_q && t < kDecodeMaxFused; ++t) {
-      const int pos = clampi(seq_len - a.n_q + t, 0, cap - 1);
+      const int pos = seq_len - a.n_q + t;                  // <= seq_len - 1 <= cap - 1
+      if (pos < 0) continue;                                // no cell before position 0: skipped
       const int pl = pos / KVQ_PAGE_SIZE - p_begin;
       if (pl < 0 || pl >= a.pages_per_split || pl % NW != wv) continue;
       const int i = pl / NW, slot = pos % KVQ_PAGE_SIZE;

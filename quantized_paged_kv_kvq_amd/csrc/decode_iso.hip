@@ -1,8 +1,9 @@
 // Split-K decode / verify attention over ISO3 (or ISO4) K and V stores.
 //
-// FreeToken PR #398, "Pull request overview": the ISO backend attends decode tokens over the packed
-// cells with its own kernel ("What": decode tokens are quantised as they are written), checked
-// against attention over the dequantised cells ("Correctness").  "What": an ISO3 cell holds, per 128-value block, the 3-bit codes of the block's
+// FreeToken PR #398, section What: the ISO attention backend runs its own kernels over the packed
+// cells (its file table lists the ISO attention source), and a decode step stores each new token
+// already quantised; section Correctness checks that attention against attention over the
+// dequantised cells.  "What": an ISO3 cell holds, per 128-value block, the 3-bit codes of the block's
 // unit vector after every 4-value group was rotated by one unit quaternion r, and the block's norm
 // n.  A key block is k = n * conj(r) (x) c group by group (c: the level values of its codes), so its
 // score is <q, k> = n * <r (x) q, c>: the query is rotated once per workgroup and the codes enter

@@ -73,8 +73,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = c_int32
-        for name in ("kvq_append", "kvq_decode_attn", "kvq_decode_attn_append", "kvq_extend_attn",
-                     "kvq_dequant_gather"):
+        for name in ("kvq_append", "kvq_decode_attn", "kvq_decode_attn_append",
+                     "kvq_extend_attn", "kvq_dequant_gather"):
             getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -93,6 +93,45 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype, device: torch.device, optional: bool = False):
+    """Raise ValueError / TypeError unless t has this shape, dtype and device (checked before any launch:
+    the kernels trust these sizes, so a mismatch would read or write past a buffer on the device)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _expect_numel(t: Optional[torch.Tensor], name: str, n: int, dtype, device: torch.device, optional: bool = False):
+    """As _expect for index arrays whose element count matters, not their shape."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements, got {t.numel()}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _on_gpu(dev: torch.device):
+    if dev.type != "cuda":
+        raise ValueError(f"the cache slabs must be on a GPU, got {dev} (the kernels take device pointers only)")
+
+
+def _head_map_len(head_map, n_q_heads: int):
+    if head_map is not None and len(head_map) != n_q_heads:
+        raise ValueError(f"head_map must have one entry per query head ({n_q_heads}), got {len(head_map)}")
 
 
 def _stream(stream) -> Optional[int]:
@@ -129,6 +168,10 @@ class PagedKVCache:
         self.v_scales = torch.zeros((num_pages, n_kv_heads, PAGE_SIZE, nsv), dtype=torch.float16, device=device)
         self._desc = None
 
+    @property
+    def device(self) -> torch.device:
+        return self.k_codes.device
+
     def descriptor(self) -> KvqCache:
         if self._desc is None:
             d = KvqCache()
@@ -147,6 +190,11 @@ class Pages:
     def __init__(self, block_table: torch.Tensor, seq_lens: torch.Tensor):
         if block_table.dim() != 2:
             raise ValueError("block_table must be [batch][max_pages]")
+        if seq_lens.numel() != block_table.shape[0]:
+            raise ValueError(f"seq_lens must have one entry per sequence ({block_table.shape[0]}), "
+                             f"got {seq_lens.numel()}")
+        if seq_lens.device != block_table.device:
+            raise ValueError("block_table and seq_lens must be on the same device")
         self.block_table, self.seq_lens = block_table, seq_lens
         d = KvqPages()
         d.block_table = _ptr(block_table, torch.int32, "block_table")
@@ -161,6 +209,10 @@ class Pages:
     @property
     def max_pages(self) -> int:
         return self._desc.max_pages
+
+    @property
+    def device(self) -> torch.device:
+        return self.block_table.device
 
     def descriptor(self) -> KvqPages:
         return self._desc
@@ -177,6 +229,15 @@ def kvq_append(cache: PagedKVCache, pages: Pages, k_new: Optional[torch.Tensor],
                tok_seq: torch.Tensor, tok_pos: torch.Tensor, stream=None) -> None:
     """Quantise bf16 [n_tok][n_kv_heads][head_dim] K and/or V into the cells (tok_seq[i], tok_pos[i])."""
     n_tok = tok_seq.numel()
+    dev = cache.device
+    _expect_numel(tok_seq, "tok_seq", n_tok, torch.int32, dev)
+    _expect_numel(tok_pos, "tok_pos", n_tok, torch.int32, dev)
+    shape = (n_tok, cache.n_kv_heads, cache.head_dim)
+    _expect(k_new, "k_new", shape, torch.bfloat16, dev, optional=True)
+    _expect(v_new, "v_new", shape, torch.bfloat16, dev, optional=True)
+    if pages.device != dev:
+        raise ValueError(f"the page table must be on {dev}, got {pages.device}")
+    _on_gpu(dev)
     _check(lib().kvq_append(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
                             _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
                             _ptr(tok_seq, torch.int32, "tok_seq"), _ptr(tok_pos, torch.int32, "tok_pos"),
@@ -193,11 +254,27 @@ def kvq_decode_workspace_bytes(cache: PagedKVCache, batch: int, max_pages: int, 
     return n
 
 
+def _decode_shapes(cache: PagedKVCache, pages: Pages, q: torch.Tensor, q_lens, head_map, out):
+    """Check the decode tensors against the cache and page-table descriptors; (B, n_q, Hq, D)."""
+    dev = cache.device
+    if q.dim() != 4:
+        raise ValueError(f"q must be [batch][n_q][n_q_heads][head_dim], got shape {tuple(q.shape)}")
+    B, n_q, Hq, D = q.shape
+    _expect(q, "q", (pages.batch, n_q, Hq, cache.head_dim), torch.bfloat16, dev)
+    if pages.device != dev:
+        raise ValueError(f"the page table must be on {dev}, got {pages.device}")
+    _expect_numel(q_lens, "q_lens", B * n_q, torch.int32, dev, optional=True)
+    _expect(out, "out", (B, n_q, Hq, D), torch.float32, dev, optional=True)
+    _head_map_len(head_map, Hq)
+    return B, n_q, Hq, D
+
+
 def kvq_decode_attn(cache: PagedKVCache, pages: Pages, q: torch.Tensor, q_lens: Optional[torch.Tensor] = None,
                     head_map=None, sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Decode / verify attention.  q: bf16 [batch][n_q][n_q_heads][head_dim] -> fp32 of the same shape."""
-    B, n_q, Hq, D = q.shape
+    B, n_q, Hq, D = _decode_shapes(cache, pages, q, q_lens, head_map, out)
+    _on_gpu(cache.device)
     if sm_scale is None:
         sm_scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
     if out is None:
@@ -220,7 +297,10 @@ def kvq_decode_attn_append(cache: PagedKVCache, pages: Pages, k_new: torch.Tenso
                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Decode step in one launch: k/v_new bf16 [batch][n_q][n_kv_heads][head_dim] go to positions
     seq_lens[b] - n_q .. seq_lens[b] - 1, then attention as kvq_decode_attn."""
-    B, n_q, Hq, D = q.shape
+    B, n_q, Hq, D = _decode_shapes(cache, pages, q, q_lens, head_map, out)
+    _expect(k_new, "k_new", (B, n_q, cache.n_kv_heads, D), torch.bfloat16, cache.device)
+    _expect(v_new, "v_new", (B, n_q, cache.n_kv_heads, D), torch.bfloat16, cache.device)
+    _on_gpu(cache.device)
     if sm_scale is None:
         sm_scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
     if out is None:
@@ -250,7 +330,19 @@ def kvq_extend_attn(cache: PagedKVCache, pages: Pages, q: torch.Tensor, k_new: t
                     out: Optional[torch.Tensor] = None, pack_after: bool = True,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Extend (prefill chunk) attention.  q: bf16 [n_new][n_q_heads][D]; k/v_new: bf16 [n_new][n_kv_heads][D]."""
+    dev = cache.device
+    if q.dim() != 3:
+        raise ValueError(f"q must be [n_new][n_q_heads][head_dim], got shape {tuple(q.shape)}")
     N, Hq, D = q.shape
+    _expect(q, "q", (N, Hq, cache.head_dim), torch.bfloat16, dev)
+    _expect(k_new, "k_new", (N, cache.n_kv_heads, cache.head_dim), torch.bfloat16, dev)
+    _expect(v_new, "v_new", (N, cache.n_kv_heads, cache.head_dim), torch.bfloat16, dev)
+    _expect_numel(cu_new, "cu_new", pages.batch + 1, torch.int32, dev)
+    _expect(out, "out", (N, Hq, D), torch.float32, dev, optional=True)
+    if pages.device != dev:
+        raise ValueError(f"the page table must be on {dev}, got {pages.device}")
+    _head_map_len(head_map, Hq)
+    _on_gpu(dev)
     if sm_scale is None:
         sm_scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
     if out is None:
@@ -275,6 +367,10 @@ def kvq_dequant_gather(cache: PagedKVCache, pages: Pages, which: str, seq: int, 
                        stream=None) -> torch.Tensor:
     """Dequantised cells [start, start+count) of sequence `seq`: [count][n_kv_heads][head_dim]."""
     code, tdt = OUT_DTYPE[out_dtype]
+    _expect(out, "out", (count, cache.n_kv_heads, cache.head_dim), tdt, cache.device, optional=True)
+    if pages.device != cache.device:
+        raise ValueError(f"the page table must be on {cache.device}, got {pages.device}")
+    _on_gpu(cache.device)
     if out is None:
         out = torch.empty((count, cache.n_kv_heads, cache.head_dim), dtype=tdt, device=cache.k_codes.device)
     _check(lib().kvq_dequant_gather(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),

@@ -311,3 +311,37 @@ def ragged_extend(prefix_lens, new_lens, seed: int = 21, n_q_heads: int = 8, n_k
     return Workload("ragged_extend", fmt, fmt, len(lens), n_q_heads, n_kv_heads, head_dim, PAGE_SIZE,
                     lens, table, npages, ks, vs, q, n_q=int(new.max()) if len(new) else 0, n_step=0, quat=quat,
                     kind="extend", meta={"new": new})
+
+
+# ---------------------------------------------------------------------------------------------
+# Moving a workload to the device (torch is imported only when these are called)
+
+def dev_bf16(bits):
+    """uint16 bf16 bit patterns -> a torch.bfloat16 tensor on the current GPU."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def dev_i32(a):
+    """An integer array -> a torch.int32 tensor on the current GPU."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
+
+
+def token_lists(w: "Workload", which: str):
+    """(tok_seq, tok_pos, K rows, V rows) of the tokens that pre-fill the cache ('prefix') or of the
+    step's own tokens ('step'), ordered by sequence, then position; None when there are none."""
+    seqs, poss, rows = [], [], []
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        P = L - w.n_step
+        lo, hi = (0, P) if which == "prefix" else (max(P, 0), L)
+        if hi <= lo:
+            continue
+        seqs.append(np.full(hi - lo, b, np.int32))
+        poss.append(np.arange(lo, hi, dtype=np.int32))
+        rows.append((w.k[b][lo:hi], w.v[b][lo:hi]))
+    if not seqs:
+        return None
+    return (np.concatenate(seqs), np.concatenate(poss), np.concatenate([r[0] for r in rows]),
+            np.concatenate([r[1] for r in rows]))

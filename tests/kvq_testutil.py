@@ -10,39 +10,10 @@ import numpy as np
 
 from oracle import attention as oatt
 from oracle import paged as opaged
-from synth import Workload
+from synth import Workload, dev_bf16, dev_i32, token_lists  # noqa: F401  (re-exported for the tests)
 
 ATOL = 1e-3          # max-abs error bound on attention outputs
 MIN_COS = 0.9999     # cosine bound, whole tensor and every row
-
-
-def dev_bf16(bits):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
-
-
-def dev_i32(a):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
-
-
-def token_lists(w: Workload, which: str):
-    """(tok_seq, tok_pos, bf16 rows) of the prefix ('prefix') or of the step's own tokens ('step')."""
-    seqs, poss, rows = [], [], []
-    src = w.k, w.v
-    for b in range(w.batch):
-        L = int(w.seq_lens[b])
-        P = L - w.n_step
-        lo, hi = (0, P) if which == "prefix" else (P, L)
-        if hi <= lo:
-            continue
-        seqs.append(np.full(hi - lo, b, np.int32))
-        poss.append(np.arange(lo, hi, dtype=np.int32))
-        rows.append((src[0][b][lo:hi], src[1][b][lo:hi]))
-    if not seqs:
-        return None
-    return (np.concatenate(seqs), np.concatenate(poss), np.concatenate([r[0] for r in rows]),
-            np.concatenate([r[1] for r in rows]))
 
 
 def gpu_cache(w: Workload):

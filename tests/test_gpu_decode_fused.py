@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import attention as oatt
 from kvq_testutil import (assert_attention_close, assert_slabs_equal, dev_bf16, dev_i32, gpu_append, gpu_cache,
                           oracle_decode, oracle_stores)
 
@@ -87,7 +88,8 @@ def test_fused_kv_head_without_queries_still_appends():
 @pytest.mark.parametrize("lens", [[3, 17, 33, 100], [18, 16, 1000, 64]])
 def test_fused_verify_window_across_page_edges(lens):
     """Three new tokens per sequence, some windows straddling a page boundary; 24 rows per KV head
-    make three row-group workgroups per split (all patch, one stores)."""
+    make three row-group workgroups per split, each of which encodes and stores the window's cells
+    of its split (identical bytes) before reading them back."""
     w = synth.ragged_decode("int8", "int8", lens, seed=54 + lens[0], n_q=3, q_len_back=[2, 1, 0], n_q_heads=16,
                             n_kv_heads=2, head_dim=256)
     check_fused(w)
@@ -134,41 +136,95 @@ def test_fused_graph_replays():
     assert_attention_close(eager.cpu().numpy(), oracle_decode(w, sk, sv))
 
 
+@pytest.mark.parametrize("fk,fv,D,n_q", [("int8", "int8", 256, 1), ("int8", "int8", 256, 3), ("int8", "q4h", 256, 3),
+                                         ("int8", "f32", 128, 3)])
+def test_fused_short_sequences_skip_missing_positions(fk, fv, D, n_q):
+    """A sequence shorter than the step's window (an idle slot of length 0, or 2 cells under a 3-token
+    window) has no cell for the window's first tokens: they are skipped, never written elsewhere.  A
+    zero-length sequence's page-table row reads page 0, which holds another sequence's cells: every
+    cell of the cache must stay exactly as the oracle encodes the sequences' real tokens, and the
+    short sequence's cells hold its own last tokens."""
+    import torch
+    import quantized_paged_kv_kvq_amd as kvq
+    lens = [0, 300, 2, 17] if n_q == 3 else [0, 300, 17]
+    back = list(range(n_q - 1, -1, -1)) if n_q > 1 else None
+    w = synth.ragged_decode(fk, fv, lens, seed=70 + n_q + D, n_q=n_q, n_q_heads=16, n_kv_heads=2, head_dim=D,
+                            q_len_back=back)
+    assert int(w.block_table[0, 0]) == 0, "the zero-length row points at page 0"
+    rng = np.random.default_rng(71)
+    junk = synth.normal_bf16(rng, (w.n_kv_heads, D))          # tokens with no cell: must go nowhere
+    kn = np.stack([np.stack([w.k[b][L - n_q + t] if L - n_q + t >= 0 else junk for t in range(n_q)])
+                   for b, L in enumerate(lens)])
+    vn = np.stack([np.stack([w.v[b][L - n_q + t] if L - n_q + t >= 0 else junk for t in range(n_q)])
+                   for b, L in enumerate(lens)])
+    cache, pages = gpu_cache(w)
+    seq = np.concatenate([np.full(max(L - n_q, 0), b, np.int32) for b, L in enumerate(lens)])
+    pos = np.concatenate([np.arange(max(L - n_q, 0), dtype=np.int32) for L in lens])
+    kp = np.concatenate([w.k[b][:max(L - n_q, 0)] for b, L in enumerate(lens)])
+    vp = np.concatenate([w.v[b][:max(L - n_q, 0)] for b, L in enumerate(lens)])
+    kvq.kvq_append(cache, pages, dev_bf16(kp), dev_bf16(vp), dev_i32(seq), dev_i32(pos))
+    q_lens = dev_i32(w.q_lens) if w.q_lens is not None else None
+    out = kvq.kvq_decode_attn_append(cache, pages, dev_bf16(kn), dev_bf16(vn), dev_bf16(w.q), q_lens=q_lens,
+                                     sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    sk, sv = oracle_stores(w)                                 # every real token of every sequence, nothing else
+    assert_slabs_equal(cache, sk, sv)
+    got = out.cpu().numpy()
+    assert_attention_close(got, oracle_decode(w, sk, sv))
+    assert not got[0].any(), "the zero-length sequence's rows are zeros"
+
+
 def test_fused_moe_full_size_131072():
     """The benchmark's workload and launch configuration at full size."""
     m = check_fused(synth.moe_int8_decode(ctx=131072))
     print(f"[fused 131072] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
 
 
-def test_fused_batched_full_size_sampled_sequences():
+def test_fused_moe_full_size_65536():
+    """The MoE layer at 65,536 tokens (the 64K column of strata PR #2698, Measurements): a launch plan
+    with 32-page splits, at full size in the fused launch configuration."""
+    m = check_fused(synth.moe_int8_decode(ctx=65536))
+    print(f"[fused 65536] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
+
+
+def test_fused_batched_full_size_all_sequences():
     """The 32-sequence batched workload (4,096-32,768 tokens each, 32 / 8 heads, head_dim 128) at full
-    size in the benchmark's launch configuration (fused quantize-on-write + decode).  The oracle encodes
-    and attends a sample of sequences (shortest, longest, first, last); their step cells are compared
-    byte for byte and their outputs to the tolerance; the fused output equals append + decode bit for
-    bit over the whole batch."""
+    size in the benchmark's launch configuration (fused quantize-on-write + decode).  The oracle runs
+    one sequence at a time (its own pages only, so host memory stays bounded): every cell of every
+    sequence -- the prefix written by kvq_append and the step's cell written by the decode launch -- is
+    compared byte for byte in both stores (codes and scales), and every output row to the tolerance;
+    the fused output equals append + decode bit for bit over the whole batch."""
     from oracle import paged as opaged
+    from kvq_testutil import tile_index
     w = synth.batched_int8_decode()
     lens = np.asarray(w.seq_lens)
-    seqs = sorted({0, w.batch - 1, int(np.argmin(lens)), int(np.argmax(lens))})
-    print(f"[fused batched] sampled sequences {seqs} of {w.batch}, lengths {[int(lens[b]) for b in seqs]}", flush=True)
+    print(f"[fused batched] {w.batch} sequences, {int(lens.sum())} cells", flush=True)
     cache, got = run_fused(w)
-    sk = opaged.Store.empty(w.fmt_k, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
-    sv = opaged.Store.empty(w.fmt_v, w.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
-    for b in seqs:
+    slabs = {x: (getattr(cache, f"{x}_codes").cpu().numpy(), getattr(cache, f"{x}_scales").cpu().numpy())
+             for x in ("k", "v")}
+    idx = {"k": tile_index("k_chunk", w.head_dim), "v": tile_index("v_quad", w.head_dim)}
+    worst = [0.0, 1.0, 1.0]
+    for b in range(w.batch):
         L = int(lens[b])
-        opaged.append(sk, w.block_table, np.full(L, b), np.arange(L), w.k[b], w.page_size)
-        opaged.append(sv, w.block_table, np.full(L, b), np.arange(L), w.v[b], w.page_size)
-    ref = oracle_decode(w, sk, sv, seqs=seqs)
-    assert_attention_close(got[seqs], ref[seqs])
-    kc, ks = (cache.k_codes.cpu().numpy(), cache.k_scales.cpu().numpy())
-    for b in seqs:                                   # the step's cell (last position) of each sampled sequence
-        pos = int(lens[b]) - 1
-        page, slot = int(w.block_table[b, pos // 16]), pos % 16
-        from kvq_testutil import tile_index
-        idx = tile_index("k_chunk", w.head_dim)[slot]
-        assert np.array_equal(kc[page][:, idx], sk.codes[page, :, slot, :]), f"K cell of sequence {b}"
-        assert np.array_equal(ks[page][:, slot].view(np.uint16), sk.scales[page, :, slot].view(np.uint16))
+        need = (L + w.page_size - 1) // w.page_size
+        bt = np.arange(need, dtype=np.int32)[None, :]             # the sequence's pages, renumbered
+        st = {x: opaged.Store.empty(getattr(w, f"fmt_{x}"), need, w.n_kv_heads, w.page_size, w.head_dim)
+              for x in ("k", "v")}
+        opaged.append(st["k"], bt, np.zeros(L, int), np.arange(L), w.k[b], w.page_size)
+        opaged.append(st["v"], bt, np.zeros(L, int), np.arange(L), w.v[b], w.page_size)
+        pages = w.block_table[b, :need]
+        for x in ("k", "v"):
+            codes = slabs[x][0][pages][:, :, idx[x]]                  # [need][hkv][slot][code byte]
+            assert np.array_equal(codes, st[x].codes), f"{x} codes of sequence {b} (length {L})"
+            assert np.array_equal(slabs[x][1][pages].view(np.uint16), st[x].scales.view(np.uint16)), \
+                f"{x} scales of sequence {b}"
+        ref = oatt.decode(st["k"], st["v"], bt, np.array([L], np.int32), w.q[b:b + 1], w.page_size, w.sm_scale)
+        m = assert_attention_close(got[b:b + 1], ref)
+        worst = [max(worst[0], m[0]), min(worst[1], m[1]), min(worst[2], m[2])]
+    print(f"[fused batched] all {w.batch} sequences: max-abs {worst[0]:.2e} min cosine {worst[1]:.8f} "
+          f"min row cosine {worst[2]:.8f}")
     assert np.array_equal(got.view(np.uint32), run_unfused(w).view(np.uint32)), "fused and unfused outputs differ"
+
 
 @pytest.mark.parametrize("lens", [[33, 2500], [16, 17, 1000]])
 def test_fused_k8v4_single_query(lens):

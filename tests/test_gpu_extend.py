@@ -144,11 +144,19 @@ def test_extend_deterministic():
 
 @pytest.mark.parametrize("fmt", ["iso3", "int8"])
 def test_extend_full_size_sampled(fmt):
-    """30,000-cell ISO3 (int8) prefix + 2,048 new tokens, 32 / 8 heads: every output element of sampled
-    query tokens (first, tile edges, middle, last) against the oracle."""
+    """30,000-cell ISO3 (int8) prefix + 2,048 new tokens, 32 / 8 heads, in the benchmark's launch
+    configuration: every output element of every 64th query token and of the tile edges, middle and
+    last tokens against the oracle; then the slabs after the deferred packing (FreeToken PR #398,
+    What: the chunk's tokens are packed after its attention) byte for byte against the oracle's
+    encoding of all 32,048 tokens."""
     w = synth.iso3_extend(fmt=fmt)
-    rows = np.array([0, 1, 31, 32, 63, 64, 127, 128, 1000, 1500, 2046, 2047])
+    rows = np.unique(np.concatenate([np.arange(0, 2048, 64), [1, 31, 32, 63, 127, 128, 1000, 1500, 2046, 2047]]))
+    print(f"[extend full size] {fmt}: {len(rows)} sampled query tokens", flush=True)
     cache, got = run_extend(w)
     ref = oracle_extend(w, rows=rows)
-    assert_attention_close(got[rows], ref[rows])
+    m = assert_attention_close(got[rows], ref[rows])
     assert np.isfinite(got).all()
+    sk, sv = oracle_stores(w)                   # every token packed: prefix + chunk
+    assert_slabs_equal(cache, sk, sv)
+    print(f"[extend full size] {fmt}: max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}; "
+          f"slabs equal after packing")

@@ -242,6 +242,13 @@ def test_decode_moe_full_size_131072():
     print(f"[131072] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
 
 
+def test_decode_moe_full_size_65536():
+    """The MoE layer at 65,536 tokens (the 64K column of strata PR #2698, Measurements), whose launch
+    plan takes 32-page splits, at full size."""
+    m = check_decode(synth.moe_int8_decode(ctx=65536))
+    print(f"[65536] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
+
+
 def test_verify_k8v4_full_size():
     m = check_decode(synth.k8v4_verify())
     print(f"[k8v4 118750] max-abs {m[0]:.2e} cosine {m[1]:.8f} min row cosine {m[2]:.8f}")
