@@ -17,7 +17,9 @@
  * Conventions shared by every entry point
  *   - Ownership: the caller owns every buffer (cache slabs, page tables, lengths,
  *     q/k/v, outputs, workspaces).  The library allocates nothing and keeps no
- *     per-call state; it only caches per-device properties.
+ *     per-call state; it only caches per-device properties.  The one exception is
+ *     kvq_decode_attn_noalloc's scratch, a fixed device array of the library's own
+ *     (see there).
  *   - Pointers marked "device" are HIP device pointers; "host" pointers are read
  *     during the call only.  Nothing is retained after a call returns.
  *   - Execution: every call enqueues its kernels on `stream` (a hipStream_t; NULL =
@@ -240,6 +242,23 @@ kvq_status kvq_decode_attn_append(const kvq_cache* cache, const kvq_pages* pages
                                   const int32_t* q_lens, const int32_t* head_map,
                                   float sm_scale, float* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* kvq_decode_attn for callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops that forbid allocation, harnesses that cannot call hipMalloc.  It takes no workspace:
+ * the split partials go to a scratch array the library keeps in device memory, one copy of
+ * KVQ_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU it runs on, held from module load until the process
+ * ends.  The call itself allocates nothing (the first call on a device looks up that device's
+ * address of the array once).  Arguments, results and limits are those of kvq_decode_attn; a call
+ * whose partials would exceed the scratch (kvq_decode_workspace_bytes(...) > KVQ_NOALLOC_SCRATCH_BYTES)
+ * returns KVQ_ERR_WORKSPACE and enqueues nothing.  Every call on one GPU shares that GPU's scratch,
+ * which keeps the last call's partials (nothing in it needs clearing between calls): calls that
+ * overlap in time on one GPU (different streams, or host threads without ordering between them)
+ * race and give wrong results.  Calls on one stream are ordered and safe. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* cache, const kvq_pages* pages,
+                                   const void* q, int32_t n_q, int32_t n_q_heads,
+                                   const int32_t* q_lens, const int32_t* head_map,
+                                   float sm_scale, float* out, void* stream);
 
 /* Workspace bytes kvq_decode_attn needs for this geometry (0 on invalid arguments). */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t max_pages,

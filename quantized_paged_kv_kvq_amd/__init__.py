@@ -6,5 +6,5 @@ The hot path is libkvq.so (hand-written HIP for gfx950, C ABI in include/kvq.h);
 call does, and raises if it has not been built.
 """
 from .kvq import (FMT, PAGE_SIZE, KVQError, PagedKVCache, Pages, cell_bytes, kvq_append,  # noqa: F401
-                  kvq_decode_attn, kvq_decode_attn_append, kvq_decode_workspace_bytes, kvq_dequant_gather,
+                  kvq_decode_attn, kvq_decode_attn_append, kvq_decode_attn_noalloc, kvq_decode_workspace_bytes, kvq_dequant_gather,
                   kvq_extend_attn, kvq_extend_workspace_bytes, lib)

@@ -111,6 +111,37 @@ kvq_status build_head_lists(int hq, int hkv, const int32_t* head_map, int16_t* o
 
 }  // namespace
 
+namespace {
+// Scratch of kvq_decode_attn_noalloc: the split partials of one call, in device memory the library
+// holds from module load until the process ends (one copy per GPU, at that GPU's own address).  Host
+// code never passes the array's name to a kernel (on the host it is only a stand-in for the symbol):
+// it takes each device's address once with hipGetSymbolAddress and uses that.
+__device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// This device's address of the scratch array, looked up on the first call on each device (with that
+// device current), then cached.
+kvq_status noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVQ_ERR_HIP, "hipGetSymbolAddress of the decode scratch: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
 int device_cu_count() {
   static std::mutex mu;
   static std::vector<int> counts;
@@ -272,14 +303,14 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
   return plan.part_bytes;
 }
 
-static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, const void* k_new, const void* v_new,
-                              const void* q, int32_t n_q, int32_t n_q_heads, const int32_t* q_lens,
-                              const int32_t* head_map, float sm_scale, float* out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+// Validates every decode argument but the workspace and fills the kernel arguments and the launch plan
+// (plan.part_bytes: the split partials the workspace must hold).
+static kvq_status decode_prepare(const kvq_cache* cache, const kvq_pages* pages, const void* k_new,
+                                 const void* v_new, const void* q, int32_t n_q, int32_t n_q_heads,
+                                 const int32_t* q_lens, const int32_t* head_map, float sm_scale, float* out,
+                                 DecodeArgs& a, DecodePlan& plan) {
   kvq_status st;
   if ((st = check_pages(pages)) != KVQ_OK) return st;
-  DecodeArgs a;
-  DecodePlan plan;
   if ((st = decode_setup(cache, pages->batch, pages->max_pages, n_q, n_q_heads, head_map, &a, &plan)) != KVQ_OK)
     return st;
   if ((st = check_store(cache, cache->k, false)) != KVQ_OK) return st;
@@ -287,10 +318,6 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   if (!q || !out) return fail(KVQ_ERR_NULL, "q or out is NULL");
   if (((uintptr_t)q & 15) || ((uintptr_t)out & 15)) return fail(KVQ_ERR_SHAPE, "q and out must be 16-byte aligned");
   if (!(sm_scale == sm_scale)) return fail(KVQ_ERR_SHAPE, "sm_scale is NaN");
-  if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.part_bytes);
-  if ((uintptr_t)workspace & 255) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (workspace_bytes < plan.part_bytes)
-    return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, decode needs %zu", workspace_bytes, plan.part_bytes);
   a.k_codes = static_cast<const uint8_t*>(cache->k.codes);
   a.k_scales = static_cast<const uint16_t*>(cache->k.scales);
   a.v_codes = static_cast<const uint8_t*>(cache->v.codes);
@@ -301,7 +328,7 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   a.q_lens = q_lens;
   a.seq_lens = pages->seq_lens;
   a.bt = pages->block_table;
-  a.part = static_cast<float*>(workspace);
+  a.part = nullptr;
   a.out = out;
   a.hkv = cache->n_kv_heads;
   a.num_pages = cache->num_pages;
@@ -319,6 +346,13 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   a.g_uniform = n_q_heads % cache->n_kv_heads == 0 ? n_q_heads / cache->n_kv_heads : 0;
   for (int h = 0; h < n_q_heads && a.g_uniform; ++h)
     if (a.head_list[h] != h || (h % a.g_uniform == 0 && a.head_off[h / a.g_uniform] != h)) a.g_uniform = 0;
+  return KVQ_OK;
+}
+
+// Launches the decode kernels of a prepared call with its split partials at `part`.
+static kvq_status decode_launch(const kvq_cache* cache, const DecodePlan& plan, DecodeArgs& a, void* part,
+                                void* stream) {
+  a.part = static_cast<float*>(part);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (cache->k.fmt == KVQ_FMT_ISO3 || cache->k.fmt == KVQ_FMT_ISO4)
     return hip_status(launch_decode_iso(cache->k.fmt == KVQ_FMT_ISO4 ? 4 : 3, cache->head_dim, plan, a, hs),
@@ -331,11 +365,45 @@ static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, co
   return hip_status(launch_decode(cache->v.fmt, cache->head_dim, plan, a, hs), "decode launch");
 }
 
+static kvq_status decode_impl(const kvq_cache* cache, const kvq_pages* pages, const void* k_new, const void* v_new,
+                              const void* q, int32_t n_q, int32_t n_q_heads, const int32_t* q_lens,
+                              const int32_t* head_map, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  DecodeArgs a;
+  DecodePlan plan;
+  kvq_status st = decode_prepare(cache, pages, k_new, v_new, q, n_q, n_q_heads, q_lens, head_map, sm_scale, out, a,
+                                 plan);
+  if (st != KVQ_OK) return st;
+  if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.part_bytes);
+  if ((uintptr_t)workspace & 255) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.part_bytes)
+    return fail(KVQ_ERR_WORKSPACE, "workspace has %zu bytes, decode needs %zu", workspace_bytes, plan.part_bytes);
+  return decode_launch(cache, plan, a, workspace, stream);
+}
+
 kvq_status kvq_decode_attn(const kvq_cache* cache, const kvq_pages* pages, const void* q, int32_t n_q,
                            int32_t n_q_heads, const int32_t* q_lens, const int32_t* head_map, float sm_scale,
                            float* out, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(cache, pages, nullptr, nullptr, q, n_q, n_q_heads, q_lens, head_map, sm_scale, out, workspace,
                      workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* cache, const kvq_pages* pages, const void* q, int32_t n_q,
+                                   int32_t n_q_heads, const int32_t* q_lens, const int32_t* head_map,
+                                   float sm_scale, float* out, void* stream) {
+  DecodeArgs a;
+  DecodePlan plan;
+  kvq_status st = decode_prepare(cache, pages, nullptr, nullptr, q, n_q, n_q_heads, q_lens, head_map, sm_scale, out,
+                                 a, plan);
+  if (st != KVQ_OK) return st;
+  if (plan.part_bytes > (size_t)KVQ_NOALLOC_SCRATCH_BYTES)
+    return fail(KVQ_ERR_WORKSPACE,
+                "kvq_decode_attn_noalloc: this call's split partials need %zu bytes, more than the library's "
+                "%zu-byte scratch (use kvq_decode_attn with a workspace)",
+                plan.part_bytes, (size_t)KVQ_NOALLOC_SCRATCH_BYTES);
+  void* part = nullptr;
+  if ((st = noalloc_scratch(&part)) != KVQ_OK) return st;
+  return decode_launch(cache, plan, a, part, stream);
 }
 
 kvq_status kvq_decode_attn_append(const kvq_cache* cache, const kvq_pages* pages, const void* k_new,

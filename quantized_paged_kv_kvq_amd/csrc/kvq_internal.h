@@ -183,5 +183,7 @@ hipError_t launch_extend(const ExtendArgs& a, int tiles_per_seq, hipStream_t s);
 
 int device_cu_count();
 int decode_max_splits();
+// this device's address of kvq_decode_attn_noalloc's scratch array (looked up once per device)
+kvq_status noalloc_scratch(void** ptr);
 
 }  // namespace kvq

@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
                                       c_void_p, c_size_t, c_void_p]
         L.kvq_decode_attn_append.argtypes = [cp, ip, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                              c_void_p, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.kvq_decode_attn_noalloc.argtypes = [cp, ip, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_float,
+                                              c_void_p, c_void_p]
         L.kvq_decode_workspace_bytes.argtypes = [cp, c_int32, c_int32, c_int32, c_int32, c_void_p]
         L.kvq_decode_workspace_bytes.restype = c_size_t
         L.kvq_extend_attn.argtypes = [cp, ip, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
@@ -73,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = c_int32
-        for name in ("kvq_append", "kvq_decode_attn", "kvq_decode_attn_append",
+        for name in ("kvq_append", "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_noalloc",
                      "kvq_extend_attn", "kvq_dequant_gather"):
             getattr(L, name).restype = c_int32
         _lib = L
@@ -287,6 +289,25 @@ def kvq_decode_attn(cache: PagedKVCache, pages: Pages, q: torch.Tensor, q_lens: 
                                  _ptr(q, torch.bfloat16, "q"), n_q, Hq, _ptr(q_lens, torch.int32, "q_lens"), hm,
                                  float(sm_scale), _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    del keep
+    return out
+
+
+def kvq_decode_attn_noalloc(cache: PagedKVCache, pages: Pages, q: torch.Tensor, q_lens: Optional[torch.Tensor] = None,
+                            head_map=None, sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """kvq_decode_attn without a workspace: the split partials go to the library's own per-GPU scratch
+    (calls that overlap in time on one GPU race).  `out` must be passed by callers that cannot allocate."""
+    B, n_q, Hq, D = _decode_shapes(cache, pages, q, q_lens, head_map, out)
+    _on_gpu(cache.device)
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=torch.float32, device=q.device)
+    keep, hm = _head_map_arg(head_map)
+    _check(lib().kvq_decode_attn_noalloc(ctypes.byref(cache.descriptor()), ctypes.byref(pages.descriptor()),
+                                         _ptr(q, torch.bfloat16, "q"), n_q, Hq, _ptr(q_lens, torch.int32, "q_lens"),
+                                         hm, float(sm_scale), _ptr(out, torch.float32, "out"), _stream(stream)))
     del keep
     return out
 

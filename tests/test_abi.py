@@ -236,3 +236,27 @@ def test_extend_validation_errors():
     assert L.kvq_extend_workspace_bytes(ctypes.byref(make_cache()), 1, 64, 64, 64, 16) == 0
     i8 = make_cache(D=128)
     assert L.kvq_extend_workspace_bytes(ctypes.byref(i8), 1, 64, 64, 64, 16) == 2 * (16 + 1) * 36864
+
+
+def decode_noalloc(c, p, n_q=1, hq=16, q=FAKE, out=FAKE):
+    L = kvq.lib()
+    return L.kvq_decode_attn_noalloc(ctypes.byref(c) if c else None, ctypes.byref(p) if p else None, q, n_q, hq,
+                                     None, None, 0.0625, out, None)
+
+
+def test_decode_noalloc_validation_and_scratch_limit():
+    """kvq_decode_attn_noalloc validates like kvq_decode_attn, and refuses (on the host, before any HIP
+    call) a call whose split partials exceed its fixed scratch, whose size the header states."""
+    L = kvq.lib()
+    m = re.search(r"#define KVQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == 16 << 20
+    assert decode_noalloc(None, make_pages()) == 1
+    assert decode_noalloc(make_cache(), make_pages(), n_q=5) == 3
+    assert decode_noalloc(make_cache(), make_pages(), q=None) == 1
+    c = make_cache(hkv=8, D=128)
+    big = make_pages(batch=64, max_pages=4096)
+    need = L.kvq_decode_workspace_bytes(ctypes.byref(c), 64, 4096, 1, 32, None)
+    assert need > limit
+    assert decode_noalloc(c, big, hq=32) == 4
+    assert "scratch" in L.kvq_last_error().decode()
