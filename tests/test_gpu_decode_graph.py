@@ -128,3 +128,58 @@ def test_extend_graph_replays(fmt):
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager.cpu().numpy()), f"replay {i} differs from the eager run"
         del junk
+
+
+def _prepared(w):
+    """A filled cache, its pages and the device query of a decode workload."""
+    cache, pages = gpu_cache(w)
+    gpu_append(w, cache, pages, "prefix")
+    gpu_append(w, cache, pages, "step")
+    q_lens = dev_i32(w.q_lens) if w.q_lens is not None else None
+    return cache, pages, dev_bf16(w.q), q_lens
+
+
+def test_decode_workspace_reused_across_different_inputs():
+    """One workspace for consecutive launches over different caches and queries (single-sequence
+    decode and verify shapes, and a batch): the combine must read the partials of its own launch.
+    Launches with the same inputs write the same partials, so only alternating inputs can show a
+    stale read: every launch, eager and inside one replayed graph, must equal its own
+    fresh-workspace result bit for bit."""
+    import torch
+    import quantized_paged_kv_kvq_amd as kvq
+    ws_ = [synth.moe_int8_decode(ctx=20000, seed=91), synth.k8v4_verify(ctx=9000, seed=92),
+           synth.moe_int8_decode(ctx=20000, seed=93),
+           synth.ragged_decode("int8", "int8", [3000, 700, 5000], seed=94, n_q_heads=16, n_kv_heads=2, head_dim=256),
+           synth.k8v4_verify(ctx=100000, seed=95)]
+    prep = [_prepared(w) for w in ws_]
+    refs = [kvq.kvq_decode_attn(c, p, q, q_lens=ql, sm_scale=w.sm_scale) for w, (c, p, q, ql) in zip(ws_, prep)]
+    torch.cuda.synchronize()
+    for w, r, (c, p, q, ql) in list(zip(ws_, refs, prep))[:4]:    # and the fresh results are right
+        sk, sv = oracle_stores(w)
+        assert_attention_close(r.cpu().numpy(), oracle_decode(w, sk, sv))
+    nbytes = max(kvq.kvq_decode_workspace_bytes(c, p.batch, p.max_pages, w.n_q, w.n_q_heads)
+                 for w, (c, p, q, ql) in zip(ws_, prep))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(r) for r in refs]
+    order = [0, 1, 4, 2, 3, 0, 4, 2, 1, 0, 3, 4, 2]
+
+    def run_all():
+        for i in order:
+            w, (c, p, q, ql) = ws_[i], prep[i]
+            kvq.kvq_decode_attn(c, p, q, q_lens=ql, sm_scale=w.sm_scale, out=outs[i], workspace=ws)
+
+    for i in order:                                               # eager, checked after each launch
+        w, (c, p, q, ql) = ws_[i], prep[i]
+        kvq.kvq_decode_attn(c, p, q, q_lens=ql, sm_scale=w.sm_scale, out=outs[i], workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[i], refs[i]), f"eager launch of workload {i}"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, refs)):
+            assert torch.equal(o, r), f"replay {rep}, workload {i}"
