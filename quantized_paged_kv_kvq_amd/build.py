@@ -24,13 +24,14 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
 # translation unit -> extra flags.  The decode kernels need their page loops fully unrolled (a rolled
-# loop waits for every outstanding load); the k8v4 row-tile and q4_0-K kernels keep their MFMA
+# loop waits for every outstanding load); the k8v4 verify and q4_0-K kernels keep their MFMA
 # accumulators in VGPRs (the default placed them in AGPRs and copied them around every MFMA).
 UNITS = {
     "kvq_api.hip": [],
     "append.hip": ["-ffp-contract=off"],
     "gather.hip": ["-ffp-contract=off"],
     "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "decode_verify.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode_iso.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
     "decode_q4.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode_f32.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],

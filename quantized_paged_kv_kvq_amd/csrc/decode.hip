@@ -7,8 +7,9 @@
 // own causal lengths (per-query step arrays).
 //
 // Work decomposition (one workgroup = one (sequence, KV head, split) triple):
-//   * The query rows of a KV head are its (query token, query head) pairs: n_q * G <= 32 rows,
-//     laid out as 16-wide MFMA column tiles (RT = 1 or 2).
+//   * The query rows of a KV head are its (query token, query head) pairs: n_q * G <= 32 rows, in
+//     groups of 8 (one workgroup each; MFMA columns 8..15 repeat the group's rows, see DUP below).
+//     k8v4 with more than 8 rows per KV head runs in the wave-pair verify kernel (decode_verify.hip).
 //   * Each wave streams every NW-th page of the split: K codes token-major (16 B per lane per
 //     64-group: the lane's token is lane % 16), V codes d-major (4 tokens of one head_dim
 //     position per 32-bit load), both with 256-byte-coalesced wave accesses.
@@ -26,10 +27,9 @@
 //     the per-group sums of the weights.  Every MFMA tile of 16 head_dim rows lies inside one
 //     scale group, so one weight vector per group serves all its tiles.
 //   * The NW waves of a workgroup merge (m, l, O) through LDS in one round (each wave merges and
-//     writes a share of the head_dim tiles); the workgroup writes one unnormalised partial.  A second kernel merges the splits with a log-sum-exp combine,
-//     normalises, applies H to k8v4 outputs and writes fp32 rows.
-#include <type_traits>
-
+//     writes a share of the head_dim tiles; k8v4 rotates the merged partial back by H); the
+//     workgroup writes one unnormalised partial.  A second kernel merges the splits with a
+//     log-sum-exp combine, normalises and writes fp32 rows.
 #include "kvq_internal.h"
 #include "device_util.h"
 #include "int8_cell.h"
@@ -41,8 +41,8 @@ namespace {
 
 // Launch shapes: waves per workgroup, pages per wave per split (a split is NW * PPW pages), pages
 // each wave keeps in flight ahead of the one it processes, and waves per SIMD the registers allow.
-// The last shape serves only the k8v4 row-tile kernel (one wave per SIMD), whose long page step
-// hides the load of the next page without a second one in flight.
+// The last shape plans the k8v4 verify kernel's 64-page splits (decode_verify.hip: 4 wave pairs of
+// 16 pages each); with 32-page splits it takes shape 1 (4 pairs of 8 pages).
 struct Shape { int nw, ppw, pd, occ; };
 constexpr Shape kShapes[] = {{4, 16, 2, 2}, {4, 8, 1, 2}, {8, 8, 1, 2}, {4, 16, 1, 2}};
 constexpr int kRowTileShape = 3;
@@ -199,8 +199,9 @@ constexpr float kLazyLog2 = 8.0f;     // weights stay below 2^8 between rescalin
 
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
 // DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the bf16 hi part of
-// the softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both.
-template <int D, int RT, int VF, bool DUP, bool V16, class QF>
+// the softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both.  (k8v4 with
+// more than 8 rows per KV head runs in the wave-pair verify kernel.)
+template <int D, int RT, int VF, bool DUP, class QF>
 __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j4, bool lo_col, const int (&Lrow)[RT],
                                           const QF& qf, const float (&qmul)[RT],
                                           float (&m_run)[RT], float (&l_run)[RT],
@@ -208,19 +209,7 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
   constexpr int NG = D / 64;
   constexpr int NVG = VF == 1 ? D / 64 : D / 32;
   constexpr int NT = D / 16;
-  // k8v4 with more than 8 rows (verify windows; 16 rows per row tile, no duplicated columns):
-  // V enters the MFMA as a two-part product built once per page for all row tiles, and the softmax
-  // weights are split into hi / lo once per row tile instead of once per 32-value scale group; three
-  // K = 16 MFMAs take V hi x w hi, V lo x w hi and V hi x w lo (V lo x w lo is below 2^-16 of the
-  // term).  When every V scale of the wave's pages is 0 or at least 2^-10 (V16), the product is
-  // (code - 8) x scale / 16 in fp16 (hi = the rounded product, lo = its exact rounding error from one
-  // fma, exact since its last bit is at least 2^-24; the 1/16 keeps it below 2^15) from packed fp16
-  // arithmetic, against fp16 parts of 16 x the weights (a weight's parts miss it by at most 2^-29,
-  // with the largest weight at least 1); otherwise (code - 8) x scale in bf16 parts (a 4-bit code
-  // times an fp16 scale has at most 15 significant bits: 8 in hi, 7 in lo) against bf16 parts of the
-  // weights.
-  constexpr bool Q4A = VF == 2 && !DUP;
-  float pkr[RT][4];
+  static_assert(DUP, "rows beyond 8 per KV head take one workgroup per group of 8 rows");
 
   // ---- QK: S^T[token 4*j4 + k][row] per 64-group
   f32x4 acc[RT][NG];
@@ -266,15 +255,8 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
     if (__any(rescale)) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) O[rt][t] *= alpha;
-      if constexpr (!Q4A) {
 #pragma unroll
-        for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
-      }
-    }
-    if constexpr (Q4A) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pkr[rt][k] = pk[k];
-      continue;
+      for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
     }
 
     // ---- PV per V scale group
@@ -324,84 +306,6 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
         O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, O[rt][2 * g], 0, 0, 0);
         O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bhi, O[rt][2 * g + 1], 0, 0, 0);
         O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, O[rt][2 * g + 1], 0, 0, 0);
-      }
-    }
-  }
-  if constexpr (Q4A) {
-    if constexpr (V16) {
-      f16x4 wh[RT], wl[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float x = 16.0f * pkr[rt][k];
-          wh[rt][k] = (_Float16)x;
-          wl[rt][k] = (_Float16)(x - (float)wh[rt][k]);
-        }
-      const f16x2 mul = {(_Float16)0.0625f, (_Float16)0.0625f}, add = {(_Float16)-64.5f, (_Float16)-64.5f};
-#pragma unroll
-      for (int g = 0; g < NVG; ++g) {
-        // byte k of the word: token 4*j4 + k; its low / high nibble: head_dim 32g + 2*i16 (+1)
-        const uint32_t w = word_of(pb.v[g >> 2], g & 3);
-        // (scale of token 4*j4, of token 4*j4 + 1) and tokens + 2, + 3: half k * NVG + g of vs
-        const uint32_t hsel = (g & 1) ? 0x07060302u : 0x05040100u;
-        const f16x2 d01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(pb.vs[4 + (g >> 1)], pb.vs[g >> 1], hsel));
-        const f16x2 d23 =
-            __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(pb.vs[12 + (g >> 1)], pb.vs[8 + (g >> 1)], hsel));
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
-          // [code, 0x64] per token pair reads 1024 + code; one packed fma gives (code - 8) / 16 exactly
-          const f16x2 c01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, nib, 0x04010400u)) * mul + add;
-          const f16x2 c23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, nib, 0x04030402u)) * mul + add;
-          const f16x2 h01 = c01 * d01, h23 = c23 * d23;
-          const f16x2 l01 = __builtin_elementwise_fma(c01, d01, -h01), l23 = __builtin_elementwise_fma(c23, d23, -h23);
-          const f16x4 ah = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(uint32_t, h01),
-                                                                __builtin_bit_cast(uint32_t, h23)));
-          const f16x4 al = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(uint32_t, l01),
-                                                                __builtin_bit_cast(uint32_t, l23)));
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, wh[rt], O[rt][2 * g + e], 0, 0, 0);
-            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(al, wh[rt], O[rt][2 * g + e], 0, 0, 0);
-            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, wl[rt], O[rt][2 * g + e], 0, 0, 0);
-          }
-        }
-      }
-    } else {                        // bf16 parts
-      s16x4 bqh[RT], bql[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) split_bf16(pkr[rt], bqh[rt], bql[rt]);
-#pragma unroll
-      for (int g = 0; g < NVG; ++g) {
-        const uint32_t w = word_of(pb.v[g >> 2], g & 3);
-        float sc[4], off[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          sc[k] = pb.vscale(k, g);
-          off[k] = -8.0f * sc[k];
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t nib = (w >> (4 * e)) & 0x0f0f0f0fu;
-          uint32_t hb[4], lb[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float x = fmaf((float)((nib >> (8 * k)) & 0xffu), sc[k], off[k]);   // exact
-            hb[k] = __float_as_uint(x) & 0xffff0000u;
-            lb[k] = __float_as_uint(x - __uint_as_float(hb[k]));                    // exact, low half 0
-          }
-          const s16x4 ahi = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
-                                                                 __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)));
-          const s16x4 alo = __builtin_bit_cast(s16x4, make_uint2(__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
-                                                                 __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)));
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bqh[rt], O[rt][2 * g + e], 0, 0, 0);
-            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bqh[rt], O[rt][2 * g + e], 0, 0, 0);
-            O[rt][2 * g + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bql[rt], O[rt][2 * g + e], 0, 0, 0);
-          }
-        }
       }
     }
   }
@@ -531,7 +435,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   // ---- encode this wave's new cells into the cache; pages of the prologue that hold one are
   // loaded again once the stores have completed
-  bool fz_small = false;                                   // a new q4_0 V cell has a d below 2^-10
   if (fz_mask) {
 #pragma unroll
     for (int t = 0; t < kDecodeMaxFused; ++t) {
@@ -547,7 +450,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
         codes[v_tile_offset(2 * lane + 1, fz_slot[t])] = e.b1;
         if ((lane & 7) == 0)
           const_cast<uint16_t*>(a.v_scales)[(tile * KVQ_PAGE_SIZE + fz_slot[t]) * (D / 32) + (lane >> 3)] = e.d_bits;
-        fz_small = fz_small || (uint16_t)((e.d_bits & 0x7fffu) - 1u) < 0x13ffu;
       }
 #pragma unroll
       for (int kv = 0; kv < (VF == 1 ? 2 : 1); ++kv) {
@@ -647,63 +549,25 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;          // pages of this wave, >= 1
     // page i of the wave sits in ring slot i % (PD + 1)
-    auto run = [&](auto v16_tag) {
-      constexpr bool V16 = decltype(v16_tag)::value;
 #pragma unroll
-      for (int i = 0; i < PPW; ++i) {
-        const int pc = p0 + i * NW;
-        if (i + PD < PPW) load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page_id(min(i + PD, n_mine - 1)), kvh, lane);
-        page_step<D, RT, VF, DUP, V16>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
-        if (i + 1 >= n_mine) break;
-      }
-    };
-    if constexpr (VF == 2 && !DUP) {
-      // The row-tile kernel's fp16 V parts need every V scale of the wave's pages to be 0 or at least
-      // 2^-10 (fp16 exponent field >= 5): one look at all of them up front (lane l reads the scales
-      // of tokens 4 (l % 4) .. +3 of the wave's page l / 4, NVG / 2 16-byte units), then one of two
-      // page loops.
-      static_assert(PPW <= 16, "the scale scan covers 16 pages");
-      const int pl = min(lane >> 2, n_mine - 1);
-      const int pid = __shfl(my_ids, pl);
-      const uint4* vsp = reinterpret_cast<const uint4*>(a.v_scales + (((size_t)pid * a.hkv + kvh) * 16 + 4 * (lane & 3)) * NVG);
-      u16x2 mn = {0xffff, 0xffff};
-#pragma unroll
-      for (int c = 0; c < NVG / 2; ++c) {
-        const uint4 q = vsp[c];
-        const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, wd[e] & 0x7fff7fffu) - u16x2{1, 1});
-      }
-      // (the scan's plain loads may return a fused cell's slot as it was before this wave's store,
-      // from the CU's L1; the encoder's own check covers the new d)
-      if (__any(mn[0] < 0x13ffu || mn[1] < 0x13ffu || fz_small)) run(std::false_type{});
-      else run(std::true_type{});
-    } else {
-#pragma unroll
-      for (int i = 0; i < PPW; ++i) {
-        const int pc = p0 + i * NW;
-        if (i + PD < PPW) load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page_id(min(i + PD, n_mine - 1)), kvh, lane);
-        page_step<D, RT, VF, DUP, false>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
-        if (i + 1 >= n_mine) break;
-      }
+    for (int i = 0; i < PPW; ++i) {
+      const int pc = p0 + i * NW;
+      if (i + PD < PPW) load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page_id(min(i + PD, n_mine - 1)), kvh, lane);
+      page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
+      if (i + 1 >= n_mine) break;
     }
   }
 
-  // ---- per-wave totals: row sums over the 4 lane groups; remove the V operand bias (the exact
-  // code x scale operand of k8v4 with several row tiles carries none)
-  constexpr bool Q4A = VF == 2 && !DUP;
+  // ---- per-wave totals: row sums over the 4 lane groups; remove the V operand bias
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     l_run[rt] = sum_over_row_lanes(l_run[rt]);
-    if constexpr (!Q4A) {
 #pragma unroll
-      for (int g = 0; g < NVG; ++g) ls[rt][g] = sum_over_row_lanes(ls[rt][g]);
+    for (int g = 0; g < NVG; ++g) ls[rt][g] = sum_over_row_lanes(ls[rt][g]);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int g = VF == 1 ? t / 4 : t / 2;
-        O[rt][t] -= kOff * ls[rt][g];
-      }
+    for (int t = 0; t < NT; ++t) {
+      const int g = VF == 1 ? t / 4 : t / 2;
+      O[rt][t] -= kOff * ls[rt][g];
     }
   }
 
@@ -916,12 +780,8 @@ hipError_t launch_t(const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) 
   const bool groups = plan.row_tiles == 0 && plan.row_groups > 1;
   const int gx = groups ? (plan.n_splits + 7) / 8 * 8 * plan.row_groups : plan.n_splits;
   const dim3 grid((unsigned)gx, a.hkv, a.batch), block(sh.nw * 64);
-  if (plan.row_tiles > 0) {
-    if constexpr (VF == 2)
-      k_decode_split<D, RT, VF, sh.nw, sh.ppw, sh.pd, 1, false, true><<<grid, block, 0, s>>>(a);
-    else
-      return hipErrorInvalidValue;
-  } else if (!groups) {
+  if (plan.row_tiles > 0) return hipErrorInvalidValue;   // the wave-pair verify kernel takes these
+  if (!groups) {
     k_decode_split<D, 1, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, true><<<grid, block, 0, s>>>(a);
   } else {
     k_decode_split<D, 1, VF, sh.nw, sh.ppw, sh.pd, sh.occ, true, false><<<grid, block, 0, s>>>(a);
@@ -938,9 +798,6 @@ hipError_t launch_shape(const DecodePlan& plan, const DecodeArgs& a, hipStream_t
     case 2:                                   // 8 waves: not with several row tiles (LDS)
       if constexpr (RT == 1) return launch_t<D, RT, VF, 2>(plan, a, s);
       else return launch_t<D, RT, VF, 0>(plan, a, s);
-    case kRowTileShape:
-      if constexpr (VF == 2) return launch_t<D, RT, VF, kRowTileShape>(plan, a, s);
-      else return launch_t<D, RT, VF, 0>(plan, a, s);
     default: return launch_t<D, RT, VF, 0>(plan, a, s);
   }
 }
@@ -952,16 +809,15 @@ int decode_max_splits() { return kMaxSplits; }
 DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_pages, int max_rows) {
   DecodePlan p{};
   // up to 8 query rows per KV head share one MFMA (weights' hi parts in columns 0-7, lo parts in
-  // 8-15); more rows take one workgroup per group of 8 rows, except with a k8v4 V store, where
-  // one workgroup holds up to 4 row groups (its V operand is built once per page for all rows)
+  // 8-15); more rows take one workgroup per group of 8 rows, except with a k8v4 V store, where the
+  // wave-pair verify kernel holds all rows in row tiles of 16 (its V operand built once per page)
   p.rows = max_rows;
   p.row_groups = max(1, (max_rows + 7) / 8);
   p.row_tiles = (v_fmt == KVQ_FMT_Q4_0_H256 && max_rows > 8) ? (max_rows + 15) / 16 : 0;
   // 64-page splits (16 pages per wave, two in flight) unless they fill at most about half of the
   // CUs; then 32-page splits (twice the workgroups, one page in flight).  Measured: 64-page splits
   // win at 90% of the CUs (232 workgroups, 31.5 vs 33.5 us), 32-page splits at 50% (128, 22.7 vs
-  // 28.7 us).  The row-tile kernel takes its 64-page splits with one page in flight (66 vs 68 us
-  // for 3 query tokens x 8 query heads per KV head over 118750 cached tokens).
+  // 28.7 us).  The k8v4 verify kernel plans its 64-page splits as shape kRowTileShape.
   auto splits_of = [&](int sh) { return (max_pages + kShapes[sh].nw * kShapes[sh].ppw - 1) / (kShapes[sh].nw * kShapes[sh].ppw); };
   p.shape = shape_override();
   if (p.shape < 0) {
@@ -991,7 +847,7 @@ hipError_t launch_decode_combine(int D, const DecodePlan& plan, const DecodeArgs
 
 hipError_t launch_decode(int v_fmt, int D, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   if (v_fmt == KVQ_FMT_Q4_0_H256)
-    return plan.row_tiles == 2 ? launch_shape<256, 2, 2>(plan, a, s) : launch_shape<256, 1, 2>(plan, a, s);
+    return plan.row_tiles > 0 ? launch_decode_verify(plan.row_tiles, plan, a, s) : launch_shape<256, 1, 2>(plan, a, s);
   switch (D) {
     case 64: return launch_shape<64, 1, 1>(plan, a, s);
     case 128: return launch_shape<128, 1, 1>(plan, a, s);

@@ -121,6 +121,9 @@ struct DecodePlan {
 DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_pages, int max_rows);
 hipError_t launch_decode(int v_fmt, int head_dim, const DecodePlan& plan, const DecodeArgs& a,
                          hipStream_t s);
+// k8v4 (INT8_G64 K, Q4_0_H256 V) with more than 8 rows per KV head: wave pairs splitting head_dim
+// (row_tiles 1 or 2 tiles of 16 rows), then the combine
+hipError_t launch_decode_verify(int row_tiles, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 // the log-sum-exp combine of the split partials (every decode kernel writes the same layout)
 hipError_t launch_decode_combine(int head_dim, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 // ISO3 or ISO4 K and V stores (bits 3 or 4; head_dim 128 or 256, at most kIsoDecodeMaxRows rows per
