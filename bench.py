@@ -389,6 +389,72 @@ def read_probe(nbytes: int):
     print(json.dumps({"probe_bytes": nbytes, **res}))
 
 
+def page_probe(args):
+    """The int8 decode kernel's page stream without its arithmetic (libkvq_probe.so): for each
+    (waves, pages per wave, pages in flight, with / without scale loads) of a sweep, the per-launch µs
+    and GB/s over the workload's cache shape, on cache copies that together exceed the MALL.  One
+    JSON line per configuration."""
+    import ctypes
+    import torch
+    import quantized_paged_kv_kvq_amd as kvq
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(kvq.__file__), "libkvq_probe.so"))
+    lib.kvq_probe_page_stream.restype = ctypes.c_int
+    lib.kvq_probe_page_stream.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 8 + [ctypes.c_void_p] * 2
+    lib.kvq_probe_sink_words.restype = ctypes.c_int
+    lib.kvq_probe_sink_words.argtypes = [ctypes.c_int32] * 4
+    w = make_workload(args.workload)
+    if (w.fmt_k, w.fmt_v) != ("int8", "int8") or w.batch != 1:
+        raise SystemExit("--page-probe takes a single-sequence int8 K + V workload")
+    D, hkv, npg = w.head_dim, w.n_kv_heads, w.num_pages
+    max_pages = int((w.seq_lens[0] + w.page_size - 1) // w.page_size)
+    code_bytes, scale_halves = npg * hkv * 16 * D, npg * hkv * 16 * (D // 64)
+    per_copy = 2 * code_bytes + 4 * scale_halves
+    R = args.replicas or max(2, int(np.ceil(3 * MALL_BYTES / per_copy)) + 1)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    copies = []
+    for _ in range(R):
+        k = torch.randint(0, 256, (code_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
+        v = torch.randint(0, 256, (code_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
+        ks = torch.randint(0, 1 << 15, (scale_halves,), dtype=torch.int16, device="cuda", generator=gen)
+        vs = torch.randint(0, 1 << 15, (scale_halves,), dtype=torch.int16, device="cuda", generator=gen)
+        copies.append((k, v, ks, vs))
+    table = torch.from_numpy(np.ascontiguousarray(w.block_table[0][:max_pages], dtype=np.int32)).cuda()
+    stream = torch.cuda.current_stream()
+    full = max_pages * hkv * (2 * 16 * D + 2 * 16 * (D // 64) * 2)     # codes and scales of every page
+    sweep = [(4, 16, 2), (4, 16, 1), (4, 16, 3), (4, 8, 1), (4, 8, 2), (8, 8, 1), (8, 8, 2), (8, 4, 1),
+             (4, 4, 2), (2, 16, 2), (8, 16, 2)]
+    for waves, ppw, depth in sweep:
+        for no_scales in (0, 1):
+            n_sink = lib.kvq_probe_sink_words(max_pages, hkv, waves, ppw)
+            sink = torch.empty(n_sink, dtype=torch.int32, device="cuda")
+
+            def launch(r, st):
+                k, v, ks, vs = copies[r]
+                rc = lib.kvq_probe_page_stream(k.data_ptr(), v.data_ptr(), ks.data_ptr(), vs.data_ptr(),
+                                               table.data_ptr(), max_pages, npg, hkv, D, waves, ppw, depth,
+                                               no_scales, sink.data_ptr(), st.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"page probe failed ({rc})")
+
+            for r in range(R):
+                launch(r, stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(R):
+                    launch(r, torch.cuda.current_stream())
+            g.replay()
+            torch.cuda.synchronize()
+            us = time_batches(stream, 50, R, g, None)
+            moved = full if not no_scales else max_pages * hkv * 2 * 16 * D
+            med = float(np.median(us))
+            print(json.dumps({"page_probe": w.name, "waves": waves, "pages_per_wave": ppw, "in_flight": depth,
+                              "scales": not no_scales, "workgroups": n_sink // waves, "cache_replicas": R,
+                              "us_p50": round(med, 3), "us_p10": round(float(np.percentile(us, 10)), 3),
+                              "bytes": moved, "GB/s": round(moved / (med * 1e-6) / 1e9, 1)}), flush=True)
+            del g
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,6 +474,9 @@ def main():
                     help="run only a plain device copy of BYTES (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--read-probe", type=int, default=0, metavar="BYTES",
                     help="time only a plain streaming read and a plain copy of BYTES (context for the roofline)")
+    ap.add_argument("--page-probe", action="store_true",
+                    help="time only the int8 decode kernel's page stream (no arithmetic) over a sweep of launch "
+                         "shapes, with and without the scale loads, on the workload's cache shape")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the hot path runs on one GPU "
@@ -424,6 +493,8 @@ def main():
     if args.read_probe:
         return read_probe(args.read_probe)
     kvq.lib()
+    if args.page_probe:
+        return page_probe(args)
     if args.workload in ("iso3_extend", "int8_extend"):
         return bench_extend(args)
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)

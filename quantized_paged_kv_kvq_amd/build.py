@@ -1,4 +1,5 @@
-"""Build libkvq.so (HIP for gfx950) in place, next to this file.
+"""Build libkvq.so (HIP for gfx950) in place, next to this file, and the measurement library
+libkvq_probe.so (a page-stream probe that bench.py times; libkvq does not use it).
 
     python -m quantized_paged_kv_kvq_amd.build [--asm]
 
@@ -19,6 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
+PROBE_UNIT = "page_probe.hip"
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
@@ -63,17 +66,25 @@ def _compile(unit: str, extra, asm: bool) -> str:
 def build(asm: bool = False, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     units = [u for u in UNITS if os.path.exists(os.path.join(CSRC, u))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(units))) as ex:
-        objs = list(ex.map(lambda u: _compile(u, UNITS[u], asm), units))
-    tmp = LIB + ".tmp"
+    probe = [PROBE_UNIT] if os.path.exists(os.path.join(CSRC, PROBE_UNIT)) else []
+    extra = {**UNITS, PROBE_UNIT: ["-mllvm", "-pragma-unroll-threshold=200000"]}
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(units) + len(probe))) as ex:
+        objs = list(ex.map(lambda u: _compile(u, extra[u], asm), units + probe))
+    _link(objs[:len(units)], LIB)
+    if probe:
+        _link(objs[len(units):], PROBE_LIB)
+    if verbose:
+        print(f"built {LIB}" + (f" and {PROBE_LIB}" if probe else ""))
+    return LIB
+
+
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":
