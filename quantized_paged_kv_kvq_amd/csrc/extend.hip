@@ -362,12 +362,14 @@ __device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, cons
       for (int kb = 0; kb < 2; ++kb)
         ka[cb ^ 1][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, 2 * (ks + 1) + h));
     }
+    // the next step's operand reads are issued before this step's MFMAs (a real double buffer:
+    // the scheduler would otherwise reuse one register set and wait for each read)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int part = 0; part < NQ; ++part)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) S[kb] = Ops::mma(ka[cb][kb], q[part][ks], S[kb]);
-    if (ks + 1 < KS1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NQ, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -596,8 +598,8 @@ __device__ __forceinline__ void sync_tiles(bool loads) {
   __syncthreads();
 }
 
-// Ping-pong over n tiles.  The two 4-wave groups alternate between an MFMA cluster (QK of tile
-// it+1, PV of tile it) and a VALU cluster (softmax of tile it's scores, the weights' split); group
+// Ping-pong over n tiles.  The two 4-wave groups alternate between an MFMA cluster (PV of tile
+// it, QK of tile it+1) and a VALU cluster (softmax of tile it's scores, the weights' split); group
 // B runs one barrier phase behind group A, so one group's MFMAs overlap the other's softmax.
 // Tiles live in a ring of three LDS buffers; tile it+2 is loaded during barrier phase 2*it+1 (by
 // group A in its MFMA cluster, group B in its VALU cluster), after the last read of tile it-1
@@ -630,11 +632,16 @@ __device__ __forceinline__ void run_tiles(const Tiles& k, int n, uint8_t* ring, 
     // weights and the rescale into the MFMA cluster, next to their uses)
     pin(Pw, O);
     sync_tiles(!group_b);            // group A: tile it+1's loads, issued one phase ago, have landed
-    // ---- MFMA cluster: QK of tile it+1, PV of tile it
-    if (!group_b && it + 2 < n) issue_tile(k.image(it + 2), buf(it + 2), wv, lane);
-    if (it + 1 < n && k.active(it + 1)) k.qk(buf(it + 1), l32, h, S);
+    // ---- MFMA cluster: PV of tile it, then QK of tile it+1 (in this order the weights are dead
+    // before the scores are born, which leaves registers for operand double buffering); group A
+    // issues tile it+2's loads after them, so that no wait on the vector memory counter inside the
+    // cluster (a register reload) waits for the tile
     if (act) k.pv(buf(it), l32, h, Pw, O);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < n && k.active(it + 1)) k.qk(buf(it + 1), l32, h, S);
     pin(S, O);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!group_b && it + 2 < n) issue_tile(k.image(it + 2), buf(it + 2), wv, lane);
     sync_tiles(group_b);             // group B: tile it+2's loads, issued one phase ago, have landed
   }
   if (!group_b) sync_tiles(true);
