@@ -198,12 +198,13 @@ __device__ __forceinline__ void load_page_dev(PageBuf<D, 2>& pb, const DecodeArg
 constexpr float kLazyLog2 = 8.0f;     // weights stay below 2^8 between rescalings
 
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
-// DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the bf16 hi part of
-// the softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both.  (k8v4 with
+// DUP (at most 8 rows): MFMA columns 8..15 repeat rows 0..7; columns 0..7 take the hi part of the
+// softmax weights and columns 8..15 the lo part, so one PV MFMA per tile does both (int8 V: fp16
+// parts against the exact fp16 codes; q4_0 V: bf16 parts against biased bf16 codes).  (k8v4 with
 // more than 8 rows per KV head runs in the wave-pair verify kernel.)
 template <int D, int RT, int VF, bool DUP, class QF>
 __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j4, bool lo_col, const int (&Lrow)[RT],
-                                          const QF& qf, const float (&qmul)[RT],
+                                          const QF& qf, const float (&qmul)[RT], float kexp,
                                           float (&m_run)[RT], float (&l_run)[RT],
                                           float (&ls)[RT][VF == 1 ? D / 64 : D / 32], f32x4 (&O)[RT][D / 16]) {
   constexpr int NG = D / 64;
@@ -248,15 +249,20 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
     const bool rescale = move && m_run[rt] != kNegInf;
     const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run[rt] - m_use) : 1.0f;
     m_run[rt] = m_new;
+    // int8 V: the weights carry the wave's factor 2^kexp (l and O with them; the partial's m is
+    // m_run - kexp)
+    const float m_w = VF == 1 ? m_use - kexp : m_use;
     float pk[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_use);
+    for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_w);
     l_run[rt] = l_run[rt] * alpha + ((pk[0] + pk[1]) + (pk[2] + pk[3]));
     if (__any(rescale)) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) O[rt][t] *= alpha;
+      if constexpr (VF != 1) {
 #pragma unroll
-      for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
+        for (int g = 0; g < NVG; ++g) ls[rt][g] *= alpha;
+      }
     }
 
     // ---- PV per V scale group
@@ -267,46 +273,32 @@ __device__ __forceinline__ void page_step(const PageBuf<D, VF>& pb, int p, int j
       // masked tokens have pk == 0; the scales of cells past a sequence's length are finite by
       // contract (zero-initialised slabs), so their weights are exact zeros without a select
       for (int k = 0; k < 4; ++k) pw[k] = pk[k] * pb.vscale(k, g);
-      s16x4 bhi, blo;
-      if constexpr (DUP) {
-        float used[4];
-        split_bf16_select(pw, lo_col ? 0xffffffffu : 0u, bhi, used);
-        ls[rt][g] += (used[0] + used[1]) + (used[2] + used[3]);
-        if constexpr (VF == 1) {
+      if constexpr (VF == 1) {
+        // fp16 parts of the weights (below 2^15 by the choice of kexp) against the exact fp16 codes:
+        // columns 0..7 the rounded weight, 8..15 its rounding error
+        f16x4 bw;
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const int t = 4 * g + tt;
-            O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(codes_to_bf16_biased(word_of(pb.v[g], tt)), bhi,
-                                                                 O[rt][t], 0, 0, 0);
-          }
-        } else {
-          const uint32_t w = word_of(pb.v[g >> 2], g & 3);
-          O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nibbles_to_bf16_biased(w & 0x0f0f0f0fu), bhi,
-                                                                   O[rt][2 * g], 0, 0, 0);
-          O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              nibbles_to_bf16_biased((w >> 4) & 0x0f0f0f0fu), bhi, O[rt][2 * g + 1], 0, 0, 0);
+        for (int k = 0; k < 4; ++k) {
+          const _Float16 hi = (_Float16)pw[k];
+          bw[k] = lo_col ? (_Float16)(pw[k] - (float)hi) : hi;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int t = 4 * g + tt;
+          O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes_to_f16x4(word_of(pb.v[g], tt)), bw, O[rt][t], 0, 0, 0);
         }
         continue;
       }
-      ls[rt][g] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-      split_bf16(pw, bhi, blo);
-      if constexpr (VF == 1) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {              // tiles 4g .. 4g+3 (head_dim 64g .. 64g+63)
-          const int t = 4 * g + tt;
-          const s16x4 av = codes_to_bf16_biased(word_of(pb.v[g], tt));
-          O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bhi, O[rt][t], 0, 0, 0);
-          O[rt][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, blo, O[rt][t], 0, 0, 0);
-        }
-      } else {
-        const uint32_t w = word_of(pb.v[g >> 2], g & 3);   // pair row 16g + i16: d = 32g + 2*i16 (+1)
-        const s16x4 alo = nibbles_to_bf16_biased(w & 0x0f0f0f0fu);
-        const s16x4 ahi = nibbles_to_bf16_biased((w >> 4) & 0x0f0f0f0fu);
-        O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bhi, O[rt][2 * g], 0, 0, 0);
-        O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, O[rt][2 * g], 0, 0, 0);
-        O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bhi, O[rt][2 * g + 1], 0, 0, 0);
-        O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, O[rt][2 * g + 1], 0, 0, 0);
-      }
+      // q4_0 V: biased bf16 codes (pair row 16g + i16: d = 32g + 2*i16 (+1)) against bf16 parts
+      s16x4 bhi;
+      float used[4];
+      split_bf16_select(pw, lo_col ? 0xffffffffu : 0u, bhi, used);
+      ls[rt][g] += (used[0] + used[1]) + (used[2] + used[3]);
+      const uint32_t w = word_of(pb.v[g >> 2], g & 3);
+      O[rt][2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nibbles_to_bf16_biased(w & 0x0f0f0f0fu), bhi,
+                                                               O[rt][2 * g], 0, 0, 0);
+      O[rt][2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nibbles_to_bf16_biased((w >> 4) & 0x0f0f0f0fu),
+                                                                   bhi, O[rt][2 * g + 1], 0, 0, 0);
     }
   }
 }
@@ -316,7 +308,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   constexpr int NG = D / 64;
   constexpr int NVG = VF == 1 ? D / 64 : D / 32;
   constexpr int NT = D / 16;                                // PV tiles of 16 head_dim rows
-  constexpr float kOff = VF == 1 ? 128.0f : 136.0f;         // bias carried by the V A-operand
+  constexpr float kOff = 136.0f;                            // bias carried by the q4_0 V A-operand
   const int RA = a.row_alloc;                               // allocated rows per (sequence, KV head)
 
   // wave-uniform wave index: page addresses are scalar arithmetic
@@ -419,6 +411,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   constexpr int kQBytes = RT * NG * 2 * 64 * 16;
   constexpr int kMergeBytes = NW * (NT * 64 * 16 + 2 * 64 * 4);   // one row tile at a time
   __shared__ __align__(16) uint8_t smem[kQBytes + kMergeBytes];
+  // int8 V: the V scales of this wave's pages (lane l reads a quarter of the scales of page l / 4 of
+  // the wave's list), issued before the page stream so that waiting for them waits for nothing else
+  constexpr int kScanWords = 2 * NG;
+  uint32_t vscan[kScanWords] = {};
+  if constexpr (VF == 1) {
+    const int pid = __shfl(my_ids, min(lane >> 2, PPW - 1));
+    const uint32_t* src =
+        reinterpret_cast<const uint32_t*>(a.v_scales + ((size_t)pid * a.hkv + kvh) * KVQ_PAGE_SIZE * NG) +
+        (lane & 3) * kScanWords;
+    if constexpr (kScanWords == 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(src);
+      vscan[0] = t.x; vscan[1] = t.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < kScanWords / 4; ++c) {
+        const uint4 t = *reinterpret_cast<const uint4*>(src + 4 * c);
+        vscan[4 * c] = t.x; vscan[4 * c + 1] = t.y; vscan[4 * c + 2] = t.z; vscan[4 * c + 3] = t.w;
+      }
+    }
+  }
   PageBuf<D, VF> buf[PD + 1];
 #pragma unroll
   for (int i = 0; i < PD && i < PPW; ++i)
@@ -435,6 +447,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   float* part_o = a.part + (size_t)a.batch * a.hkv * RA * a.n_splits * 2;
   // ---- encode this wave's new cells into the cache; pages of the prologue that hold one are
   // loaded again once the stores have completed
+  uint32_t fz_vmax = 0;                                     // the new cells' V scales (int8 V)
   if (fz_mask) {
 #pragma unroll
     for (int t = 0; t < kDecodeMaxFused; ++t) {
@@ -466,6 +479,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
             for (int q = 0; q < 4; ++q) codes[v_tile_offset(4 * lane + q, fz_slot[t])] = (uint8_t)(e.packed >> (8 * q));
           }
           if ((lane & 15) == 0) scales[(tile * KVQ_PAGE_SIZE + fz_slot[t]) * NG + (lane >> 4)] = e.scale_bits;
+          if (kv == 1) fz_vmax = max(fz_vmax, (uint32_t)(e.scale_bits & 0x7fffu));
         }
       }
     }
@@ -474,6 +488,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
 #pragma unroll
     for (int i = 0; i < PD && i < PPW; ++i)
       if ((fz_mask >> i) & 1) load_page_dev<D>(buf[i], a, page_id(i), kvh, lane);
+  }
+
+  // int8 V: the weights' factor 2^kexp, from the largest V scale d of the wave's visible pages (the
+  // scan may read a new cell's slot as it was before this wave's store: the encoder's own scales are
+  // included).  With weights below 2^8 (lazy rescaling) and d < 2^(E - 14) (E: d's fp16 exponent
+  // field), 2^(21 - E) keeps every weight times d below 2^15, where its fp16 hi and lo parts are
+  // exact to 22 bits, and small weights stay clear of the fp16 subnormals.
+  float kexp = 0.0f;
+  if constexpr (VF == 1) {
+    const int n_w = p0 < p_end ? (p_end - 1 - p0) / NW + 1 : 0;
+    uint32_t mx = fz_vmax;
+    if ((lane >> 2) < n_w) {
+#pragma unroll
+      for (int c = 0; c < kScanWords; ++c) mx = max(mx, max(vscan[c] & 0x7fffu, (vscan[c] >> 16) & 0x7fffu));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    kexp = (float)(21 - clampi((int)(mx >> 10), 1, 31));
   }
 
   if (R == 0) return;
@@ -553,21 +585,23 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
     for (int i = 0; i < PPW; ++i) {
       const int pc = p0 + i * NW;
       if (i + PD < PPW) load_page<D, VF, NTL>(buf[(i + PD) % (PD + 1)], a, page_id(min(i + PD, n_mine - 1)), kvh, lane);
-      page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, m_run, l_run, ls, O);
+      page_step<D, RT, VF, DUP>(buf[i % (PD + 1)], pc, j4, lo_col, Lrow, qlds, qmul, kexp, m_run, l_run, ls, O);
       if (i + 1 >= n_mine) break;
     }
   }
 
-  // ---- per-wave totals: row sums over the 4 lane groups; remove the V operand bias
+  // ---- per-wave totals: row sums over the 4 lane groups; int8 V: the reference of l and O is
+  // m_run - kexp; q4_0 V: remove the V operand bias
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     l_run[rt] = sum_over_row_lanes(l_run[rt]);
+    if constexpr (VF == 1) {
+      if (m_run[rt] != kNegInf) m_run[rt] -= kexp;
+    } else {
 #pragma unroll
-    for (int g = 0; g < NVG; ++g) ls[rt][g] = sum_over_row_lanes(ls[rt][g]);
+      for (int g = 0; g < NVG; ++g) ls[rt][g] = sum_over_row_lanes(ls[rt][g]);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int g = VF == 1 ? t / 4 : t / 2;
-      O[rt][t] -= kOff * ls[rt][g];
+      for (int t = 0; t < NT; ++t) O[rt][t] -= kOff * ls[rt][t / 2];
     }
   }
 
@@ -576,6 +610,63 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
   // Hadamard, so there wave 0 merges everything.
   float* lds_o = reinterpret_cast<float*>(smem + kQBytes);           // [wave][t][lane] x f32x4
   float* lds_ml = lds_o + NW * NT * 64 * 4;                           // [wave][m | l][lane]
+  const bool direct = a.n_splits == 1;
+  if constexpr (VF == 1 && NW > 1 && (D / 16) % NW == 0) {
+    // int8 V (one row tile, duplicated columns): straight-line code -- wave w's tiles are
+    // t = w + NW * tt, held in a statically indexed array, so the LDS reads of all of them are in
+    // flight together and no branch separates them
+    static_assert(RT == 1 && DUP, "one row tile of duplicated columns");
+    constexpr int TPW = NT / NW;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(lds_o + ((wv * NT + t) * 64 + lane) * 4) = O[0][t];
+    lds_ml[(wv * 2 + 0) * 64 + lane] = m_run[0];
+    lds_ml[(wv * 2 + 1) * 64 + lane] = l_run[0];
+    __syncthreads();
+    float mv[NW], lv[NW], cv[NW];
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      mv[v] = lds_ml[(v * 2 + 0) * 64 + lane];
+      lv[v] = lds_ml[(v * 2 + 1) * 64 + lane];
+      M = fmaxf(M, mv[v]);
+    }
+    const float Mu = M == kNegInf ? 0.0f : M;
+    float l = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      cv[v] = __builtin_amdgcn_exp2f(mv[v] - Mu);
+      l += cv[v] * lv[v];
+    }
+    f32x4 mo[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int t = wv + NW * tt;
+      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int v = 0; v < NW; ++v) acc += cv[v] * *reinterpret_cast<const f32x4*>(lds_o + ((v * NT + t) * 64 + lane) * 4);
+      // column r + 8 holds the lo-part sums of row r: add them in (each DPP source a scalar copy,
+      // written to a fresh vector: see dpp_ror8)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = acc[k];
+        mo[tt][k] = x + dpp_ror8(x);
+      }
+    }
+    // the workgroup's partial for rows r < R; with a single split the normalised output itself
+    const int r = 8 * rg + i16;
+    if (r >= R || i16 >= 8) return;
+    float* row = direct ? a.out + (size_t)qrow[0] * D : part_o + ((row0 + r) * a.n_splits + split) * D;
+    const float sc = direct ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f;
+    if (!direct && j4 == 0 && wv == 0) {
+      float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
+      ml[0] = M; ml[1] = l;
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)                   // lane holds d = 16t + 4*j4 + k
+      *reinterpret_cast<float4*>(row + 16 * (wv + NW * tt) + 4 * j4) =
+          make_float4(mo[tt][0] * sc, mo[tt][1] * sc, mo[tt][2] * sc, mo[tt][3] * sc);
+    return;
+  }
   if constexpr (NW > 1) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -634,7 +725,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_split(const DecodeArgs 
 
   // ---- write the workgroup's partial for rows r < R; with a single split, the normalised output
   // itself (no combine launch follows)
-  const bool direct = a.n_splits == 1;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = DUP ? 8 * (rg + rt) + i16 : 16 * rt + i16;

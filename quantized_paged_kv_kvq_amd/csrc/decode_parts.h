@@ -20,6 +20,15 @@ __device__ __forceinline__ f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// 4 int8 codes (code e in byte e) -> 4 exact fp16 values.
+__device__ __forceinline__ f16x4 codes_to_f16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;                                 // biased: code + 128
+  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u)) - off;
+  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u)) - off;
+  return f16x4{p0[0], p0[1], p1[0], p1[1]};
+}
+
 // 4 int8 codes -> bf16 (code + 128), exact (integers below 256 have 8 significant bits).
 __device__ __forceinline__ s16x4 codes_to_bf16_biased(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;
