@@ -19,13 +19,16 @@
 //     accumulates separately and is weighted by its (token, group) scale in fp32.
 //   * Online softmax in base 2 per row; the row max is shared by the 4 lanes holding a row's 16
 //     tokens of a page; the running sum stays per lane until the end.
-//   * PV: O^T[d][row] with v_mfma_f32_16x16x16bf16_1k.  The B operand is the S^T accumulator
-//     layout itself (lane: 4 tokens x 1 row) after exp2 and multiplication by the (token, group)
-//     V scale, split into bf16 hi + lo parts (16 significant bits); the A operand is 4 tokens'
-//     codes at one head_dim position converted exactly to bf16 as (code + 128) -- int8 -- or
-//     (code + 128) -- 4-bit q4_0 code, value code - 8 -- with the offset removed at the end from
-//     the per-group sums of the weights.  Every MFMA tile of 16 head_dim rows lies inside one
-//     scale group, so one weight vector per group serves all its tiles.
+//   * PV: O^T[d][row] with a 16x16x16 MFMA.  The B operand is the S^T accumulator layout itself
+//     (lane: 4 tokens x 1 row) after exp2 and multiplication by the (token, group) V scale, split
+//     into a hi and a lo part.  int8 V: fp16 parts (22 significant bits) against the 4 tokens'
+//     codes at one head_dim position as exact fp16 values (the permute above); every weight
+//     carries the wave's factor 2^kexp, from the largest V scale of its pages, which keeps weight
+//     times scale below 2^15 (no fp16 overflow, small weights clear of the subnormals); the
+//     partial records the reference max minus kexp.  q4_0 V (k8v4, up to 8 rows): bf16 parts
+//     (16 bits) against (code + 128) in bf16 -- 4-bit code, value code - 8 -- with the offset
+//     removed at the end from the per-group sums of the weights.  Every MFMA tile of 16 head_dim
+//     rows lies inside one scale group, so one weight vector per group serves all its tiles.
 //   * The NW waves of a workgroup merge (m, l, O) through LDS in one round (each wave merges and
 //     writes a share of the head_dim tiles; k8v4 rotates the merged partial back by H); the
 //     workgroup writes one unnormalised partial.  A second kernel merges the splits with a
