@@ -107,6 +107,24 @@ def recorded_traffic(workload: str):
     return int(m.group(4))
 
 
+def recorded_kernel(workload: str):
+    """The split kernel's cold median (us) from the committed kernel-trace record of this workload, or
+    None when there is none or the decode kernel source has changed since the trace was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "decode_int8_moe_131072.md")
+    if not os.path.exists(path):
+        return None
+    for m in re.finditer(r"kernel-record: workload=(\S+) kernel=(\S+) source=(\S+) source_sha256_16=([0-9a-f]+) "
+                         r"median_us=([0-9.]+)", open(path).read()):
+        if m.group(1) != workload:
+            continue
+        src = os.path.join(ROOT, m.group(3))
+        if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] == m.group(4):
+            return {"kernel": m.group(2), "median_us": float(m.group(5))}
+    return None
+
+
 def host_info():
     """CPU model, the machine's physical cores and the threads this process may run on."""
     model, cores, phys, core = None, set(), None, None
@@ -632,6 +650,14 @@ def main():
         warm_us = float(np.mean(time_batches(stream, 20, R, warm_graph,
                                              lambda: [decode_one(0, stream) for _ in range(R)])))
     pct = {k: round(float(np.percentile(dec_us, q)), 3) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+    # The dominant kernel alone: the same algorithmic bytes over the split kernel's cold median from
+    # the committed rocprofv3 trace of this build (None when the source has changed since)
+    rk = recorded_kernel(w.name) if fused else None
+    kernel_level = None if rk is None else {
+        "kernel": rk["kernel"], "median_us": rk["median_us"],
+        "achieved": round(algo / (rk["median_us"] * 1e-6) / 1e9, 1),
+        "frac": round(algo / (rk["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "timing": "rocprofv3 kernel trace, committed profile (cold-phase median)"}
     print(f"[bench] {mode}: decode launch avg {dec_avg:.2f} us over {n_batches} x {per_batch} launches "
           f"(p10/p50/p90 {pct['p10']}/{pct['p50']}/{pct['p90']}), step {ms_per_step * 1e3:.2f} us, "
           f"{achieved:.0f} GB/s; warm {warm_us if warm_us is None else round(warm_us, 2)} us",
@@ -670,6 +696,7 @@ def main():
                                 "the step's cells + log-sum-exp combine kernel)" if fused else
                                 "decode attention launch (split-K kernel + log-sum-exp combine kernel)"),
                      "launch_us": round(dec_avg, 3), "algorithmic_bytes": int(algo),
+                     "kernel_level": kernel_level,
                      "timing": f"HIP events around {n_batches} batches of {per_batch} back-to-back launches, "
                                f"one per cache copy"},
         "launch_us_percentiles": {**pct, "n": n_batches,
