@@ -290,8 +290,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a)
   constexpr int NT = D / 16;                        // PV tiles of 16 head_dim rows
   constexpr int NTG = NT / 4;                       // groups of 4 tiles: 4 consecutive head_dim per lane
   constexpr int NL = 1 << (2 * BITS);               // pair-table entries
-  __shared__ uint32_t lut[NL];
-  __shared__ __align__(16) float mrg[NW * (NT * 64 * 4 + 2 * 64)];
+  // one LDS allocation with the pair table at its start: table addresses then fit the 16-bit offset
+  // of the LDS loads, so a lookup's address is the shifted, masked code pair alone (two separate
+  // arrays put the table after the merge buffers, past that range, with one more add per lookup)
+  __shared__ __align__(16) uint32_t lds[NL + NW * (NT * 64 * 4 + 2 * 64)];
+  uint32_t* const lut = lds;
+  float* const mrg = reinterpret_cast<float*>(lds + NL);
 
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
