@@ -281,9 +281,13 @@ __device__ __forceinline__ void fpage_step(const FPage<D, KF, VF>& pb, int p, in
 template <int D, int RT, bool KF, bool VF, int NW, int PPW, int PD>
 __global__ __launch_bounds__(NW * 64, 1) void k_decode_f32(const DecodeArgs a) {
   constexpr int NG = D / 64, NT = D / 16, NS = D / 32;
-  __shared__ __align__(16) uint4 qlds[RT * NS * 64];            // QK B operands: [row tile][step][lane]
-  __shared__ float qmul_lds[RT * 16];
-  __shared__ __align__(16) float mrg[(NW - 1) * NT * 64 * 4 + NW * RT * 2 * 64];
+  // one LDS allocation, the per-page operands first (their addresses then fit the 16-bit offset of
+  // the LDS loads)
+  constexpr int kQBytes = RT * NS * 64 * 16, kMulBytes = RT * 16 * 4;
+  __shared__ __align__(16) uint8_t lds[kQBytes + kMulBytes + ((NW - 1) * NT * 64 * 4 + NW * RT * 2 * 64) * 4];
+  uint4* const qlds = reinterpret_cast<uint4*>(lds);             // QK B operands: [row tile][step][lane]
+  float* const qmul_lds = reinterpret_cast<float*>(lds + kQBytes);
+  float* const mrg = reinterpret_cast<float*>(lds + kQBytes + kMulBytes);
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, j4 = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;

@@ -173,9 +173,13 @@ __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, boo
 template <bool DUP, int NW, int PPW, int PD, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) {
   constexpr int NP = DUP ? 1 : 2;                       // query fragment parts per group
-  __shared__ __align__(16) float mrg[NW * (kTiles * 64 * 4 + 2 * 64)];
-  __shared__ __align__(16) f16x8 qlds[kGroups * NP * 64];    // B operands of QK: [group][part][lane]
-  __shared__ float qmul_lds[64];
+  // one LDS allocation, the per-page operands first: the query fragments' addresses then fit the
+  // 16-bit offset of the LDS loads (after the merge buffers they would need one more add per read)
+  constexpr int kQBytes = kGroups * NP * 64 * 16, kMulBytes = 64 * 4;
+  __shared__ __align__(16) uint8_t lds[kQBytes + kMulBytes + NW * (kTiles * 64 * 4 + 2 * 64) * 4];
+  f16x8* const qlds = reinterpret_cast<f16x8*>(lds);           // B operands of QK: [group][part][lane]
+  float* const qmul_lds = reinterpret_cast<float*>(lds + kQBytes);
+  float* const mrg = reinterpret_cast<float*>(lds + kQBytes + kMulBytes);
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15, w = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -433,9 +437,11 @@ DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows) {
     const int pps = kQ4Shapes[sh].nw * kQ4Shapes[sh].ppw;
     return (max_pages + pps - 1) / pps;
   };
-  // 64-page splits unless they would fill at most about half of the CUs; then 32-page splits
+  // 64-page splits unless they would put at most one workgroup on each CU; then 32-page splits (the
+  // kernel's registers allow two waves per SIMD, so two workgroups share a CU: 40.5 -> 39.3 us for one
+  // 131,072-token sequence over two KV heads)
   p.shape = q4_shape_override();
-  if (p.shape < 0) p.shape = ((long)splits_of(0) * hkv * batch * 20 <= (long)device_cu_count() * 11) ? 1 : 0;
+  if (p.shape < 0) p.shape = ((long)splits_of(0) * hkv * batch <= (long)device_cu_count()) ? 1 : 0;
   p.waves = kQ4Shapes[p.shape].nw;
   p.pages_per_split = kQ4Shapes[p.shape].nw * kQ4Shapes[p.shape].ppw;
   p.n_splits = splits_of(p.shape);

@@ -66,6 +66,13 @@ def test_iso4_decode_ragged_lengths(D):
                               n_kv_heads=2, head_dim=D))
 
 
+def test_iso4_decode_64_page_splits():
+    """Four sequences over eight KV heads: 9 x 8 x 4 = 288 splits of 64 pages fill more than one
+    workgroup per CU, so the plan keeps 64-page splits (the other launch shape)."""
+    check(synth.ragged_decode("iso4", "iso4", [9000, 8200, 4100, 9000], seed=83, n_q_heads=16, n_kv_heads=8,
+                              head_dim=128))
+
+
 def test_iso4_decode_eight_rows_head_dim_256():
     check(synth.ragged_decode("iso4", "iso4", [5, 700, 4100], seed=93, n_q_heads=16, n_kv_heads=2, head_dim=256))
 

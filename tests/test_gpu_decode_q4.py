@@ -47,6 +47,12 @@ def test_q4_decode_ragged_lengths():
     check(q4([1, 15, 16, 17, 300, 1024, 2100], 81, n_q_heads=8, n_kv_heads=2))
 
 
+def test_q4_decode_64_page_splits():
+    """Four sequences over eight KV heads: 9 x 8 x 4 = 288 splits of 64 pages fill more than one
+    workgroup per CU, so the plan keeps 64-page splits (the other launch shape)."""
+    check(q4([9000, 8200, 4100, 9000], 82, n_q_heads=16, n_kv_heads=8))
+
+
 def test_q4_decode_eight_rows():
     check(q4([5, 700, 4100], 82, n_q_heads=16, n_kv_heads=2))
 
