@@ -38,8 +38,21 @@ METRIC = "decode-attn µs/step + achieved HBM GB/s vs peak, int8 KV @128K ctx"
 EXTEND_METRIC = "extend-attn µs/step + achieved MFMA TFLOP/s vs dense fp16 peak, ISO3 KV, 30k prefix + 2048 new"
 
 
-def make_workload(name: str):
+def make_workload(name: str, ctx: int = 0):
+    """The named workload; ctx > 0 sets the context of the single-sequence MoE-layer decode workloads."""
     import synth
+    if ctx and name.startswith("moe_") and name != "moe_int8_decode_64k":
+        if name == "moe_int8_decode":
+            return synth.moe_int8_decode(ctx=ctx)
+        if name in ("moe_iso3_decode", "moe_iso4_decode"):
+            return synth.moe_iso3_decode(ctx=ctx, fmt=name[4:8])
+        if name == "moe_q4h_decode":
+            return synth.moe_q4h_decode(ctx=ctx)
+        if name in ("moe_k8v32_decode", "moe_k32v8_decode"):
+            return synth.moe_single_store_decode("int8" if name[5] == "8" else "f32",
+                                                 "f32" if name[5] == "8" else "int8", ctx=ctx)
+    elif ctx:
+        raise SystemExit("--ctx applies to the single-sequence moe_* decode workloads")
     if name == "moe_int8_decode":
         return synth.moe_int8_decode(ctx=131072)
     if name == "moe_int8_decode_64k":
@@ -420,7 +433,7 @@ def page_probe(args):
     lib.kvq_probe_page_stream.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 8 + [ctypes.c_void_p] * 2
     lib.kvq_probe_sink_words.restype = ctypes.c_int
     lib.kvq_probe_sink_words.argtypes = [ctypes.c_int32] * 4
-    w = make_workload(args.workload)
+    w = make_workload(args.workload, args.ctx)
     if (w.fmt_k, w.fmt_v) != ("int8", "int8") or w.batch != 1:
         raise SystemExit("--page-probe takes a single-sequence int8 K + V workload")
     D, hkv, npg = w.head_dim, w.n_kv_heads, w.num_pages
@@ -483,6 +496,8 @@ def main():
                          "iso3_extend, "
                          "int8_extend, moe_q4h_decode, moe_iso3_decode, batched_iso3_decode, moe_iso4_decode, "
                          "moe_k8v32_decode, moe_k32v8_decode")
+    ap.add_argument("--ctx", type=int, default=0,
+                    help="context length for the single-sequence moe_* decode workloads (default: their own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--unfused", action="store_true",
@@ -516,7 +531,7 @@ def main():
     if args.workload in ("iso3_extend", "int8_extend"):
         return bench_extend(args)
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
-    w = make_workload(args.workload)
+    w = make_workload(args.workload, args.ctx)
     cb_k, ns_k = kvq.cell_bytes(w.fmt_k, w.head_dim)
     cb_v, ns_v = kvq.cell_bytes(w.fmt_v, w.head_dim)
     cache_bytes = w.num_pages * w.n_kv_heads * 16 * ((cb_k + 2 * ns_k) + (cb_v + 2 * ns_v))

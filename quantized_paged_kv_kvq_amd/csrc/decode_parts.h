@@ -29,6 +29,14 @@ __device__ __forceinline__ f16x4 codes_to_f16x4(uint32_t w) {
   return f16x4{p0[0], p0[1], p1[0], p1[1]};
 }
 
+// 4 q4_0 codes (code e, 0..15, in byte e) -> 4 exact fp16 values code - 8.
+__device__ __forceinline__ f16x4 nibbles_to_f16x4(uint32_t nib) {
+  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};              // 0x64nn reads 1024 + nn
+  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, nib, 0x05010400u)) - off;
+  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, nib, 0x05030402u)) - off;
+  return f16x4{p0[0], p0[1], p1[0], p1[1]};
+}
+
 // 4 int8 codes -> bf16 (code + 128), exact (integers below 256 have 8 significant bits).
 __device__ __forceinline__ s16x4 codes_to_bf16_biased(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;

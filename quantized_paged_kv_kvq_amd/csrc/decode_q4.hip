@@ -17,10 +17,13 @@
 //     a power of two in fp16 hi + lo parts; each group's accumulator is weighted by its (token,
 //     group) d in fp32.
 //   * Online softmax in base 2 with a lazily moved reference max (as the other decode kernels).
-//   * PV: O^T[d][row] on v_mfma_f32_16x16x16bf16_1k, as the k8v4 kernel: the A operand is 4 tokens'
-//     4-bit codes at one head_dim row as bf16 (128 + code), the B operand the weights times the
-//     token's V d split into bf16 hi and lo parts; the code offset comes off at the end through the
-//     per-group weight sums.
+//   * PV: O^T[d][row] on v_mfma_f32_16x16x16f16: the A operand is 4 tokens' 4-bit codes at one
+//     head_dim row as the exact fp16 values code - 8 (a byte permute into 0x64xx and one packed
+//     subtract), the B operand the weights times the token's V d in fp16 hi and lo parts (22
+//     significant bits).  Every weight carries the wave's factor 2^kexp, from the largest V d of its
+//     pages (scanned before the page stream), which keeps weight times d below 2^15 (no fp16
+//     overflow, small weights clear of the subnormals); the partial records the reference max
+//     minus kexp.
 //   * The waves merge through LDS (wave 0 takes whole rows), the partial is rotated back by H and
 //     goes to the log-sum-exp combine shared with the other decode kernels.
 #include "kvq_internal.h"
@@ -36,9 +39,10 @@ constexpr int kTiles = 16;                      // PV tiles of 16 head_dim rows
 constexpr float kLazyQ4 = 8.0f;                 // weights stay below 2^8 between rescalings
 
 // Launch shapes: waves per workgroup, pages per wave per split, pages each wave keeps in flight,
-// waves per SIMD the registers allow.
+// and the occupancy hint of the launch bounds.  An 8-wave workgroup takes about 150 KB of LDS for its
+// merge, so one fits a CU (two waves per SIMD).
 struct Q4Shape { int nw, ppw, pd, occ; };
-constexpr Q4Shape kQ4Shapes[] = {{4, 16, 1, 1}, {4, 8, 1, 1}};
+constexpr Q4Shape kQ4Shapes[] = {{4, 16, 1, 1}, {8, 8, 1, 1}, {8, 4, 1, 1}};
 constexpr int kNumQ4Shapes = (int)(sizeof(kQ4Shapes) / sizeof(kQ4Shapes[0]));
 
 // KVQ_Q4_DECODE_SHAPE overrides the choice (for tuning); -1 when unset
@@ -108,8 +112,8 @@ __device__ __forceinline__ f16x8 k_group_f16(uint32_t x) {
 // in LDS, [group][part][lane] (one part with DUP: hi or lo by column).
 template <bool DUP>
 __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, bool lo_col, int Lrow,
-                                             const f16x8* qb, float qmul, float& m_run, float& l_run,
-                                             float (&ls)[kGroups], f32x4 (&O)[kTiles]) {
+                                             const f16x8* qb, float qmul, float kexp, float& m_run, float& l_run,
+                                             f32x4 (&O)[kTiles]) {
   constexpr int NP = DUP ? 1 : 2;
   // ---- QK: per group, S^T[token 4w + k][column]; weighted by the group's d
   float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -135,37 +139,35 @@ __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, boo
   const bool rescale = move && m_run != kNegInf;
   const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
   m_run = m_new;
+  // the weights carry the wave's factor 2^kexp (l and O with them; the partial's m is m_run - kexp)
+  const float m_w = m_use - kexp;
   float pk[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_use);
+  for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_w);
   l_run = l_run * alpha + ((pk[0] + pk[1]) + (pk[2] + pk[3]));
   if (__any(rescale)) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) O[t] *= alpha;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) ls[g] *= alpha;
   }
-  // ---- PV per V group g: tiles 2g (even head_dim) and 2g + 1 (odd); masked tokens have pk == 0
+  // ---- PV per V group g: tiles 2g (even head_dim) and 2g + 1 (odd); masked tokens have pk == 0 (the
+  // d of cells past a sequence's length are finite by contract: zero-initialised slabs)
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
-    float pw[4];
+    f16x4 bpart, blo;                                      // DUP: hi or lo part by column
 #pragma unroll
-    for (int k = 0; k < 4; ++k) pw[k] = pk[k] * pb.vd(k, g);
-    s16x4 bpart, blo;
-    float used[4], used_lo[4];
-    split_bf16_select(pw, lo_col ? 0xffffffffu : 0u, bpart, used);            // DUP: hi or lo by column
-    ls[g] += (used[0] + used[1]) + (used[2] + used[3]);
-    if constexpr (!DUP) {
-      split_bf16_select(pw, 0xffffffffu, blo, used_lo);                       // the lo part as well
-      ls[g] += (used_lo[0] + used_lo[1]) + (used_lo[2] + used_lo[3]);
+    for (int k = 0; k < 4; ++k) {
+      const float pw = pk[k] * pb.vd(k, g);
+      const _Float16 hi = (_Float16)pw, lo = (_Float16)(pw - (float)hi);
+      bpart[k] = (DUP && lo_col) ? lo : hi;
+      blo[k] = lo;
     }
     const uint32_t wv = word_of(pb.v[g >> 2], g & 3);      // byte k: token 4w + k; nibbles: dims 32g + 2t (+1)
-    const s16x4 alo = nibbles_to_bf16_biased(wv & 0x0f0f0f0fu), ahi = nibbles_to_bf16_biased((wv >> 4) & 0x0f0f0f0fu);
-    O[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bpart, O[2 * g], 0, 0, 0);
-    O[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bpart, O[2 * g + 1], 0, 0, 0);
+    const f16x4 alo = nibbles_to_f16x4(wv & 0x0f0f0f0fu), ahi = nibbles_to_f16x4((wv >> 4) & 0x0f0f0f0fu);
+    O[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bpart, O[2 * g], 0, 0, 0);
+    O[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bpart, O[2 * g + 1], 0, 0, 0);
     if constexpr (!DUP) {
-      O[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, O[2 * g], 0, 0, 0);
-      O[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, O[2 * g + 1], 0, 0, 0);
+      O[2 * g] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, O[2 * g], 0, 0, 0);
+      O[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, blo, O[2 * g + 1], 0, 0, 0);
     }
   }
 }
@@ -204,21 +206,32 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
   const int seq_len = clampi(a.seq_lens[b], 0, cap);
   const int Lrow = valid ? (a.q_lens ? clampi(a.q_lens[(size_t)b * a.n_q + tq], 0, cap) : seq_len) : 0;
 
-  // ---- q first, then this wave's first PD pages (vector-memory waits are in issue order)
+  // ---- the wave's page ids (lane l: the wave's page l, clamped to the split and the table; the page
+  // loop takes them with lane reads), q, the V d of the wave's pages, then its first PD pages
+  // (vector-memory waits are in issue order)
   const int* bt_row = a.bt + (size_t)b * a.max_pages;
   const int p_begin = split * a.pages_per_split;
   const int p0 = p_begin + wv;
   const int p_cap = min(p_begin + a.pages_per_split, a.max_pages) - 1;
+  const int my_ids = clampi(bt_row[min(p0 + min(lane, PPW - 1) * NW, p_cap)], 0, a.num_pages - 1);
+  auto page_id = [&](int i) -> int { return __builtin_amdgcn_readlane(my_ids, i); };   // i uniform
   uint4 qraw[kGroups];                              // q[row][32G + 8w .. +7]
   {
     const uint16_t* qp = a.q + ((size_t)(b * a.n_q + tq) * a.n_q_heads + hq) * kD + 8 * w;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) qraw[g] = *reinterpret_cast<const uint4*>(qp + 32 * g);
   }
+  uint4 vscan[4];                                   // lane l: V d of tokens 4(l & 3) .. + 3 of page l / 4
+  {
+    const int pid = __shfl(my_ids, min(lane >> 2, PPW - 1));
+    const uint4* src =
+        reinterpret_cast<const uint4*>(a.v_scales + ((size_t)pid * a.hkv + kvh) * KVQ_PAGE_SIZE * kGroups) + 4 * (lane & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vscan[i] = src[i];
+  }
   Q4Page buf[PD + 1];
 #pragma unroll
-  for (int i = 0; i < PD && i < PPW; ++i)
-    load_q4_page(buf[i], a, clampi(bt_row[min(p0 + i * NW, p_cap)], 0, a.num_pages - 1), kvh, lane);
+  for (int i = 0; i < PD && i < PPW; ++i) load_q4_page(buf[i], a, page_id(i), kvh, lane);
 
   int Lmax = 0;
   for (int t = 0; t < a.n_q; ++t)
@@ -314,14 +327,32 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
       }
     qmul_lds[lane] = ldexpf(a.scale_log2, -ex);
   }
+  // The weights' factor 2^kexp, from the largest V d of the wave's visible pages: with weights below
+  // 2^8 (lazy rescaling) and d < 2^(E - 14) (E: d's fp16 exponent field), 2^(21 - E) keeps every
+  // weight times d below 2^15, where its fp16 hi and lo parts are exact to 22 bits, and small weights
+  // stay clear of the fp16 subnormals.
+  float kexp;
+  {
+    const int n_w = p0 < p_end ? (p_end - 1 - p0) / NW + 1 : 0;
+    uint32_t mx = 0;
+    if ((lane >> 2) < n_w) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wd[4] = {vscan[i].x, vscan[i].y, vscan[i].z, vscan[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = max(mx, max(wd[e] & 0x7fffu, (wd[e] >> 16) & 0x7fffu));
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    kexp = (float)(21 - clampi((int)(mx >> 10), 1, 31));
+  }
   __syncthreads();
   const float qmul = qmul_lds[lane];
   const f16x8* qb = qlds + lane;
 
-  float m_run = kNegInf, l_run = 0.0f, ls[kGroups];
+  float m_run = kNegInf, l_run = 0.0f;
   f32x4 O[kTiles];
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) ls[g] = 0.0f;
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) O[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -330,23 +361,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_q4(const DecodeArgs a) 
   // covers exactly the page about to be processed.  Prefetches past the wave's last page re-read it.
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;
-    const int p_last = p0 + (n_mine - 1) * NW;
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       const int pc = p0 + i * NW;
-      if (i + PD < PPW)
-        load_q4_page(buf[(i + PD) % (PD + 1)], a, clampi(bt_row[min(pc + PD * NW, p_last)], 0, a.num_pages - 1),
-                     kvh, lane);
-      q4_page_step<DUP>(buf[i % (PD + 1)], pc, w, lo_col, Lrow, qb, qmul, m_run, l_run, ls, O);
+      if (i + PD < PPW) load_q4_page(buf[(i + PD) % (PD + 1)], a, page_id(min(i + PD, n_mine - 1)), kvh, lane);
+      q4_page_step<DUP>(buf[i % (PD + 1)], pc, w, lo_col, Lrow, qb, qmul, kexp, m_run, l_run, O);
       if (i + 1 >= n_mine) break;
     }
   }
-  // ---- per-wave totals; remove the V operand's offset (128 + 8) through the group weight sums
+  // ---- per-wave totals: row sums over the 4 lane groups; the reference of l and O is m_run - kexp
   l_run = sum_over_row_lanes(l_run);
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) ls[g] = sum_over_row_lanes(ls[g]);
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t) O[t] -= 136.0f * ls[t >> 1];
+  if (m_run != kNegInf) m_run -= kexp;
 
   // ---- merge the NW waves: every wave stores (m, l, O) in LDS; wave 0 merges whole rows (the
   // back-rotation needs them)
@@ -437,11 +462,16 @@ DecodePlan plan_decode_q4(int hkv, int batch, int max_pages, int max_rows) {
     const int pps = kQ4Shapes[sh].nw * kQ4Shapes[sh].ppw;
     return (max_pages + pps - 1) / pps;
   };
-  // 64-page splits unless they would put at most one workgroup on each CU; then 32-page splits (the
-  // kernel's registers allow two waves per SIMD, so two workgroups share a CU: 40.5 -> 39.3 us for one
-  // 131,072-token sequence over two KV heads)
+  // More 64-page splits than CUs: 4-wave workgroups (two share a CU).  Otherwise one 8-wave workgroup
+  // per CU, each wave with half the pages: 64-page splits while they fill more than half of the CUs,
+  // else 32-page splits.  Measured launches for one sequence over two KV heads (4x16 / 4x8 / 8x8 /
+  // 8x4 waves x pages): 131,072 tokens 37.8 / 39.8 / 35.5 / 48.8 us; 65,536 tokens 37.0 / 26.9 / 34.3
+  // / 26.4 us; 32,768 tokens 36.6 / 26.3 / 33.8 / 25.8 us.
   p.shape = q4_shape_override();
-  if (p.shape < 0) p.shape = ((long)splits_of(0) * hkv * batch <= (long)device_cu_count()) ? 1 : 0;
+  if (p.shape < 0) {
+    const long n64 = (long)splits_of(0) * hkv * batch, cus = device_cu_count();
+    p.shape = n64 > cus ? 0 : (2 * n64 > cus ? 1 : 2);
+  }
   p.waves = kQ4Shapes[p.shape].nw;
   p.pages_per_split = kQ4Shapes[p.shape].nw * kQ4Shapes[p.shape].ppw;
   p.n_splits = splits_of(p.shape);

@@ -170,10 +170,12 @@ def test_decode_workspace_size_formula():
         assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 4, 16, None) == 2 * 128 * 32 * (256 + 2) * 4
         assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 5, 16, None) == 0
     q4 = make_cache(fk=2, fv=2)
-    # q4_0: the same rule as ISO3 / ISO4 (32-page splits at one workgroup per CU or fewer)
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 1, 16, None) == 2 * 256 * 8 * (256 + 2) * 4
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 2, 16, None) == 2 * 256 * 16 * (256 + 2) * 4
+    # q4_0: 64-page splits while they fill more than half of the CUs, else 32-page splits
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 2, 16, None) == 2 * 128 * 16 * (256 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 2, 8192, 1, 16, None) == 2 * 2 * 128 * 8 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 4096, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 2048, 1, 16, None) == 2 * 64 * 8 * (256 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 3, 16, None) == 0
 
 
