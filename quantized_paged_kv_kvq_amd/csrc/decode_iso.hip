@@ -64,7 +64,7 @@ constexpr int kNonTemporal = 2;                 // streaming loads: each cell is
 // at 4 waves per SIMD beat 4, 6 or 8 pages at 2-3 waves per SIMD (the kernel is bound by its VALU
 // work per page, not by memory latency).
 struct IsoShape { int nw, ppw, pd, occ; };
-constexpr IsoShape kIsoShapes[] = {{4, 16, 2, 2}, {4, 8, 1, 2}};
+constexpr IsoShape kIsoShapes[] = {{4, 16, 2, 2}, {8, 8, 1, 2}, {8, 4, 1, 2}};
 constexpr int kNumIsoShapes = (int)(sizeof(kIsoShapes) / sizeof(kIsoShapes[0]));
 
 // KVQ_ISO3_DECODE_SHAPE overrides the choice (for tuning); -1 when unset
@@ -547,14 +547,20 @@ DecodePlan plan_decode_iso(int head_dim, int hkv, int batch, int max_pages, int 
   p.rows = max_rows;
   p.row_groups = max(1, (max_rows + 7) / 8);        // partial rows: 8 (one MFMA half) or 16
   p.row_tiles = 0;
-  // 64-page splits unless they would give at most one workgroup per CU; then 32-page splits, two
-  // waves per SIMD (measured on one sequence at 131,072 tokens, 2 KV heads: 6% faster launches)
+  // More 64-page splits than CUs: 4-wave workgroups (two share a CU).  Otherwise one 8-wave workgroup
+  // per CU (two waves per SIMD), each wave with half the pages: 64-page splits while they fill more
+  // than half of the CUs, else 32-page splits.  Measured ISO3 launches for one sequence over two KV
+  // heads at head_dim 256 (4x16 / 4x8 / 8x8 / 8x4 waves x pages): 131,072 tokens 33.6 / 31.3 / 30.1 /
+  // 38.9 us; 65,536 tokens 32.3 / 22.2 / 28.3 / 21.5 us; 32,768 tokens 31.8 / 21.3 / 27.6 / 20.5 us.
   auto splits_of = [&](int sh) {
     const int pps = kIsoShapes[sh].nw * kIsoShapes[sh].ppw;
     return (max_pages + pps - 1) / pps;
   };
   p.shape = iso_shape_override();
-  if (p.shape < 0) p.shape = ((long)splits_of(0) * hkv * batch <= (long)device_cu_count()) ? 1 : 0;
+  if (p.shape < 0) {
+    const long n64 = (long)splits_of(0) * hkv * batch, cus = device_cu_count();
+    p.shape = n64 > cus ? 0 : (2 * n64 > cus ? 1 : 2);
+  }
   p.waves = kIsoShapes[p.shape].nw;
   p.pages_per_split = kIsoShapes[p.shape].nw * kIsoShapes[p.shape].ppw;
   p.n_splits = splits_of(p.shape);

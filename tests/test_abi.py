@@ -106,8 +106,11 @@ def test_decode_validation_iso4():
     assert decode(make_cache(fk=5, fv=5, D=128), make_pages(), ws=None) == 4  # valid up to the workspace
     L = kvq.lib()
     c = make_cache(fk=5, fv=5, D=128)
-    # one sequence, 2 KV heads: 128 splits of 64 pages would give one workgroup per CU -> 256 of 32
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 1, 16, None) == 2 * 256 * 8 * (128 + 2) * 4
+    # one sequence, 2 KV heads: 128 splits of 64 pages fill the CUs once (one 8-wave workgroup each)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (128 + 2) * 4
+    # 64 splits of 64 pages would fill half of them -> 128 of 32
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 4096, 1, 16, None) == 2 * 128 * 8 * (128 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 2048, 1, 16, None) == 2 * 64 * 8 * (128 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 4, 8192, 1, 16, None) == 4 * 2 * 128 * 8 * (128 + 2) * 4
 
 
@@ -158,9 +161,9 @@ def test_decode_workspace_size_formula():
     assert n == 2 * 128 * 8 * (256 + 2) * 4           # 2 KV heads x 128 splits x 8 rows x (D + m, l) fp32
     assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 5, 16, None) == 0
     iso = make_cache(fk=3, fv=3, D=128)
-    # ISO3 / ISO4: 32-page splits when 64-page splits would give at most one workgroup per CU
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 1, 16, None) == 2 * 256 * 8 * (128 + 2) * 4
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 2, 16, None) == 2 * 256 * 16 * (128 + 2) * 4
+    # ISO3 / ISO4 (like q4_0): 64-page splits while they fill more than half of the CUs
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (128 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 2, 16, None) == 2 * 128 * 16 * (128 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 2, 8192, 1, 16, None) == 2 * 2 * 128 * 8 * (128 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(iso), 1, 8192, 3, 16, None) == 0
     for fk, fv in ((1, 4), (4, 1), (4, 4)):
@@ -170,7 +173,7 @@ def test_decode_workspace_size_formula():
         assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 4, 16, None) == 2 * 128 * 32 * (256 + 2) * 4
         assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 5, 16, None) == 0
     q4 = make_cache(fk=2, fv=2)
-    # q4_0: 64-page splits while they fill more than half of the CUs, else 32-page splits
+    # q4_0 the same
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 2, 16, None) == 2 * 128 * 16 * (256 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 2, 8192, 1, 16, None) == 2 * 2 * 128 * 8 * (256 + 2) * 4
