@@ -925,6 +925,16 @@ DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_page
   p.waves = sh.nw;
   p.pages_per_split = sh.nw * sh.ppw;
   p.n_splits = splits_of(p.shape);
+  if (p.row_tiles && shape_override() < 0) {
+    // the verify kernel (one 8-wave workgroup per CU): the fewest pages per split, a multiple of its 4
+    // wave pairs and at most 64, that keeps the workgroups within one round of the CUs, so every CU
+    // works and each takes fewer pages (118,750 tokens: 116 splits of 64 pages on 232 CUs ->
+    // 124 of 60 on 248)
+    const long per = max(1L, (long)device_cu_count() / ((long)hkv * batch));
+    const long need = (max_pages + per - 1) / per;
+    p.pages_per_split = (int)min(64L, max(4L, (need + 3) / 4 * 4));
+    p.n_splits = (max_pages + p.pages_per_split - 1) / p.pages_per_split;
+  }
   p.part_bytes = (size_t)batch * hkv * p.n_splits * (8 * p.row_groups) * (head_dim + 2) * sizeof(float);
   return p;
 }

@@ -634,16 +634,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
 // Pages per pair of a split: 16 with 64-page splits, 8 with 32-page splits.
 hipError_t launch_decode_verify(int row_tiles, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)plan.n_splits, a.hkv, a.batch), block(kWaves * 64);
+  // pages per wave pair: the kernel's loop takes up to PPP (8 or 16) and exits after the pair's last
   const int ppp = plan.pages_per_split / kPairs;
-  if (ppp * kPairs != plan.pages_per_split) return hipErrorInvalidValue;
+  if (ppp * kPairs != plan.pages_per_split || ppp < 1 || ppp > 16) return hipErrorInvalidValue;
   if (row_tiles == 2) {
-    if (ppp == 16) k_verify_k8v4<2, 16><<<grid, block, 0, s>>>(a);
-    else if (ppp == 8) k_verify_k8v4<2, 8><<<grid, block, 0, s>>>(a);
-    else return hipErrorInvalidValue;
+    if (ppp > 8) k_verify_k8v4<2, 16><<<grid, block, 0, s>>>(a);
+    else k_verify_k8v4<2, 8><<<grid, block, 0, s>>>(a);
   } else if (row_tiles == 1) {
-    if (ppp == 16) k_verify_k8v4<1, 16><<<grid, block, 0, s>>>(a);
-    else if (ppp == 8) k_verify_k8v4<1, 8><<<grid, block, 0, s>>>(a);
-    else return hipErrorInvalidValue;
+    if (ppp > 8) k_verify_k8v4<1, 16><<<grid, block, 0, s>>>(a);
+    else k_verify_k8v4<1, 8><<<grid, block, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }

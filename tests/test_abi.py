@@ -172,6 +172,13 @@ def test_decode_workspace_size_formula():
         assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 3, 16, None) == 2 * 128 * 24 * (256 + 2) * 4
         assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 4, 16, None) == 2 * 128 * 32 * (256 + 2) * 4
         assert L.kvq_decode_workspace_bytes(ctypes.byref(f), 1, 8192, 5, 16, None) == 0
+    # k8v4 verify (24 rows: the wave-pair kernel): the fewest pages per split (a multiple of 4, at most
+    # 64) that keeps 2 KV heads within 256 workgroups
+    k8v4 = make_cache(fk=1, fv=2)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(k8v4), 1, 7422, 3, 16, None) == 2 * 124 * 24 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(k8v4), 1, 8192, 3, 16, None) == 2 * 128 * 24 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(k8v4), 1, 2000, 3, 16, None) == 2 * 125 * 24 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(k8v4), 1, 20000, 3, 16, None) == 2 * 313 * 24 * (256 + 2) * 4
     q4 = make_cache(fk=2, fv=2)
     # q4_0 the same
     assert L.kvq_decode_workspace_bytes(ctypes.byref(q4), 1, 8192, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
