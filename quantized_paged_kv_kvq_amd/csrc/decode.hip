@@ -925,6 +925,18 @@ DecodePlan plan_decode(int v_fmt, int head_dim, int hkv, int batch, int max_page
   p.waves = sh.nw;
   p.pages_per_split = sh.nw * sh.ppw;
   p.n_splits = splits_of(p.shape);
+  if (!p.row_tiles && shape_override() < 0 && p.shape == 1) {
+    // 64-page splits fill at most about half of the CUs: the fewest pages per split (a multiple of the
+    // 4 waves, at most 32) that keeps one round, so more CUs work and each takes fewer pages (40,000
+    // tokens: 125 splits of 20 pages, 17.5 us, against 79 of 32, 18.6 us).  At 78-90% of the CUs the
+    // same rule does not pay: the kernel is bound by HBM there (100,000 tokens 28.3 vs 27.8 us).
+    const long per = (long)device_cu_count() / ((long)hkv * batch * p.row_groups);
+    if (per >= 1) {
+      const long need = (max_pages + per - 1) / per;
+      p.pages_per_split = (int)min(32L, max(4L, (need + 3) / 4 * 4));
+      p.n_splits = (max_pages + p.pages_per_split - 1) / p.pages_per_split;
+    }
+  }
   if (p.row_tiles && shape_override() < 0) {
     // the verify kernel (one 8-wave workgroup per CU): the fewest pages per split, a multiple of its 4
     // wave pairs and at most 64, that keeps the workgroups within one round of the CUs, so every CU

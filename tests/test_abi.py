@@ -159,6 +159,11 @@ def test_decode_workspace_size_formula():
     c = make_cache()
     n = L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 1, 16, None)
     assert n == 2 * 128 * 8 * (256 + 2) * 4           # 2 KV heads x 128 splits x 8 rows x (D + m, l) fp32
+    # 64-page splits fill at most about half of the CUs: the fewest pages per split (a multiple of 4, at
+    # most 32) keeping one round (2,500 pages: 125 splits of 20); above that 64-page splits stay
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 2500, 1, 16, None) == 2 * 125 * 8 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 4096, 1, 16, None) == 2 * 128 * 8 * (256 + 2) * 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 7422, 1, 16, None) == 2 * 116 * 8 * (256 + 2) * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(c), 1, 8192, 5, 16, None) == 0
     iso = make_cache(fk=3, fv=3, D=128)
     # ISO3 / ISO4 (like q4_0): 64-page splits while they fill more than half of the CUs
