@@ -63,8 +63,8 @@ constexpr int kNonTemporal = 2;                 // streaming loads: each cell is
 // the registers allow.  Measured on 32 sequences of 4K-32K tokens (head_dim 128): 2 pages in flight
 // at 4 waves per SIMD beat 4, 6 or 8 pages at 2-3 waves per SIMD (the kernel is bound by its VALU
 // work per page, not by memory latency).
-struct IsoShape { int nw, ppw, pd, occ; };
-constexpr IsoShape kIsoShapes[] = {{4, 16, 2, 2}, {8, 8, 1, 2}, {8, 4, 1, 2}};
+struct IsoShape { int nw, ppw, pd, occ, pps; };   // pps: pages per split (the waves take pages w, w + nw, ...)
+constexpr IsoShape kIsoShapes[] = {{4, 16, 2, 2, 64}, {8, 8, 1, 2, 64}, {8, 4, 1, 2, 32}};
 constexpr int kNumIsoShapes = (int)(sizeof(kIsoShapes) / sizeof(kIsoShapes[0]));
 
 // KVQ_ISO3_DECODE_SHAPE overrides the choice (for tuning); -1 when unset
@@ -179,7 +179,7 @@ __device__ __forceinline__ void split_f16(const float x[4], f16x4& hi, f16x4& lo
 // One page of one wave: QK on MFMA, online softmax, PV on MFMA.
 template <int BITS, int D, bool DUP>
 __device__ __forceinline__ void iso_page_step(const IsoPage<BITS, D / 128>& pb, int p, int g, bool lo_col, int Lrow,
-                                              const f16x8 (&qb)[D / 128][4][DUP ? 1 : 2], float qmul, int v_shift,
+                                              const f16x8* qb, float qmul, int v_shift,
                                               const uint32_t* lut, float& m_run, float& l_run, f32x4 (&O)[D / 16]) {
   constexpr int NB = D / 128;
   // ---- QK: S^T[token 4g + k][row] per block
@@ -204,8 +204,10 @@ __device__ __forceinline__ void iso_page_step(const IsoPage<BITS, D / 128>& pb, 
       const u32x4 pairs = {lut[x[c] & PM], lut[(x[c] >> PB) & PM], lut[(x[c] >> (2 * PB)) & PM],
                            lut[(x[c] >> (3 * PB)) & PM]};
       const f16x8 av = __builtin_bit_cast(f16x8, pairs);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[b][c][0], acc[b], 0, 0, 0);
-      if constexpr (!DUP) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[b][c][1], acc[b], 0, 0, 0);
+      constexpr int NP = DUP ? 1 : 2;
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[((b * 4 + c) * NP) * 64], acc[b], 0, 0, 0);
+      if constexpr (!DUP)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[((b * 4 + c) * NP + 1) * 64], acc[b], 0, 0, 0);
     }
     if constexpr (DUP) {          // columns r (hi part of q) and r + 8 (lo part): both get the sum
 #pragma unroll
@@ -292,10 +294,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a)
   constexpr int NL = 1 << (2 * BITS);               // pair-table entries
   // one LDS allocation with the pair table at its start: table addresses then fit the 16-bit offset
   // of the LDS loads, so a lookup's address is the shifted, masked code pair alone (two separate
-  // arrays put the table after the merge buffers, past that range, with one more add per lookup)
-  __shared__ __align__(16) uint32_t lds[NL + NW * (NT * 64 * 4 + 2 * 64)];
+  // arrays put the table after the merge buffers, past that range, with one more add per lookup).
+  // Then the query fragments (B operands of QK, [block][group][part][lane], written by wave 0) and
+  // each row's score multiplier, then the merge buffers (half of the tiles at a time).
+  constexpr int NP = DUP ? 1 : 2;
+  constexpr int kQWords = NB * 4 * NP * 64 * 4;
+  __shared__ __align__(16) uint32_t lds[NL + kQWords + 64 + NW * ((NT / 2) * 64 * 4 + 2 * 64)];
   uint32_t* const lut = lds;
-  float* const mrg = reinterpret_cast<float*>(lds + NL);
+  f16x8* const qlds = reinterpret_cast<f16x8*>(lds + NL);
+  float* const qmul_lds = reinterpret_cast<float*>(lds + NL + kQWords);
+  float* const mrg = reinterpret_cast<float*>(lds + NL + kQWords + 64);
 
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
@@ -380,9 +388,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a)
   // ---- B operands of QK: r (x) q per 4-value group, times 2^ex (max |.| of the row in
   // [2^14, 2^15)), as fp16 hi + lo parts
   const float quat[4] = {a.quat[0], a.quat[1], a.quat[2], a.quat[3]};
-  f16x8 qb[NB][4][DUP ? 1 : 2];
-  float qmul;
-  {
+  if (wv == 0) {
     float qr[NB][32];
     float mx = 0.0f;
 #pragma unroll
@@ -415,13 +421,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a)
           const float x = ldexpf(qr[bb][8 * c + j], ex);
           const _Float16 hi = (_Float16)x, lo = (_Float16)(x - (float)hi);
           if constexpr (DUP) {
-            qb[bb][c][0][j] = lo_col ? lo : hi;
+            qlds[((bb * 4 + c) * NP) * 64 + lane][j] = lo_col ? lo : hi;
           } else {
-            qb[bb][c][0][j] = hi;
-            qb[bb][c][1][j] = lo;
+            qlds[((bb * 4 + c) * NP) * 64 + lane][j] = hi;
+            qlds[((bb * 4 + c) * NP + 1) * 64 + lane][j] = lo;
           }
         }
-    qmul = ldexpf(a.scale_log2 * (1.0f / kLevelScale<BITS>), -ex);
+    qmul_lds[lane] = ldexpf(a.scale_log2 * (1.0f / kLevelScale<BITS>), -ex);
   }
 
   float m_run = kNegInf, l_run = 0.0f;
@@ -433,7 +439,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a)
   // of the one it processes, in a ring of PD + 1 register buffers; the loop is fully unrolled so
   // every wait on the vector memory counter covers exactly the page about to be processed.
   // Prefetches past the wave's last page re-read that page.
-  __syncthreads();                                  // the pair table
+  __syncthreads();                                  // the pair table, the query fragments
+  const float qmul = qmul_lds[lane];
+  const f16x8* const qb = qlds + lane;
   if (p0 < p_end) {
     const int n_mine = (p_end - 1 - p0) / NW + 1;
     const int p_last = p0 + (n_mine - 1) * NW;
@@ -449,64 +457,74 @@ __global__ __launch_bounds__(NW * 64, OCC) void k_decode_iso(const DecodeArgs a)
   }
   l_run = sum_over_row_lanes(l_run);
 
-  // ---- merge the NW waves: each stores (m, l, O) in LDS, then wave w merges the tile groups
-  // w, w + NW, ... (4 tiles = 4 consecutive head_dim of every lane: whole rotation groups)
-  float* lds_o = mrg;                               // [wave][tile][lane] x f32x4
-  float* lds_ml = mrg + NW * NT * 64 * 4;           // [wave][m | l][lane]
-#pragma unroll
-  for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(lds_o + ((wv * NT + t) * 64 + lane) * 4) = O[t];
+  // ---- merge the NW waves, half of the tiles at a time: each stores (m, l) and its half of O in LDS,
+  // then wave w merges the tile groups w, w + NW, ... of the half (4 tiles = 4 consecutive head_dim of
+  // every lane: whole rotation groups)
+  constexpr int NTH = NT / 2, NTGH = NTG / 2;        // tiles, tile groups per half
+  static_assert(NTH % 4 == 0, "whole tile groups per half");
+  float* lds_o = mrg;                               // [wave][tile of the half][lane] x f32x4
+  float* lds_ml = mrg + NW * NTH * 64 * 4;          // [wave][m | l][lane]
   lds_ml[(wv * 2 + 0) * 64 + lane] = m_run;
   lds_ml[(wv * 2 + 1) * 64 + lane] = l_run;
-  __syncthreads();
-  float cv[NW];
-  float M = kNegInf;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    cv[v] = lds_ml[(v * 2 + 0) * 64 + lane];
-    M = fmaxf(M, cv[v]);
-  }
-  const float Mu = M == kNegInf ? 0.0f : M;
-  float l = 0.0f;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    cv[v] = __builtin_amdgcn_exp2f(cv[v] - Mu);
-    l += cv[v] * lds_ml[(v * 2 + 1) * 64 + lane];
-  }
   const bool writer = valid && !lo_col;
   // with a single split the workgroup writes the normalised output itself (no combine follows)
   const bool direct = a.n_splits == 1;
-  const float sc = direct ? (l > 0.0f ? 512.0f / l : 0.0f) : 512.0f;   // 512: the weights' 2^-9
-  if (!direct && wv == 0 && g == 0 && writer) {
-    float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
-    ml[0] = M; ml[1] = l;
-  }
   const float cq[4] = {quat[0], -quat[1], -quat[2], -quat[3]};
+  float cv[NW];
+  float M = kNegInf, l = 0.0f, sc = 0.0f;
 #pragma unroll
-  for (int tg = 0; tg < NTG; ++tg) {
-    if (tg % NW != wv) continue;
-    f32x4 o[4];
+  for (int hf = 0; hf < 2; ++hf) {
+    if (hf) __syncthreads();                        // the first half is merged
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NTH; ++t)
+      *reinterpret_cast<f32x4*>(lds_o + ((wv * NTH + t) * 64 + lane) * 4) = O[hf * NTH + t];
+    __syncthreads();
+    if (hf == 0) {
 #pragma unroll
-      for (int v = 0; v < NW; ++v) acc += cv[v] * *reinterpret_cast<const f32x4*>(lds_o + ((v * NT + 4 * tg + q) * 64 + lane) * 4);
-      if constexpr (DUP) {          // column r + 8 holds the lo-part sums of row r
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] += dpp_ror8(acc[k]);
+      for (int v = 0; v < NW; ++v) {
+        cv[v] = lds_ml[(v * 2 + 0) * 64 + lane];
+        M = fmaxf(M, cv[v]);
       }
-      o[q] = acc * sc;
-    }
-    // tile 4tg + q, element i: head_dim 128 * (tg / 2) + 32g + 8i + 4 * (tg % 2) + q
-    if (writer) {
-      float* row = (direct ? a.out + (size_t)((b * a.n_q + tq) * a.n_q_heads + hq) * D
-                           : part_o + ((row0 + r) * a.n_splits + split) * D) +
-                   128 * (tg >> 1) + 32 * g + 4 * (tg & 1);
+      const float Mu = M == kNegInf ? 0.0f : M;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float u[4] = {o[0][i], o[1][i], o[2][i], o[3][i]};
-        float y[4];
-        quat_mul(cq, u, y);
-        *reinterpret_cast<float4*>(row + 8 * i) = make_float4(y[0], y[1], y[2], y[3]);
+      for (int v = 0; v < NW; ++v) {
+        cv[v] = __builtin_amdgcn_exp2f(cv[v] - Mu);
+        l += cv[v] * lds_ml[(v * 2 + 1) * 64 + lane];
+      }
+      sc = direct ? (l > 0.0f ? 512.0f / l : 0.0f) : 512.0f;   // 512: the weights' 2^-9
+      if (!direct && wv == 0 && g == 0 && writer) {
+        float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
+        ml[0] = M; ml[1] = l;
+      }
+    }
+#pragma unroll
+    for (int tg = hf * NTGH; tg < (hf + 1) * NTGH; ++tg) {
+      if (tg % NW != wv) continue;
+      f32x4 o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const int th = 4 * (tg - hf * NTGH) + q;    // tile of the half
+#pragma unroll
+        for (int v = 0; v < NW; ++v) acc += cv[v] * *reinterpret_cast<const f32x4*>(lds_o + ((v * NTH + th) * 64 + lane) * 4);
+        if constexpr (DUP) {          // column r + 8 holds the lo-part sums of row r
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[k] += dpp_ror8(acc[k]);
+        }
+        o[q] = acc * sc;
+      }
+      // tile 4tg + q, element i: head_dim 128 * (tg / 2) + 32g + 8i + 4 * (tg % 2) + q
+      if (writer) {
+        float* row = (direct ? a.out + (size_t)((b * a.n_q + tq) * a.n_q_heads + hq) * D
+                             : part_o + ((row0 + r) * a.n_splits + split) * D) +
+                     128 * (tg >> 1) + 32 * g + 4 * (tg & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float u[4] = {o[0][i], o[1][i], o[2][i], o[3][i]};
+          float y[4];
+          quat_mul(cq, u, y);
+          *reinterpret_cast<float4*>(row + 8 * i) = make_float4(y[0], y[1], y[2], y[3]);
+        }
       }
     }
   }
@@ -553,7 +571,7 @@ DecodePlan plan_decode_iso(int head_dim, int hkv, int batch, int max_pages, int 
   // heads at head_dim 256 (4x16 / 4x8 / 8x8 / 8x4 waves x pages): 131,072 tokens 33.6 / 31.3 / 30.1 /
   // 38.9 us; 65,536 tokens 32.3 / 22.2 / 28.3 / 21.5 us; 32,768 tokens 31.8 / 21.3 / 27.6 / 20.5 us.
   auto splits_of = [&](int sh) {
-    const int pps = kIsoShapes[sh].nw * kIsoShapes[sh].ppw;
+    const int pps = kIsoShapes[sh].pps;
     return (max_pages + pps - 1) / pps;
   };
   p.shape = iso_shape_override();
@@ -562,7 +580,7 @@ DecodePlan plan_decode_iso(int head_dim, int hkv, int batch, int max_pages, int 
     p.shape = n64 > cus ? 0 : (2 * n64 > cus ? 1 : 2);
   }
   p.waves = kIsoShapes[p.shape].nw;
-  p.pages_per_split = kIsoShapes[p.shape].nw * kIsoShapes[p.shape].ppw;
+  p.pages_per_split = kIsoShapes[p.shape].pps;
   p.n_splits = splits_of(p.shape);
   p.part_bytes = (size_t)batch * hkv * p.n_splits * (8 * p.row_groups) * (head_dim + 2) * sizeof(float);
   return p;
