@@ -67,6 +67,15 @@ def test_iso3_verify_windows(n_q, hq, D):
                               n_q_heads=hq, n_kv_heads=2, head_dim=D))
 
 
+@pytest.mark.parametrize("L,D", [(20000, 256), (9000, 128)])
+def test_iso3_verify_window_eight_wave_shapes(L, D):
+    """16 rows (separate hi / lo MFMAs) over 8 KV heads in the 8-wave launch shapes: 20,000 tokens give
+    20 splits of 64 pages per KV head (160 workgroups: 64-page splits), 9,000 tokens 9 (72: 32-page
+    splits)."""
+    check(synth.ragged_decode("iso3", "iso3", [L], seed=68 + D, n_q=2, q_len_back=[1, 0], n_q_heads=64,
+                              n_kv_heads=8, head_dim=D))
+
+
 def test_iso3_decode_head_map_and_idle_kv_head():
     """An explicit head map with uneven groups; KV head 1 serves no query head."""
     w = synth.ragged_decode("iso3", "iso3", [33, 500], seed=64, n_q_heads=6, n_kv_heads=3, head_dim=128)

@@ -84,6 +84,13 @@ def test_iso4_verify_windows(n_q, hq, D):
                               n_q_heads=hq, n_kv_heads=2, head_dim=D))
 
 
+@pytest.mark.parametrize("L,D", [(20000, 128), (9000, 256)])
+def test_iso4_verify_window_eight_wave_shapes(L, D):
+    """16 rows over 8 KV heads in the 8-wave launch shapes (64-page and 32-page splits)."""
+    check(synth.ragged_decode("iso4", "iso4", [L], seed=97 + D, n_q=2, q_len_back=[1, 0], n_q_heads=64,
+                              n_kv_heads=8, head_dim=D))
+
+
 def test_iso4_decode_head_map_and_idle_kv_head():
     w = synth.ragged_decode("iso4", "iso4", [33, 500], seed=95, n_q_heads=6, n_kv_heads=3, head_dim=128)
     check(w, head_map=[2, 0, 2, 0, 2, 2])

@@ -65,6 +65,14 @@ def test_q4_verify_window(n_q, hq):
     check(q4([40, 17, 1000, 2049], 83 + n_q + hq, n_q=n_q, q_len_back=back, n_q_heads=hq, n_kv_heads=2))
 
 
+def test_q4_verify_window_eight_wave_shapes():
+    """16 rows (separate hi / lo MFMAs) over 8 KV heads in the 8-wave launch shapes: 20,000 tokens give
+    20 splits of 64 pages per KV head (160 workgroups, more than half of the CUs: 64-page splits),
+    9,000 tokens 9 (72: 32-page splits)."""
+    for L, seed in ((20000, 86), (9000, 87)):
+        check(q4([L], seed, n_q=2, q_len_back=[1, 0], n_q_heads=64, n_kv_heads=8))
+
+
 def test_q4_decode_head_map_and_idle_kv_heads():
     """Uneven groups through an explicit map; KV heads 1 and 3 (the last) serve no query head."""
     check(q4([33, 500], 84, n_q_heads=6, n_kv_heads=4), head_map=[2, 0, 2, 0, 2, 2])
