@@ -343,9 +343,11 @@ struct TileOps<bf16x8, NQ> {
 };
 
 // S^T for the tile's 64 keys (two 32-key blocks) against this wave's 32 rows over the head_dim steps
-// KS0 .. KS1 - 1 (16 values each); q is given as NQ parts (hi, lo) whose products accumulate.
-template <typename V8, int NQ, int KS0 = 0, int KS1 = 8, bool ACC = false>
-__device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, const V8 (&q)[NQ][8], f32x16 (&S)[2]) {
+// KS0 .. KS1 - 1 (16 values each); q is given as NQ parts (hi, lo) whose products accumulate.  Part
+// LP of steps KL .. 7 comes from LDS (q_lds[(ks - KL) * 64], this lane's copy) instead of registers.
+template <typename V8, int NQ, int KS0 = 0, int KS1 = 8, bool ACC = false, int KL = 8, int LP = NQ - 1>
+__device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, const V8 (&q)[NQ][8], f32x16 (&S)[2],
+                                        const V8* q_lds = nullptr) {
   using Ops = TileOps<V8, NQ>;
   if constexpr (!ACC) {
     S[0] = f32x16{};
@@ -366,16 +368,13 @@ __device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, cons
     // the scheduler would otherwise reuse one register set and wait for each read)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int part = 0; part < NQ; ++part)
+    for (int part = 0; part < NQ; ++part) {
+      const V8 qv = (part == LP && ks >= KL) ? q_lds[(ks - KL) * 64] : q[part][ks];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) S[kb] = Ops::mma(ka[cb][kb], q[part][ks], S[kb]);
+      for (int kb = 0; kb < 2; ++kb) S[kb] = Ops::mma(ka[cb][kb], qv, S[kb]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
-}
-
-template <typename V8, int NQ, int KS0, int KS1>
-__device__ __forceinline__ void qk_tile_acc(const uint8_t* buf, int l32, int h, const V8 (&q)[NQ][8], f32x16 (&S)[2]) {
-  qk_tile<V8, NQ, KS0, KS1, true>(buf, l32, h, q, S);
 }
 
 // O^T += V^T P^T for the tile: per 16-key step st, the weights' hi and lo parts (as MFMA B operands)
@@ -408,14 +407,16 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, int l32, int h, cons
 // Prefix tiles: rotated basis, fp16 MFMAs, per-key norms.
 struct PrefixTiles {
   using Weights = u32x4[1][4][2];
+  static constexpr int kQLoLds = 4;      // lo parts of head_dim steps 4 .. 7 sit in LDS (16 fewer registers)
   const ExtendArgs& a;
   int b, kvh, P;
   const f16x8 (&q)[2][8];
+  const f16x8* q_lds;                    // this lane's copies: [step - kQLoLds][64 lanes]
   float rs;
   __device__ __forceinline__ const uint8_t* image(int t) const { return prefix_image(a, b, kvh, t); }
   __device__ __forceinline__ bool active(int) const { return true; }
   __device__ __forceinline__ void qk(const uint8_t* buf, int l32, int h, f32x16 (&S)[2]) const {
-    qk_tile<f16x8, 2>(buf, l32, h, q, S);
+    qk_tile<f16x8, 2, 0, 8, false, kQLoLds>(buf, l32, h, q, S, q_lds);
   }
   // scores / rs of tile t into u (masked past the prefix), returns rs
   __device__ __forceinline__ float scores(const uint8_t* buf, int t, int h, const f32x16 (&S)[2], float (&u)[32]) const {
@@ -464,9 +465,11 @@ struct PrefixTiles {
 // group scale (QK), and per group the weights times the key's V group scale (PV); no rotation.
 struct PrefixTilesI8 {
   using Weights = u32x4[2][4][2];
+  static constexpr int kQLds = 4;        // the query's head_dim steps 4 .. 7 sit in LDS (16 fewer registers)
   const ExtendArgs& a;
   int b, kvh, P;
   const f16x8 (&q)[2][8];
+  const f16x8* q_lds;                    // this lane's copies: [step - kQLds][64 lanes]
   float rs;
   __device__ __forceinline__ const uint8_t* image(int t) const { return prefix_image(a, b, kvh, t); }
   __device__ __forceinline__ bool active(int) const { return true; }
@@ -487,7 +490,7 @@ struct PrefixTilesI8 {
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[i >> 4][(i & 15) + j] *= a0[j];
     }
-    qk_tile_acc<f16x8, 1, 4, 8>(buf, l32, h, qh, S);         // head_dim 64 .. 127, accumulated
+    qk_tile<f16x8, 1, 4, 8, true, kQLds, 0>(buf, l32, h, qh, S, q_lds);   // head_dim 64 .. 127, accumulated
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
       const int key = 16 * (i >> 3) + 8 * ((i >> 2) & 1) + 4 * h;
@@ -650,6 +653,10 @@ __device__ __forceinline__ void run_tiles(const Tiles& k, int n, uint8_t* ring, 
 template <bool I8>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_extend_attn(const ExtendArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[3 * kExtendTileBytes];
+  // each wave's query parts of the last head_dim steps, read by the prefix QK from LDS: ISO3 the lo
+  // parts of the rotated query, int8 the (single) query part
+  static_assert(PrefixTiles::kQLoLds == PrefixTilesI8::kQLds, "one LDS region for both prefix formats");
+  __shared__ __attribute__((aligned(16))) f16x8 q_lo[kWaves][8 - PrefixTiles::kQLoLds][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool group_b = wv >= kWaves / 2;
   const int l32 = lane & 31, h = lane >> 5;
@@ -722,10 +729,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_extend_attn(const ExtendArgs
       }
     }
     if constexpr (I8) {
-      const PrefixTilesI8 pk{a, b, kvh, P, qs, rs};
+#pragma unroll
+      for (int k = PrefixTilesI8::kQLds; k < 8; ++k) q_lo[wv][k - PrefixTilesI8::kQLds][lane] = qs[0][k];
+      const PrefixTilesI8 pk{a, b, kvh, P, qs, &q_lo[wv][0][lane], rs};
       run_tiles(pk, n_pt, ring, group_b, wv, lane, l32, h, m_run, l_run, O);
     } else {
-      const PrefixTiles pk{a, b, kvh, P, qs, rs};
+#pragma unroll
+      for (int k = PrefixTiles::kQLoLds; k < 8; ++k) q_lo[wv][k - PrefixTiles::kQLoLds][lane] = qs[1][k];
+      const PrefixTiles pk{a, b, kvh, P, qs, &q_lo[wv][0][lane], rs};
       run_tiles(pk, n_pt, ring, group_b, wv, lane, l32, h, m_run, l_run, O);
     }
     // back to the original basis: O[t][4g .. 4g+3] is head_dim 32t + 8g + 4h .. +3, one group
