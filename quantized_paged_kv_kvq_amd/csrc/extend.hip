@@ -54,6 +54,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kWaves = kExtendWaves;                       // attention workgroup: two groups of 4 waves
 constexpr int kKeys = 64;                                  // keys per tile
+constexpr int kQkDepth = 2;                                // QK operand reads in flight ahead of the MFMAs (steps)
 constexpr int kKRow = kD * 2 + 16;                         // K image row: one key, 256 B + 16 B pad
 constexpr int kVRow = kKeys * 2 + 16;                      // V image row: one head_dim, 128 B + 16 B pad
 constexpr int kImgK = kKeys * kKRow;                       // K image bytes: [key][d] fp16/bf16
@@ -353,25 +354,32 @@ __device__ __forceinline__ void qk_tile(const uint8_t* buf, int l32, int h, cons
     S[0] = f32x16{};
     S[1] = f32x16{};
   }
-  V8 ka[2][2];
+  // LDS operand reads run kQkDepth steps ahead of the MFMAs that use them, in a ring of kQkDepth + 1
+  // register sets: the K rows of both 32-key blocks and, from step KL on, the LDS-held query part
+  // (int8 prefix at C5's shapes: 1,798 -> 1,765 us against one step ahead with the query part read at
+  // its MFMAs; ISO3 unchanged)
+  constexpr int R = kQkDepth + 1;
+  V8 ka[R][2], ql[R];
+  auto issue = [&](int ks, int slot) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) ka[0][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, 2 * KS0 + h));
+    for (int kb = 0; kb < 2; ++kb) ka[slot][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, 2 * ks + h));
+    if (ks >= KL) ql[slot] = q_lds[(ks - KL) * 64];
+  };
+#pragma unroll
+  for (int d = 0; d < kQkDepth; ++d)
+    if (KS0 + d < KS1) issue(KS0 + d, d);
 #pragma unroll
   for (int ks = KS0; ks < KS1; ++ks) {
-    const int cb = (ks - KS0) & 1;
-    if (ks + 1 < KS1) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        ka[cb ^ 1][kb] = *reinterpret_cast<const V8*>(buf + k_img_off(32 * kb + l32, 2 * (ks + 1) + h));
-    }
-    // the next step's operand reads are issued before this step's MFMAs (a real double buffer:
-    // the scheduler would otherwise reuse one register set and wait for each read)
+    const int slot = (ks - KS0) % R;
+    if (ks + kQkDepth < KS1) issue(ks + kQkDepth, (ks - KS0 + kQkDepth) % R);
+    // the later steps' operand reads are issued before this step's MFMAs (a real ring: the scheduler
+    // would otherwise reuse one register set and wait for each read)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int part = 0; part < NQ; ++part) {
-      const V8 qv = (part == LP && ks >= KL) ? q_lds[(ks - KL) * 64] : q[part][ks];
+      const V8 qv = (part == LP && ks >= KL) ? ql[slot] : q[part][ks];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) S[kb] = Ops::mma(ka[cb][kb], qv, S[kb]);
+      for (int kb = 0; kb < 2; ++kb) S[kb] = Ops::mma(ka[slot][kb], qv, S[kb]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
