@@ -18,8 +18,9 @@
 //     accumulates its half of the rows in the rotated basis (three fp16 MFMAs per tile, as below).
 // Per wave this is half the operand work of a wave holding whole rows, and about 200 registers, so
 // two waves share a SIMD and keep two pages in flight each.
-// The 4 pairs merge (m, l, O) through LDS; the Hadamard back-rotation of the merged partial takes
-// its span-128 stage between the two halves through LDS and spans 1..64 inside each wave.
+// Pair 0 builds the query fragments in LDS for all pairs.  The 4 pairs merge (m, l, O) through LDS,
+// pair rt taking row tile rt; the Hadamard back-rotation of the merged partial takes its span-128
+// stage between the two halves through LDS and spans 1..64 inside each wave.
 #include <type_traits>
 
 #include "kvq_internal.h"
@@ -164,15 +165,18 @@ __device__ __forceinline__ void hadamard_half(f32x4 (&O)[RT][8], int lane) {
   }
 }
 
-// LDS layout (bytes)
+// LDS layout (bytes).  Page loop: q fragments, their per-row factors, partial scores.  Merge (after
+// the loop, from offset 0): every wave's half rows of every row tile, and the pairs' (m, l).
 template <int RT>
 struct VerifyLds {
   static constexpr int kQ = RT * 4 * 2 * 64 * 16;                       // q fragments
+  static constexpr int kQm = 2 * RT * 64 * 4;                           // q factors [half][rt][lane]
   static constexpr int kX = kPairs * 2 * 2 * RT * 64 * 16;              // partial scores [pair][parity][half][rt][lane]
-  static constexpr int kMergeO = kPairs * 2 * 8 * 64 * 16;              // one row tile: [pair][half][tile][lane]
-  static constexpr int kMergeML = kPairs * 2 * 64 * 4;                  // [pair][m | l][lane]
-  static constexpr int kLoop = kX > kMergeO + kMergeML ? kX : kMergeO + kMergeML;
-  static constexpr int kBytes = kQ + kLoop;
+  static constexpr int kLoop = kQ + kQm + kX;
+  static constexpr int kMergeO = RT * kPairs * 2 * 8 * 64 * 16;         // [rt][pair][half][tile][lane]
+  static constexpr int kMergeML = RT * kPairs * 2 * 64 * 4;             // [rt][pair][m | l][lane]
+  static constexpr int kMerge = kMergeO + kMergeML;
+  static constexpr int kBytes = kLoop > kMerge ? kLoop : kMerge;
 };
 
 template <int RT, int PPP>
@@ -239,15 +243,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
       }
     }
   }
-  // this wave's half of the query rows
+  // this wave's half of the query rows (pair 0 builds the fragments for all pairs)
   uint4 raw[RT][2][2];
+  if (pair == 0) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const uint16_t* qp = a.q + (size_t)qrow[rt] * kD + 16 * j4;
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint16_t* qp = a.q + (size_t)qrow[rt] * kD + 16 * j4;
 #pragma unroll
-    for (int gl = 0; gl < 2; ++gl) {
-      raw[rt][gl][0] = *reinterpret_cast<const uint4*>(qp + 64 * (2 * h + gl));
-      raw[rt][gl][1] = *reinterpret_cast<const uint4*>(qp + 64 * (2 * h + gl) + 8);
+      for (int gl = 0; gl < 2; ++gl) {
+        raw[rt][gl][0] = *reinterpret_cast<const uint4*>(qp + 64 * (2 * h + gl));
+        raw[rt][gl][1] = *reinterpret_cast<const uint4*>(qp + 64 * (2 * h + gl) + 8);
+      }
     }
   }
   __shared__ __align__(16) uint8_t smem[VerifyLds<RT>::kBytes];
@@ -307,11 +313,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
   }
 
   // q fragments (fp16, pre-scaled per row and half by a power of two so the bf16 values convert
-  // exactly), written to LDS by pair 0; the scale goes with the wave's partial scores
+  // exactly) and the factor that undoes the scaling (applied to the wave's partial scores), written
+  // to LDS by pair 0
   const QFrag<RT> qf{reinterpret_cast<const f16x8*>(smem) + lane};
-  float qmul[RT];
+  float* qmul_lds = reinterpret_cast<float*>(smem + VerifyLds<RT>::kQ);      // [half][rt][lane]
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < RT && pair == 0; ++rt) {
     float mx = 0.0f;
 #pragma unroll
     for (int gl = 0; gl < 2; ++gl)
@@ -337,9 +344,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
           f[2 * e] = (_Float16)ldexpf(bf16f(w[e] & 0xffffu), ex);
           f[2 * e + 1] = (_Float16)ldexpf(bf16f(w[e] >> 16), ex);
         }
-        if (pair == 0) const_cast<f16x8*>(qf.p)[((rt * 4 + 2 * h + gl) * 2 + x) * 64] = f;
+        const_cast<f16x8*>(qf.p)[((rt * 4 + 2 * h + gl) * 2 + x) * 64] = f;
       }
-    qmul[rt] = ldexpf(a.scale_log2, -ex);
+    qmul_lds[(h * RT + rt) * 64 + lane] = ldexpf(a.scale_log2, -ex);
   }
 
   float m_run[RT], l_run[RT];
@@ -351,7 +358,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
 #pragma unroll
     for (int t = 0; t < NT; ++t) O[rt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  f32x4* xbuf = reinterpret_cast<f32x4*>(smem + VerifyLds<RT>::kQ);   // [pair][parity][half][rt][lane]
+  f32x4* xbuf = reinterpret_cast<f32x4*>(smem + VerifyLds<RT>::kQ + VerifyLds<RT>::kQm);   // [pair][parity][half][rt][lane]
   auto xslot = [&](int par, int hh, int rt) { return xbuf + (((pair * 2 + par) * 2 + hh) * RT + rt) * 64 + lane; };
 
   // The pair's pages: n_mine of them.  The two waves of a pair meet once per page through LDS flags
@@ -361,7 +368,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
   const int last = max(n_mine, 1) - 1;
   __shared__ uint32_t flags[kWaves];
   if (lane == 0) flags[wv] = 0;
-  __syncthreads();                                          // q fragments and flags written
+  __syncthreads();                                          // q fragments, factors and flags written
+  float qmul[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) qmul[rt] = qmul_lds[(h * RT + rt) * 64 + lane];
 
   // fp16 V parts need every V scale of the wave's pages to be 0 or at least 2^-10 (see the PV step)
   bool v16;
@@ -546,86 +556,80 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) l_run[rt] = sum_over_row_lanes(l_run[rt]);
 
-  // ---- merge the 4 pairs, one row tile at a time: every wave stores its half rows (and the half-0
-  // wave the pair's m, l), then the two waves of pair 0 merge their halves over the pairs
-  f32x4* lds_o = reinterpret_cast<f32x4*>(smem + VerifyLds<RT>::kQ);          // [pair][half][tile][lane]
-  float* lds_ml = reinterpret_cast<float*>(smem + VerifyLds<RT>::kQ + VerifyLds<RT>::kMergeO);  // [pair][m | l][lane]
-  f32x4 M[RT][NT];
+  // ---- merge the 4 pairs: every wave stores its half rows of every row tile (and the half-0 wave
+  // the pair's m, l); then the two waves of pair rt merge row tile rt over the pairs
+  f32x4* lds_o = reinterpret_cast<f32x4*>(smem);                                  // [rt][pair][half][tile][lane]
+  float* lds_ml = reinterpret_cast<float*>(smem + VerifyLds<RT>::kMergeO);       // [rt][pair][m | l][lane]
+  __syncthreads();                                          // the page loop's use of this LDS is over
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    __syncthreads();                                        // the previous use of this LDS is over
 #pragma unroll
-    for (int t = 0; t < NT; ++t) lds_o[((pair * 2 + h) * NT + t) * 64 + lane] = O[rt][t];
+    for (int t = 0; t < NT; ++t) lds_o[(((rt * kPairs + pair) * 2 + h) * NT + t) * 64 + lane] = O[rt][t];
     if (h == 0) {
-      lds_ml[(pair * 2 + 0) * 64 + lane] = m_run[rt];
-      lds_ml[(pair * 2 + 1) * 64 + lane] = l_run[rt];
+      lds_ml[((rt * kPairs + pair) * 2 + 0) * 64 + lane] = m_run[rt];
+      lds_ml[((rt * kPairs + pair) * 2 + 1) * 64 + lane] = l_run[rt];
     }
-    __syncthreads();
-    if (pair != 0) continue;
+  }
+  __syncthreads();
+  const int mrt = pair < RT ? pair : 0;                     // the row tile this wave merges (pairs 0 .. RT - 1)
+  f32x4 M[1][NT];
+  float m_fin = kNegInf, l_fin = 0.0f;
+  if (pair < RT) {
     float mv[kPairs], cv[kPairs];
-    float Mx = kNegInf;
 #pragma unroll
     for (int v = 0; v < kPairs; ++v) {
-      mv[v] = lds_ml[(v * 2 + 0) * 64 + lane];
-      Mx = fmaxf(Mx, mv[v]);
+      mv[v] = lds_ml[((mrt * kPairs + v) * 2 + 0) * 64 + lane];
+      m_fin = fmaxf(m_fin, mv[v]);
     }
-    const float Mu = Mx == kNegInf ? 0.0f : Mx;
-    float l = 0.0f;
+    const float Mu = m_fin == kNegInf ? 0.0f : m_fin;
 #pragma unroll
     for (int v = 0; v < kPairs; ++v) {
       cv[v] = __builtin_amdgcn_exp2f(mv[v] - Mu);
-      l += cv[v] * lds_ml[(v * 2 + 1) * 64 + lane];
+      l_fin += cv[v] * lds_ml[((mrt * kPairs + v) * 2 + 1) * 64 + lane];
     }
-    m_run[rt] = Mx;
-    l_run[rt] = l;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      f32x4 acc = O[rt][t] * cv[0];
+      f32x4 acc = lds_o[(((mrt * kPairs + 0) * 2 + h) * NT + t) * 64 + lane] * cv[0];
 #pragma unroll
-      for (int v = 1; v < kPairs; ++v) acc += cv[v] * lds_o[((v * 2 + h) * NT + t) * 64 + lane];
-      M[rt][t] = acc;
+      for (int v = 1; v < kPairs; ++v) acc += cv[v] * lds_o[(((mrt * kPairs + v) * 2 + h) * NT + t) * 64 + lane];
+      M[0][t] = acc;
     }
   }
   // ---- back-rotation of the merged partial: span 128 between the two halves through LDS
   __syncthreads();
-  if (pair == 0) {
+  if (pair < RT) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) lds_o[((h * RT + rt) * NT + t) * 64 + lane] = M[rt][t];
+    for (int t = 0; t < NT; ++t) lds_o[((mrt * 2 + h) * NT + t) * 64 + lane] = M[0][t];
   }
   __syncthreads();
-  if (pair != 0) return;
+  if (pair >= RT) return;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const f32x4 other = lds_o[(((1 - h) * RT + rt) * NT + t) * 64 + lane];
-      M[rt][t] = h == 0 ? M[rt][t] + other : other - M[rt][t];
-    }
-  hadamard_half<RT>(M, lane);
+  for (int t = 0; t < NT; ++t) {
+    const f32x4 other = lds_o[((mrt * 2 + (1 - h)) * NT + t) * 64 + lane];
+    M[0][t] = h == 0 ? M[0][t] + other : other - M[0][t];
+  }
+  hadamard_half<1>(M, lane);
 
-  // ---- the partial of rows r < R (this wave's half); with a single split the normalised output
+  // ---- the partial of rows r < R (this wave's half of row tile mrt); with a single split the
+  // normalised output
   const bool direct = a.n_splits == 1;
+  const int r = 16 * mrt + i16;
+  if (r >= R) return;
+  const int qr = RT > 1 && mrt == 1 ? qrow[RT - 1] : qrow[0];
+  float* row = direct ? a.out + (size_t)qr * kD : part_o + ((row0 + r) * a.n_splits + split) * kD;
+  const float sc = direct ? (l_fin > 0.0f ? 1.0f / l_fin : 0.0f) : 1.0f;
+  auto put4 = [&](float* p, float x0, float x1, float x2, float x3) {
+    *reinterpret_cast<float4*>(p) = make_float4(x0 * sc, x1 * sc, x2 * sc, x3 * sc);
+  };
+  if (!direct && j4 == 0 && h == 0) {
+    float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
+    ml[0] = m_fin; ml[1] = l_fin;
+  }
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + i16;
-    if (r >= R) continue;
-    float* row = direct ? a.out + (size_t)qrow[rt] * kD : part_o + ((row0 + r) * a.n_splits + split) * kD;
-    const float sc = direct ? (l_run[rt] > 0.0f ? 1.0f / l_run[rt] : 0.0f) : 1.0f;
-    auto put4 = [&](float* p, float x0, float x1, float x2, float x3) {
-      *reinterpret_cast<float4*>(p) = make_float4(x0 * sc, x1 * sc, x2 * sc, x3 * sc);
-    };
-    if (!direct && j4 == 0 && h == 0) {
-      float* ml = part_ml + ((row0 + r) * a.n_splits + split) * 2;
-      ml[0] = m_run[rt]; ml[1] = l_run[rt];
-    }
-#pragma unroll
-    for (int gl = 0; gl < 4; ++gl) {   // tiles 2gl (even d) / 2gl+1 (odd d): d = 128h + 32gl + 8 j4 + 2k (+1)
-      const f32x4 e = M[rt][2 * gl], o = M[rt][2 * gl + 1];
-      put4(row + 128 * h + 32 * gl + 8 * j4, e[0], o[0], e[1], o[1]);
-      put4(row + 128 * h + 32 * gl + 8 * j4 + 4, e[2], o[2], e[3], o[3]);
-    }
+  for (int gl = 0; gl < 4; ++gl) {   // tiles 2gl (even d) / 2gl+1 (odd d): d = 128h + 32gl + 8 j4 + 2k (+1)
+    const f32x4 e = M[0][2 * gl], o = M[0][2 * gl + 1];
+    put4(row + 128 * h + 32 * gl + 8 * j4, e[0], o[0], e[1], o[1]);
+    put4(row + 128 * h + 32 * gl + 8 * j4 + 4, e[2], o[2], e[3], o[3]);
   }
 }
 
