@@ -11,11 +11,13 @@
 // split head_dim: wave half h holds values 128h .. 128h + 127 of every row.
 //   * QK: each wave contracts its half (K scale groups 2h, 2h + 1) on v_mfma_f32_16x16x32_f16 with
 //     exact fp16 codes and the pre-scaled query, weights the two groups by their scales and writes
-//     its partial scores to LDS; once its partner has published the same page (an LDS flag per wave)
-//     each wave adds the partner's (half 0's partial first, so both waves of a pair hold bit-identical
-//     scores) and both run the same online softmax.
+//     its partial scores to LDS (an LDS flag per wave publishes each step).  With two row tiles wave h
+//     adds the two halves' partials of row tile h, runs its online softmax and hands the weights and
+//     the rescale factor to its partner the same way; with one row tile both waves run it (half 0's
+//     partial first, so they agree bit for bit).
 //   * PV: each wave builds the exact V operand (code - 8) * d only for its four 32-value groups and
-//     accumulates its half of the rows in the rotated basis (three fp16 MFMAs per tile, as below).
+//     accumulates its half of the rows in the rotated basis (two fp16 MFMAs per tile and row tile, as
+//     below).
 // Per wave this is half the operand work of a wave holding whole rows, and about 200 registers, so
 // two waves share a SIMD and keep two pages in flight each.
 // Pair 0 builds the query fragments in LDS for all pairs.  The 4 pairs merge (m, l, O) through LDS,
@@ -172,7 +174,9 @@ struct VerifyLds {
   static constexpr int kQ = RT * 4 * 2 * 64 * 16;                       // q fragments
   static constexpr int kQm = 2 * RT * 64 * 4;                           // q factors [half][rt][lane]
   static constexpr int kX = kPairs * 2 * 2 * RT * 64 * 16;              // partial scores [pair][parity][half][rt][lane]
-  static constexpr int kLoop = kQ + kQm + kX;
+  static constexpr int kW = kPairs * 2 * 2 * 64 * 16;                   // weight records [pair][parity][half][lane]
+  static constexpr int kA = kPairs * 2 * 2 * 64 * 4;                    // rescale factors [pair][parity][half][lane]
+  static constexpr int kLoop = kQ + kQm + kX + kW + kA;
   static constexpr int kMergeO = RT * kPairs * 2 * 8 * 64 * 16;         // [rt][pair][half][tile][lane]
   static constexpr int kMergeML = RT * kPairs * 2 * 64 * 4;             // [rt][pair][m | l][lane]
   static constexpr int kMerge = kMergeO + kMergeML;
@@ -360,6 +364,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
   }
   f32x4* xbuf = reinterpret_cast<f32x4*>(smem + VerifyLds<RT>::kQ + VerifyLds<RT>::kQm);   // [pair][parity][half][rt][lane]
   auto xslot = [&](int par, int hh, int rt) { return xbuf + (((pair * 2 + par) * 2 + hh) * RT + rt) * 64 + lane; };
+  uint4* wbuf = reinterpret_cast<uint4*>(smem + VerifyLds<RT>::kQ + VerifyLds<RT>::kQm + VerifyLds<RT>::kX);
+  float* abuf = reinterpret_cast<float*>(smem + VerifyLds<RT>::kQ + VerifyLds<RT>::kQm + VerifyLds<RT>::kX + VerifyLds<RT>::kW);
+  auto wslot = [&](int par, int hh) { return wbuf + ((pair * 2 + par) * 2 + hh) * 64 + lane; };
+  auto aslot = [&](int par, int hh) { return abuf + ((pair * 2 + par) * 2 + hh) * 64 + lane; };
+  // With two row tiles the waves of a pair split the softmax: wave h runs it for row tile h (m_own,
+  // l_own) and hands its weights to the partner through LDS.
+  constexpr bool SPLIT = RT == 2;
+  float m_own = kNegInf, l_own = 0.0f;
+  const int L_own = SPLIT && h ? Lrow[RT - 1] : Lrow[0];
 
   // The pair's pages: n_mine of them.  The two waves of a pair meet once per page through LDS flags
   // (flags[w] = page steps wave w has published), not a workgroup barrier, so the pairs run apart
@@ -403,7 +416,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
       const HalfPage& pb = buf[i % (kPD + 1)];
       const int tok0 = (p0 + i * kPairs) * KVQ_PAGE_SIZE + 4 * j4;
       const int par = i & 1;
-      // ---- QK over this wave's half: partial scores, scaled, to LDS
+      // ---- QK over this wave's half: partial scores, scaled
+      f32x4 sp[RT];
       {
         f32x4 acc[RT][2];
 #pragma unroll
@@ -418,68 +432,109 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
           }
         }
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          f32x4 sp;
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            sp[k] = fmaf(acc[rt][1][k], pb.kscale(k, 1), acc[rt][0][k] * pb.kscale(k, 0)) * qmul[rt];
-          *xslot(par, h, rt) = sp;
+            sp[rt][k] = fmaf(acc[rt][1][k], pb.kscale(k, 1), acc[rt][0][k] * pb.kscale(k, 0)) * qmul[rt];
+      }
+      // Exchange with the partner wave through LDS slots of page parity par, each step published by a
+      // flag (flags[w] counts the steps wave w has published; a wave publishes two steps per page when
+      // it splits the softmax, one otherwise).  A slot is rewritten two pages later, after the partner
+      // has published a later step, which it does only after reading the slot.  The partner is in this
+      // workgroup and always gets there; each wait is bounded all the same.
+      const uint32_t steps = SPLIT ? 2u : 1u;
+      auto publish = [&](uint32_t n) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_store(&flags[wv], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      };
+      auto await = [&](uint32_t n) {
+        for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+          if (__hip_atomic_load(&flags[wv ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= n) break;
+          __builtin_amdgcn_s_sleep(0);
         }
-      }
-      // publish page step i (the scores are written before the flag), then wait for the partner's.
-      // (A slot is rewritten two steps later, after the partner has published the step between, which
-      // it does only after reading the slot.)  The partner is in this workgroup and always gets there;
-      // the wait is bounded all the same.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) __hip_atomic_store(&flags[wv], (uint32_t)(i + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
-        if (__hip_atomic_load(&flags[wv ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= (uint32_t)(i + 1)) break;
-        __builtin_amdgcn_s_sleep(0);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // ---- both halves' partial scores (half 0 first: both waves of the pair agree bit for bit),
-      // online softmax with lazy rescaling (the reference max moves only when a score exceeds it by
-      // more than 2^kLazyLog2)
-      float pk[RT][4];
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      };
+      // (values are exchanged as whole slots, and each wave reads its own back as well: a wave-uniform
+      // LDS address picks the row tile, where a choice in registers would cost a select per value)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const f32x4 s0 = *xslot(par, 0, rt), s1 = *xslot(par, 1, rt);
-        float s[4];
+      for (int rt = 0; rt < RT; ++rt) *xslot(par, h, rt) = sp[rt];
+      publish(steps * i + 1);
+      await(steps * i + 1);
+      // ---- scores (half 0's partial plus half 1's), online softmax with lazy rescaling (the reference
+      // max moves only when a score exceeds it by more than 2^kLazyLog2), the weights of each row tile
+      // as a record {hi parts of tokens 4 j4 .. + 3, lo parts}: fp16 parts of 16 x the weight (V16)
+      // or bf16 parts of the weight
+      auto softmax = [&](const f32x4& s0, const f32x4& s1, int L, float& m_run_r, float& l_run_r,
+                         float& alpha) -> uint4 {
+        float s[4], pk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s[k] = (tok0 + k < Lrow[rt]) ? s0[k] + s1[k] : kNegInf;
+        for (int k = 0; k < 4; ++k) s[k] = (tok0 + k < L) ? s0[k] + s1[k] : kNegInf;
         const float mx = max_over_row_lanes(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-        const bool move = mx > m_run[rt] + kLazyLog2;
-        const float m_new = move ? mx : m_run[rt];
+        const bool move = mx > m_run_r + kLazyLog2;
+        const float m_new = move ? mx : m_run_r;
         const float m_use = m_new == kNegInf ? 0.0f : m_new;
-        const bool rescale = move && m_run[rt] != kNegInf;
-        const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run[rt] - m_use) : 1.0f;
-        m_run[rt] = m_new;
+        const bool rescale = move && m_run_r != kNegInf;
+        alpha = rescale ? __builtin_amdgcn_exp2f(m_run_r - m_use) : 1.0f;
+        m_run_r = m_new;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pk[rt][k] = __builtin_amdgcn_exp2f(s[k] - m_use);
-        l_run[rt] = l_run[rt] * alpha + ((pk[rt][0] + pk[rt][1]) + (pk[rt][2] + pk[rt][3]));
-        if (__any(rescale)) {
+        for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_exp2f(s[k] - m_use);
+        l_run_r = l_run_r * alpha + ((pk[0] + pk[1]) + (pk[2] + pk[3]));
+        if constexpr (V16) {
+          f16x4 wh, wl;
 #pragma unroll
-          for (int t = 0; t < NT; ++t) O[rt][t] *= alpha;
+          for (int k = 0; k < 4; ++k) {
+            const float x = 16.0f * pk[k];
+            wh[k] = (_Float16)x;
+            wl[k] = (_Float16)(x - (float)wh[k]);
+          }
+          const uint2 hh2 = __builtin_bit_cast(uint2, wh), ll2 = __builtin_bit_cast(uint2, wl);
+          return make_uint4(hh2.x, hh2.y, ll2.x, ll2.y);
+        } else {
+          s16x4 ph, pl;
+          split_bf16(pk, ph, pl);
+          const uint2 hh2 = __builtin_bit_cast(uint2, ph), ll2 = __builtin_bit_cast(uint2, pl);
+          return make_uint4(hh2.x, hh2.y, ll2.x, ll2.y);
         }
+      };
+      uint4 wrec[RT];
+      float alpha[RT];
+      if constexpr (SPLIT) {
+        float a_own;
+        *wslot(par, h) = softmax(*xslot(par, 0, h), *xslot(par, 1, h), L_own, m_own, l_own, a_own);
+        *aslot(par, h) = a_own;
+        publish(steps * i + 2);
+        await(steps * i + 2);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          wrec[rt] = *wslot(par, rt);
+          alpha[rt] = *aslot(par, rt);
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          wrec[rt] = softmax(*xslot(par, 0, rt), *xslot(par, 1, rt), Lrow[rt], m_run[rt], l_run[rt], alpha[rt]);
       }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        if (__any(alpha[rt] != 1.0f)) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) O[rt][t] *= alpha[rt];
+        }
       // ---- PV over this wave's four V groups: V enters the MFMA as the exact product (code - 8) * d in
-      // two parts, built once per page for both row tiles, and the weights split into two parts once
-      // per row tile.  One K = 32 MFMA takes the lane's 4 tokens twice: A = [V hi | V lo] against
-      // B = [w hi ; w hi], then against [w lo ; w lo] (the full product of the two-part values; a
-      // K = 16 MFMA costs as much as a K = 32 one here).  fp16 parts (V16): the product / 16 in fp16
-      // (hi = the rounded product, lo = its exact rounding error from one fma; the 1/16 keeps it below
-      // 2^15) against fp16 parts of 16 x the weights; otherwise bf16 parts of the product (a 4-bit code
-      // times an fp16 scale has at most 15 significant bits) against bf16 parts of the weights.
+      // two parts, built once per page for both row tiles, and the weights in two parts (the record).
+      // One K = 32 MFMA takes the lane's 4 tokens twice: A = [V hi | V lo] against B = [w hi ; w hi],
+      // then against [w lo ; w lo] (the full product of the two-part values; a K = 16 MFMA costs as
+      // much as a K = 32 one here).  fp16 parts (V16): the product / 16 in fp16 (hi = the rounded
+      // product, lo = its exact rounding error from one fma; the 1/16 keeps it below 2^15) against
+      // fp16 parts of 16 x the weights; otherwise bf16 parts of the product (a 4-bit code times an
+      // fp16 scale has at most 15 significant bits) against bf16 parts of the weights.
       if constexpr (V16) {
         f16x8 wh[RT], wl[RT];                               // each part twice: tokens 4 j4 .. + 3, again
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float x = 16.0f * pk[rt][k];
-            wh[rt][k] = wh[rt][k + 4] = (_Float16)x;
-            wl[rt][k] = wl[rt][k + 4] = (_Float16)(x - (float)wh[rt][k]);
-          }
+        for (int rt = 0; rt < RT; ++rt) {
+          wh[rt] = __builtin_bit_cast(f16x8, make_uint4(wrec[rt].x, wrec[rt].y, wrec[rt].x, wrec[rt].y));
+          wl[rt] = __builtin_bit_cast(f16x8, make_uint4(wrec[rt].z, wrec[rt].w, wrec[rt].z, wrec[rt].w));
+        }
         const f16x2 mul = {(_Float16)0.0625f, (_Float16)0.0625f}, add = {(_Float16)-64.5f, (_Float16)-64.5f};
 #pragma unroll
         for (int gl = 0; gl < 4; ++gl) {
@@ -510,10 +565,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
         bf16x8 bqh[RT], bql[RT];                            // each part twice, as above
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          s16x4 ph, pl;
-          split_bf16(pk[rt], ph, pl);
-          bqh[rt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(ph, ph, 0, 1, 2, 3, 0, 1, 2, 3));
-          bql[rt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pl, pl, 0, 1, 2, 3, 0, 1, 2, 3));
+          bqh[rt] = __builtin_bit_cast(bf16x8, make_uint4(wrec[rt].x, wrec[rt].y, wrec[rt].x, wrec[rt].y));
+          bql[rt] = __builtin_bit_cast(bf16x8, make_uint4(wrec[rt].z, wrec[rt].w, wrec[rt].z, wrec[rt].w));
         }
 #pragma unroll
         for (int gl = 0; gl < 4; ++gl) {
@@ -553,11 +606,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
   else run(std::false_type{});
 
   // ---- per-wave row sums over the 4 lane groups
+  if constexpr (SPLIT) {
+    l_own = sum_over_row_lanes(l_own);
+  } else {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) l_run[rt] = sum_over_row_lanes(l_run[rt]);
+    for (int rt = 0; rt < RT; ++rt) l_run[rt] = sum_over_row_lanes(l_run[rt]);
+  }
 
-  // ---- merge the 4 pairs: every wave stores its half rows of every row tile (and the half-0 wave
-  // the pair's m, l); then the two waves of pair rt merge row tile rt over the pairs
+  // ---- merge the 4 pairs: every wave stores its half rows of every row tile (and the pair's m, l of
+  // row tile rt: the wave that ran its softmax, else the half-0 wave); then the two waves of pair rt
+  // merge row tile rt over the pairs
   f32x4* lds_o = reinterpret_cast<f32x4*>(smem);                                  // [rt][pair][half][tile][lane]
   float* lds_ml = reinterpret_cast<float*>(smem + VerifyLds<RT>::kMergeO);       // [rt][pair][m | l][lane]
   __syncthreads();                                          // the page loop's use of this LDS is over
@@ -565,9 +623,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_verify_k8v4(const DecodeArgs
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) lds_o[(((rt * kPairs + pair) * 2 + h) * NT + t) * 64 + lane] = O[rt][t];
-    if (h == 0) {
-      lds_ml[((rt * kPairs + pair) * 2 + 0) * 64 + lane] = m_run[rt];
-      lds_ml[((rt * kPairs + pair) * 2 + 1) * 64 + lane] = l_run[rt];
+    if (SPLIT ? rt == h : h == 0) {
+      lds_ml[((rt * kPairs + pair) * 2 + 0) * 64 + lane] = SPLIT ? m_own : m_run[rt];
+      lds_ml[((rt * kPairs + pair) * 2 + 1) * 64 + lane] = SPLIT ? l_own : l_run[rt];
     }
   }
   __syncthreads();
