@@ -71,6 +71,31 @@ def _fill(w, fmt_k, fmt_v):
     return sk, sv
 
 
+def test_locate_worked_example():
+    """Paged addressing on a hand-worked table (strata PR #120, Tests: append and gather through a
+    non-identity page table): token j of sequence b sits in slot j mod 16 of the page that the table
+    names for block j div 16.  The expected pairs are written out, not recomputed."""
+    table = np.array([[7, 3, 9, 0], [2, 11, 5, 4]], np.int32)
+    seq = [0, 0, 0, 0, 0, 1, 1, 1, 1]
+    pos = [0, 15, 16, 31, 40, 0, 17, 47, 63]
+    page, slot = paged.locate(table, seq, pos, 16)
+    assert page.tolist() == [7, 7, 3, 3, 9, 2, 11, 5, 4]
+    assert slot.tolist() == [0, 15, 0, 15, 8, 0, 1, 15, 15]
+
+
+def test_append_writes_exactly_the_located_cell():
+    """One appended token changes only its own cell: page 9, slot 8 for token 40 of sequence 0 in the
+    table above, every KV head of it, and nothing else in the store."""
+    table = np.array([[7, 3, 9, 0], [2, 11, 5, 4]], np.int32)
+    for fmt in ("int8", "q4h"):
+        st = paged.Store.empty(fmt, 12, 2, 16, 256)
+        x = synth.normal_bf16(np.random.default_rng(5), (1, 2, 256))
+        paged.append(st, table, [0], [40], x, 16)
+        changed = np.argwhere(st.codes.reshape(12, 2, 16, -1).any(axis=3))
+        assert changed.tolist() == [[9, 0, 8], [9, 1, 8]]
+        assert np.argwhere(st.scales.view(np.uint16).any(axis=3)).tolist() == [[9, 0, 8], [9, 1, 8]]
+
+
 def test_paged_gather_independent_of_page_table():
     for fmt in ("int8", "q4h", "iso3"):
         D = 256 if fmt == "q4h" else 128
