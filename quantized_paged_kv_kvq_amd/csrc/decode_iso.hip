@@ -40,6 +40,7 @@
 
 #include "kvq_internal.h"
 #include "device_util.h"
+#include "decode_parts.h"
 #include "iso_levels.h"
 
 namespace kvq {
@@ -244,12 +245,32 @@ __device__ __forceinline__ void iso_page_step(const IsoPage<BITS, D / 128>& pb, 
   // ---- PV per block: tiles 8b + t' hold head_dim 128b + 8 * (A row) + t'
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float w[4];
+    f16x4 bh, bl, bp;
+    if constexpr (DUP) {
+      // one part per column: a token pair's hi and lo parts of x * norm from four mixed-precision fmas,
+      // one packed select per pair (norm (k, b): ISO3 fp16 half (k NB + b) & 1 of word (k NB + b) / 2,
+      // ISO4 fp32 word k NB + b)
+      constexpr float C = kPScale / kLevelScale<BITS>;
+      const float x0 = pk[0] * C, x1 = pk[1] * C, x2 = pk[2] * C, x3 = pk[3] * C;
+      uint2 p01, p23;
+      if constexpr (BITS == 4) {
+        p01 = mix_parts2<0, 0, 0, 0>(x0, pb.vn[b], x1, pb.vn[NB + b]);
+        p23 = mix_parts2<0, 0, 0, 0>(x2, pb.vn[2 * NB + b], x3, pb.vn[3 * NB + b]);
+      } else if constexpr (NB == 1) {
+        p01 = mix_parts2<1, 0, 1, 1>(x0, pb.vn[0], x1, pb.vn[0]);
+        p23 = mix_parts2<1, 0, 1, 1>(x2, pb.vn[1], x3, pb.vn[1]);
+      } else {
+        static_assert(NB == 2, "head_dim 128 or 256");
+        p01 = b ? mix_parts2<1, 1, 1, 1>(x0, pb.vn[0], x1, pb.vn[1]) : mix_parts2<1, 0, 1, 0>(x0, pb.vn[0], x1, pb.vn[1]);
+        p23 = b ? mix_parts2<1, 1, 1, 1>(x2, pb.vn[2], x3, pb.vn[3]) : mix_parts2<1, 0, 1, 0>(x2, pb.vn[2], x3, pb.vn[3]);
+      }
+      bp = __builtin_bit_cast(f16x4, lo_col ? make_uint2(p01.y, p23.y) : make_uint2(p01.x, p23.x));
+    } else {
+      float w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = pk[k] * (pb.vnorm(k, b) * (kPScale / kLevelScale<BITS>));
-    f16x4 bh, bl;
-    split_f16(w, bh, bl);
-    const f16x4 bp = lo_col ? bl : bh;
+      for (int k = 0; k < 4; ++k) w[k] = pk[k] * (pb.vnorm(k, b) * (kPScale / kLevelScale<BITS>));
+      split_f16(w, bh, bl);
+    }
     uint32_t xv[4];               // code bits of token 4g + j: head_dim 8n .. 8n+7 of block b
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

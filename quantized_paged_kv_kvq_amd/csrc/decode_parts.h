@@ -37,6 +37,25 @@ __device__ __forceinline__ f16x4 nibbles_to_f16x4(uint32_t nib) {
   return f16x4{p0[0], p0[1], p1[0], p1[1]};
 }
 
+// fp16 parts of the products x0 * d0 and x1 * d1 (x fp32; d the fp16 in half H of its word when S
+// is 1, the fp32 word itself when S is 0): .x = [hi0 | hi1] with hi the product rounded to fp16, .y =
+// [lo0 | lo1] with lo the product minus hi rounded to fp16, each from one v_fma_mix (its fma is exact
+// before the one rounding), so hi + lo keeps about 22 significant bits.  The leading wait state
+// covers an x written by a transcendental instruction just before: the compiler pads that hazard
+// for its own instructions but not for inline assembly.
+template <int S0, int H0, int S1, int H1>
+__device__ __forceinline__ uint2 mix_parts2(float x0, uint32_t d0, float x1, uint32_t d1) {
+  uint32_t h, l;
+  asm("s_nop 0\n\t"
+      "v_fma_mixlo_f16 %0, %2, %3, 0 op_sel:[0,%c6,0] op_sel_hi:[0,%c7,0]\n\t"
+      "v_fma_mixhi_f16 %0, %4, %5, 0 op_sel:[0,%c8,0] op_sel_hi:[0,%c9,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel:[0,%c6,0] op_sel_hi:[0,%c7,1]\n\t"
+      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,%c8,1] op_sel_hi:[0,%c9,1]"
+      : "=&v"(h), "=&v"(l)
+      : "v"(x0), "v"(d0), "v"(x1), "v"(d1), "n"(S0 ? H0 : 0), "n"(S0), "n"(S1 ? H1 : 0), "n"(S1));
+  return make_uint2(h, l);
+}
+
 // 4 int8 codes -> bf16 (code + 128), exact (integers below 256 have 8 significant bits).
 __device__ __forceinline__ s16x4 codes_to_bf16_biased(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;

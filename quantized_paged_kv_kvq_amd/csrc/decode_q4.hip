@@ -153,13 +153,26 @@ __device__ __forceinline__ void q4_page_step(const Q4Page& pb, int p, int w, boo
   // d of cells past a sequence's length are finite by contract: zero-initialised slabs)
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
-    f16x4 bpart, blo;                                      // DUP: hi or lo part by column
+    // weight times the token's V d in fp16 parts: hi (the rounded product) and lo (the product minus
+    // hi, rounded once)
+    f16x4 bpart, blo;
+    if constexpr (DUP) {
+      // one part per column: both parts of a token pair from four mixed-precision fmas, then one
+      // packed select per pair
+      const uint32_t d0 = word_of(pb.vs[0], (g >> 1) & 3), d1 = word_of(pb.vs[1], (g >> 1) & 3),
+                     d2 = word_of(pb.vs[2], (g >> 1) & 3), d3 = word_of(pb.vs[3], (g >> 1) & 3);
+      const uint2 p01 = (g & 1) ? mix_parts2<1, 1, 1, 1>(pk[0], d0, pk[1], d1) : mix_parts2<1, 0, 1, 0>(pk[0], d0, pk[1], d1);
+      const uint2 p23 = (g & 1) ? mix_parts2<1, 1, 1, 1>(pk[2], d2, pk[3], d3) : mix_parts2<1, 0, 1, 0>(pk[2], d2, pk[3], d3);
+      bpart = __builtin_bit_cast(f16x4, lo_col ? make_uint2(p01.y, p23.y) : make_uint2(p01.x, p23.x));
+      blo = bpart;
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float pw = pk[k] * pb.vd(k, g);
-      const _Float16 hi = (_Float16)pw, lo = (_Float16)(pw - (float)hi);
-      bpart[k] = (DUP && lo_col) ? lo : hi;
-      blo[k] = lo;
+      for (int k = 0; k < 4; ++k) {
+        const float pw = pk[k] * pb.vd(k, g);
+        const _Float16 hi = (_Float16)pw, lo = (_Float16)(pw - (float)hi);
+        bpart[k] = hi;
+        blo[k] = lo;
+      }
     }
     const uint32_t wv = word_of(pb.v[g >> 2], g & 3);      // byte k: token 4w + k; nibbles: dims 32g + 2t (+1)
     const f16x4 alo = nibbles_to_f16x4(wv & 0x0f0f0f0fu), ahi = nibbles_to_f16x4((wv >> 4) & 0x0f0f0f0fu);
