@@ -27,16 +27,22 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
 # translation unit -> extra flags.  The decode kernels need their page loops fully unrolled (a rolled
-# loop waits for every outstanding load); the k8v4 verify and q4_0-K kernels keep their MFMA
-# accumulators in VGPRs (the default placed them in AGPRs and copied them around every MFMA).
+# loop waits for every outstanding load).  Their loops exit early after a wave's last page; the
+# unroller's bound for fully unrolling such loops by their maximum trip count is 8 by default, and the
+# 16-page loops of the ISO and q4_0 kernels (with their inline mixed-precision fmas) then stayed
+# rolled for some instances (ISO3 at head_dim 256, 4 waves x 16 pages: 120.8 against 47.1 us for one
+# sequence of 262,144 tokens), hence the bound of 16 for those units.  The k8v4 verify and q4_0-K
+# kernels keep their MFMA accumulators in VGPRs (the default placed them in AGPRs and copied them
+# around every MFMA).
 UNITS = {
     "kvq_api.hip": [],
     "append.hip": ["-ffp-contract=off"],
     "gather.hip": ["-ffp-contract=off"],
     "decode.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode_verify.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "decode_iso.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
-    "decode_q4.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "decode_iso.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-unroll-max-upperbound=16"],
+    "decode_q4.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-unroll-max-upperbound=16",
+                      "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode_f32.hip": ["-mllvm", "-pragma-unroll-threshold=200000", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "extend.hip": [],
 }

@@ -47,11 +47,12 @@ def test_iso3_decode_ragged_lengths(D):
                               n_kv_heads=2, head_dim=D))
 
 
-def test_iso3_decode_64_page_splits():
+@pytest.mark.parametrize("D", [128, 256])
+def test_iso3_decode_64_page_splits(D):
     """Four sequences over eight KV heads: 9 x 8 x 4 = 288 splits of 64 pages fill more than one
-    workgroup per CU, so the plan keeps 64-page splits (the other launch shape)."""
+    workgroup per CU, so the plan keeps 64-page splits (the other launch shape: 4 waves x 16 pages)."""
     check(synth.ragged_decode("iso3", "iso3", [9000, 8200, 4100, 9000], seed=83, n_q_heads=16, n_kv_heads=8,
-                              head_dim=128))
+                              head_dim=D))
 
 
 def test_iso3_decode_eight_rows_head_dim_256():
