@@ -666,7 +666,7 @@ def main():
                                              lambda: [decode_one(0, stream) for _ in range(R)])))
     pct = {k: round(float(np.percentile(dec_us, q)), 3) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
     # The dominant kernel alone: the same algorithmic bytes over the split kernel's cold median from
-    # the committed rocprofv3 trace of this build (None when the source has changed since)
+    # the committed rocprofv3 trace of the current kernel source (None when the source has changed since)
     rk = recorded_kernel(w.name) if fused else None
     kernel_level = None if rk is None else {
         "kernel": rk["kernel"], "median_us": rk["median_us"],
