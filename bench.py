@@ -544,11 +544,27 @@ def main():
     seq_lens = dev_i32(w.seq_lens)
     pages = kvq.Pages(block_table, seq_lens)
     caches = []
+    fill_us = []
+    if pre is not None:
+        p_seq, p_pos, p_k, p_v = dev_i32(pre[0]), dev_i32(pre[1]), dev_bf16(pre[2]), dev_bf16(pre[3])
     for r in range(R):
         c = kvq.PagedKVCache(w.num_pages, w.n_kv_heads, w.head_dim, w.fmt_k, w.fmt_v, quat=w.quat)
         if pre is not None:
-            kvq.kvq_append(c, pages, dev_bf16(pre[2]), dev_bf16(pre[3]), dev_i32(pre[0]), dev_i32(pre[1]))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            kvq.kvq_append(c, pages, p_k, p_v, p_seq, p_pos)
+            e1.record()
+            e1.synchronize()
+            fill_us.append(e0.elapsed_time(e1) * 1e3)
         caches.append(c)
+    if fill_us:
+        # the cache fill (outside the timed steps): one multi-token append of every prefix token
+        n_fill = len(pre[0])
+        fill_bytes = n_fill * w.n_kv_heads * (2 * 2 * w.head_dim + (cb_k + 2 * ns_k) + (cb_v + 2 * ns_v))
+        f_med = float(np.median(fill_us))
+        print(f"[bench] cache fill: kvq_append of {n_fill} tokens, median {f_med:.1f} us over {len(fill_us)} fills, "
+              f"{fill_bytes / f_med / 1e3:.0f} GB/s (bf16 read + cells written)", file=sys.stderr, flush=True)
+        del p_seq, p_pos, p_k, p_v
     s_seq, s_pos, s_k, s_v = (dev_i32(step[0]), dev_i32(step[1]), dev_bf16(step[2]), dev_bf16(step[3]))
     # the fused call takes the step's tokens as [batch][n_q][n_kv_heads][head_dim] (sequence, then position)
     f_k = s_k.view(w.batch, w.n_step, w.n_kv_heads, w.head_dim) if fusable(w) else None

@@ -56,91 +56,119 @@ __device__ __forceinline__ void locate(const AppendArgs& a, int tok, int& page, 
 // ---------------------------------------------------------------------------------------------
 // INT8_G64.  One thread encodes 4 consecutive values (int8_encode_x4); the 16 threads of a
 // 64-group are 16 consecutive lanes.
+template <int CPT>
 __device__ __forceinline__ void append_int8(const AppendArgs& a, const uint16_t* __restrict__ x,
                                             uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int D,
                                             bool is_v, int block) {
   const int tpc = D >> 2;                          // threads per cell
-  const int cpb = blockDim.x / tpc;                // cells per block
+  const int cpb = blockDim.x / tpc;                // cells per block and pass
   const int local = threadIdx.x / tpc;
   const int part = threadIdx.x - local * tpc;      // values 4*part .. 4*part+3
-  const long cell = (long)block * cpb + local;
   const long n_cells = (long)a.n_tok * a.hkv;
-  const bool active = local < cpb && cell < n_cells;
-  const long c = active ? cell : 0;
-  const int tok = (int)(c / a.hkv), head = (int)(c % a.hkv);
-
-  const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * D + 4 * part);
-  float v[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
-                bf16_to_f32(raw.y >> 16)};
-  const Int8x4 enc = int8_encode_x4(v);
-  const uint32_t packed = enc.packed;
-  if (!active) return;
-  int page, slot;
-  locate(a, tok, page, slot);
-  const size_t tile = (size_t)page * a.hkv + head;
-  uint8_t* base = codes + tile * KVQ_PAGE_SIZE * D;
-  if (!is_v) {
-    *reinterpret_cast<uint32_t*>(base + k_tile_offset(4 * part, slot)) = packed;   // 4 bytes of one chunk
-  } else {
+  // the block's CPT passes take CPT * cpb consecutive cells; every pass's load is issued before the
+  // first encode, so a thread keeps CPT loads in flight
+  uint2 raw[CPT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) base[v_tile_offset(4 * part + e, slot)] = (uint8_t)(packed >> (8 * e));
+  for (int i = 0; i < CPT; ++i) {
+    const long cell = ((long)block * CPT + i) * cpb + local;
+    const long c = cell < n_cells ? cell : 0;
+    raw[i] = *reinterpret_cast<const uint2*>(x + (size_t)c * D + 4 * part);
   }
-  if ((part & 15) == 0)
-    scales[(tile * KVQ_PAGE_SIZE + slot) * (D / 64) + (part >> 4)] = enc.scale_bits;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const long cell = ((long)block * CPT + i) * cpb + local;
+    float v[4] = {bf16_to_f32(raw[i].x & 0xffffu), bf16_to_f32(raw[i].x >> 16), bf16_to_f32(raw[i].y & 0xffffu),
+                  bf16_to_f32(raw[i].y >> 16)};
+    const Int8x4 enc = int8_encode_x4(v);          // (lane shuffles: every lane takes part)
+    if (cell >= n_cells) continue;
+    const uint32_t packed = enc.packed;
+    const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
+    int page, slot;
+    locate(a, tok, page, slot);
+    const size_t tile = (size_t)page * a.hkv + head;
+    uint8_t* base = codes + tile * KVQ_PAGE_SIZE * D;
+    if (!is_v) {
+      *reinterpret_cast<uint32_t*>(base + k_tile_offset(4 * part, slot)) = packed;   // 4 bytes of one chunk
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) base[v_tile_offset(4 * part + e, slot)] = (uint8_t)(packed >> (8 * e));
+    }
+    if ((part & 15) == 0)
+      scales[(tile * KVQ_PAGE_SIZE + slot) * (D / 64) + (part >> 4)] = enc.scale_bits;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
 // F32: one thread writes 4 consecutive values of a cell.  K tiles take them as one 16-byte chunk;
 // V tiles keep each value's 16 slots together (4-byte stores, 64 bytes apart).
+template <int CPT>
 __device__ __forceinline__ void append_f32(const AppendArgs& a, const uint16_t* __restrict__ x,
                                            uint8_t* __restrict__ codes, int D, bool is_v, int block) {
   const int tpc = D >> 2;                          // threads per cell
-  const int cpb = blockDim.x / tpc;                // cells per block
+  const int cpb = blockDim.x / tpc;                // cells per block and pass
   const int local = threadIdx.x / tpc;
   const int part = threadIdx.x - local * tpc;      // values 4*part .. 4*part+3
-  const long cell = (long)block * cpb + local;
-  if (local >= cpb || cell >= (long)a.n_tok * a.hkv) return;
-  const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
-  const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * D + 4 * part);
-  const float v[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
-                      bf16_to_f32(raw.y >> 16)};
-  int page, slot;
-  locate(a, tok, page, slot);
-  uint8_t* base = codes + ((size_t)page * a.hkv + head) * KVQ_PAGE_SIZE * (4 * D);
-  if (!is_v) {
-    *reinterpret_cast<float4*>(base + k_tile_offset(16 * part, slot)) = make_float4(v[0], v[1], v[2], v[3]);
-  } else {
+  const long n_cells = (long)a.n_tok * a.hkv;
+  uint2 raw[CPT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(base + vf32_tile_offset(4 * (4 * part + e), slot)) = v[e];
+  for (int i = 0; i < CPT; ++i) {
+    const long cell = ((long)block * CPT + i) * cpb + local;
+    raw[i] = cell < n_cells ? *reinterpret_cast<const uint2*>(x + (size_t)cell * D + 4 * part) : make_uint2(0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const long cell = ((long)block * CPT + i) * cpb + local;
+    if (cell >= n_cells) continue;
+    const float v[4] = {bf16_to_f32(raw[i].x & 0xffffu), bf16_to_f32(raw[i].x >> 16),
+                        bf16_to_f32(raw[i].y & 0xffffu), bf16_to_f32(raw[i].y >> 16)};
+    const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
+    int page, slot;
+    locate(a, tok, page, slot);
+    uint8_t* base = codes + ((size_t)page * a.hkv + head) * KVQ_PAGE_SIZE * (4 * D);
+    if (!is_v) {
+      *reinterpret_cast<float4*>(base + k_tile_offset(16 * part, slot)) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<float*>(base + vf32_tile_offset(4 * (4 * part + e), slot)) = v[e];
+    }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Q4_0_H256 (K or V; their tiles differ in byte order).  One wave per cell; lane l holds elements
 // 4l .. 4l+3 (the encoder is q4h_encode_x4).
+template <int CPT>
 __device__ __forceinline__ void append_q4h(const AppendArgs& a, const uint16_t* __restrict__ x,
                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, bool is_v,
                                            int block) {
   const int lane = threadIdx.x & 63;
-  const long cell = (long)block * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const bool active = cell < (long)a.n_tok * a.hkv;
-  const long c = active ? cell : 0;
-  const int tok = (int)(c / a.hkv), head = (int)(c % a.hkv);
-
-  const uint2 raw = *reinterpret_cast<const uint2*>(x + ((size_t)tok * a.hkv + head) * 256 + 4 * lane);
-  float y[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
-                bf16_to_f32(raw.y >> 16)};
-  const Q4x4 e = q4h_encode_x4(y, lane);
-  if (!active) return;
-  int page, slot;
-  locate(a, tok, page, slot);
-  const size_t tile = (size_t)page * a.hkv + head;
-  uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128;
-  const int o0 = is_v ? v_tile_offset(2 * lane, slot) : k4_tile_offset(2 * lane, slot);
-  const int o1 = is_v ? v_tile_offset(2 * lane + 1, slot) : k4_tile_offset(2 * lane + 1, slot);
-  base[o0] = e.b0;
-  base[o1] = e.b1;
-  if ((lane & 7) == 0) scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)] = e.d_bits;
+  const int wpb = blockDim.x >> 6;                 // cells per block and pass
+  const long n_cells = (long)a.n_tok * a.hkv;
+  uint2 raw[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const long cell = ((long)block * CPT + i) * wpb + (threadIdx.x >> 6);
+    const long c = cell < n_cells ? cell : 0;
+    raw[i] = *reinterpret_cast<const uint2*>(x + (size_t)c * 256 + 4 * lane);
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const long cell = ((long)block * CPT + i) * wpb + (threadIdx.x >> 6);
+    float y[4] = {bf16_to_f32(raw[i].x & 0xffffu), bf16_to_f32(raw[i].x >> 16), bf16_to_f32(raw[i].y & 0xffffu),
+                  bf16_to_f32(raw[i].y >> 16)};
+    const Q4x4 e = q4h_encode_x4(y, lane);         // (wave-wide shuffles: every lane takes part)
+    if (cell >= n_cells) continue;
+    const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
+    int page, slot;
+    locate(a, tok, page, slot);
+    const size_t tile = (size_t)page * a.hkv + head;
+    uint8_t* base = codes + tile * KVQ_PAGE_SIZE * 128;
+    const int o0 = is_v ? v_tile_offset(2 * lane, slot) : k4_tile_offset(2 * lane, slot);
+    const int o1 = is_v ? v_tile_offset(2 * lane + 1, slot) : k4_tile_offset(2 * lane + 1, slot);
+    base[o0] = e.b0;
+    base[o1] = e.b1;
+    if ((lane & 7) == 0) scales[(tile * KVQ_PAGE_SIZE + slot) * 8 + (lane >> 3)] = e.d_bits;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -241,13 +269,14 @@ __device__ __forceinline__ void append_iso(const AppendArgs& a, const uint16_t* 
 }
 
 // Blocks needed by one store's encoder for n_tok tokens (256 threads per block).
-long blocks_for(int fmt, int D, long cells) {
+// `passes`: cells per thread of the int8 and q4_0 encoders (FP32 and ISO take one).
+long blocks_for(int fmt, int D, long cells, int passes) {
   if (fmt == KVQ_FMT_INT8_G64 || fmt == KVQ_FMT_F32) {
-    const int cpb = 256 / (D / 4);
+    const int cpb = 256 / (D / 4) * (fmt == KVQ_FMT_INT8_G64 ? passes : 1);
     return (cells + cpb - 1) / cpb;
   }
-  if (fmt == KVQ_FMT_Q4_0_H256) return (cells + 3) / 4;   // ISO3 / ISO4 below: one wave per block
-  return (cells * (D / 128) + 3) / 4;
+  if (fmt == KVQ_FMT_Q4_0_H256) return (cells + 4 * passes - 1) / (4 * passes);
+  return (cells * (D / 128) + 3) / 4;             // ISO3 / ISO4: one wave per 128-value block
 }
 
 struct StoreArgs {
@@ -260,16 +289,29 @@ struct StoreArgs {
 };
 
 // One launch encodes both stores: blockIdx.y picks K (0) or V (1); blocks past a store's count exit.
+// PLAIN instantiates the int8, q4_0 and FP32 encoders, ISO the ISO3 / ISO4 ones (their registers
+// and code stay out of each other's kernels); PASSES is the int8 and q4_0 encoders' cells per thread.
+template <bool PLAIN, bool ISO, int PASSES>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a, StoreArgs k, StoreArgs v, int D, float qw, float qx,
                                                 float qy, float qz) {
   const StoreArgs& st = blockIdx.y == 0 ? k : v;
-  if ((long)blockIdx.x >= st.blocks) return;
-  const float quat[4] = {qw, qx, qy, qz};
-  if (st.fmt == KVQ_FMT_INT8_G64) append_int8(a, st.x, st.codes, st.scales, D, st.is_v != 0, blockIdx.x);
-  else if (st.fmt == KVQ_FMT_Q4_0_H256) append_q4h(a, st.x, st.codes, st.scales, st.is_v != 0, blockIdx.x);
-  else if (st.fmt == KVQ_FMT_F32) append_f32(a, st.x, st.codes, D, st.is_v != 0, blockIdx.x);
-  else if (st.fmt == KVQ_FMT_ISO4) append_iso<4>(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
-  else append_iso<3>(a, st.x, st.codes, st.scales, D, quat, blockIdx.x);
+  // Workgroups are dealt to the 8 XCDs round robin.  Block b encodes logical block (b % 8) * per +
+  // b / 8, so each XCD takes one contiguous run of a store's cells: the slots of a page, whose cells
+  // share cache lines, are written through one L2, which merges the partial lines before they go to HBM.
+  const long per = (st.blocks + 7) >> 3;           // this store's logical blocks per XCD
+  const long j = blockIdx.x >> 3;
+  const long lb = (long)(blockIdx.x & 7) * per + j;
+  if (j >= per || lb >= st.blocks) return;
+  if constexpr (PLAIN) {
+    if (st.fmt == KVQ_FMT_INT8_G64) return append_int8<PASSES>(a, st.x, st.codes, st.scales, D, st.is_v != 0, (int)lb);
+    if (st.fmt == KVQ_FMT_Q4_0_H256) return append_q4h<PASSES>(a, st.x, st.codes, st.scales, st.is_v != 0, (int)lb);
+    if (st.fmt == KVQ_FMT_F32) return append_f32<1>(a, st.x, st.codes, D, st.is_v != 0, (int)lb);
+  }
+  if constexpr (ISO) {
+    const float quat[4] = {qw, qx, qy, qz};
+    if (st.fmt == KVQ_FMT_ISO4) append_iso<4>(a, st.x, st.codes, st.scales, D, quat, (int)lb);
+    else if (st.fmt == KVQ_FMT_ISO3) append_iso<3>(a, st.x, st.codes, st.scales, D, quat, (int)lb);
+  }
 }
 
 }  // namespace
@@ -279,15 +321,33 @@ hipError_t launch_append_kv(int fmt_k, const uint16_t* xk, uint8_t* codes_k, uin
                             const AppendArgs& a, hipStream_t s) {
   const long cells = (long)a.n_tok * a.hkv;
   if (cells == 0 || (!xk && !xv)) return hipSuccess;
-  StoreArgs k{fmt_k, 0, xk, codes_k, scales_k, xk ? blocks_for(fmt_k, D, cells) : 0};
-  StoreArgs v{fmt_v, 1, xv, codes_v, scales_v, xv ? blocks_for(fmt_v, D, cells) : 0};
-  const long gx = k.blocks > v.blocks ? k.blocks : v.blocks;
+  // A multi-token append of more than about two rounds of the CUs (one thread per 4 values of a
+  // cell) streams from HBM: then each int8 / q4_0 thread takes 4 cells, all their loads in flight
+  // together (a cache fill of 131,072 tokens: 307 -> 212 us).  A decode step's append keeps one
+  // cell per thread, the shortest path.
+  auto is_iso = [](int f) { return f == KVQ_FMT_ISO3 || f == KVQ_FMT_ISO4; };
+  const long one_pass = (long)(xk ? blocks_for(fmt_k, D, cells, 1) : 0) + (xv ? blocks_for(fmt_v, D, cells, 1) : 0);
+  const int passes = one_pass > 16L * device_cu_count() ? 4 : 1;
+  StoreArgs k{fmt_k, 0, xk, codes_k, scales_k, xk ? blocks_for(fmt_k, D, cells, passes) : 0};
+  StoreArgs v{fmt_v, 1, xv, codes_v, scales_v, xv ? blocks_for(fmt_v, D, cells, passes) : 0};
+  const long gx = ((k.blocks > v.blocks ? k.blocks : v.blocks) + 7) / 8 * 8;   // whole rounds of the 8 XCDs
   dim3 grid((unsigned)gx, xv ? 2 : 1);
   if (!xk) {                                 // V only: make it the y == 0 slot
     k = v;
     grid.y = 1;
   }
-  k_append<<<grid, dim3(256), 0, s>>>(a, k, v, D, quat[0], quat[1], quat[2], quat[3]);
+  const bool iso = (xk && is_iso(fmt_k)) || (xv && is_iso(fmt_v));
+  const bool plain = (xk && !is_iso(fmt_k)) || (xv && !is_iso(fmt_v));
+  const float qw = quat[0], qx = quat[1], qy = quat[2], qz = quat[3];
+  if (plain && iso) {
+    if (passes == 4) k_append<true, true, 4><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
+    else k_append<true, true, 1><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
+  } else if (iso) {
+    k_append<false, true, 1><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
+  } else {
+    if (passes == 4) k_append<true, false, 4><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
+    else k_append<true, false, 1><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
+  }
   return hipGetLastError();
 }
 
