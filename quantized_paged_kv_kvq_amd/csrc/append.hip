@@ -216,67 +216,82 @@ __device__ __forceinline__ float rotate_component(float u, int lane, float w, fl
 
 // ISO4 (FreeToken PR #398, "What": the 4-bit sibling) takes the same steps with sixteen levels,
 // packs the codes as nibbles and keeps the corrected norm in binary32 (two 16-bit scale slots).
-template <int BITS>
+template <int BITS, int P>
 __device__ __forceinline__ void append_iso(const AppendArgs& a, const uint16_t* __restrict__ x,
                                            uint8_t* __restrict__ codes, uint16_t* __restrict__ norms, int D,
                                            const float quat[4], int block) {
-  __shared__ uint8_t lds_codes[4][128];
+  // P passes per wave: the wave encodes P 128-value blocks whose steps are independent, so their
+  // loads, shuffle reductions and searches overlap (one block's chain is latency-bound)
+  __shared__ uint8_t lds_codes[4][P][128];
   const float qw = quat[0], qx = quat[1], qy = quat[2], qz = quat[3];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nb = D / 128;
-  const long blk_id = (long)block * 4 + wv;
-  const bool active = blk_id < (long)a.n_tok * a.hkv * nb;
-  const long bi = active ? blk_id : 0;
-  const long cell = bi / nb;
-  const int blk = (int)(bi % nb);
-  const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
-
-  const uint16_t* src = x + ((size_t)tok * a.hkv + head) * D + blk * 128;
-  const float x0 = bf16_to_f32(src[lane]), x1 = bf16_to_f32(src[64 + lane]);
-  const float n = sqrtf(halving_sum128(x0 * x0, x1 * x1));
-  const float u0 = n > 0.0f ? x0 / n : 0.0f;
-  const float u1 = n > 0.0f ? x1 / n : 0.0f;
-  const float r0 = rotate_component(u0, lane, qw, qx, qy, qz);
-  const float r1 = rotate_component(u1, lane, qw, qx, qy, qz);
-  const int c0 = nearest_centroid<BITS>(r0), c1 = nearest_centroid<BITS>(r1);
-  const float k0 = iso_level<BITS>(c0), k1 = iso_level<BITS>(c1);
-  const float cn = sqrtf(halving_sum128(k0 * k0, k1 * k1));
-  const float norm = n / cn;
-
-  lds_codes[wv][lane] = (uint8_t)c0;
-  lds_codes[wv][64 + lane] = (uint8_t)c1;
-  __syncthreads();
-  if (!active) return;
-  int page, slot;
-  locate(a, tok, page, slot);
-  const size_t tile = (size_t)page * a.hkv + head;
-  if constexpr (BITS == 3) {
-    const int cb = nb * 48;
-    if (lane < 48) {
-      const int t = lane / 3;                          // 3 bytes hold codes 8t .. 8t+7
-      uint32_t word = 0;
+  const long n_blk = (long)a.n_tok * a.hkv * nb;
+  float x0[P], x1[P], n[P], norm[P];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) word |= (uint32_t)lds_codes[wv][8 * t + m] << (3 * m);
-      codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 48 + lane] = (uint8_t)(word >> (8 * (lane % 3)));
+  for (int i = 0; i < P; ++i) {
+    const long blk_id = ((long)block * P + i) * 4 + wv;
+    const long bi = blk_id < n_blk ? blk_id : 0;
+    const uint16_t* src = x + (size_t)(bi / nb) * D + (int)(bi % nb) * 128;
+    x0[i] = bf16_to_f32(src[lane]);
+    x1[i] = bf16_to_f32(src[64 + lane]);
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) n[i] = sqrtf(halving_sum128(x0[i] * x0[i], x1[i] * x1[i]));
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const float u0 = n[i] > 0.0f ? x0[i] / n[i] : 0.0f;
+    const float u1 = n[i] > 0.0f ? x1[i] / n[i] : 0.0f;
+    const float r0 = rotate_component(u0, lane, qw, qx, qy, qz);
+    const float r1 = rotate_component(u1, lane, qw, qx, qy, qz);
+    const int c0 = nearest_centroid<BITS>(r0), c1 = nearest_centroid<BITS>(r1);
+    x0[i] = iso_level<BITS>(c0);                       // (the levels replace the inputs)
+    x1[i] = iso_level<BITS>(c1);
+    lds_codes[wv][i][lane] = (uint8_t)c0;
+    lds_codes[wv][i][64 + lane] = (uint8_t)c1;
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) norm[i] = n[i] / sqrtf(halving_sum128(x0[i] * x0[i], x1[i] * x1[i]));
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const long blk_id = ((long)block * P + i) * 4 + wv;
+    if (blk_id >= n_blk) continue;
+    const long cell = blk_id / nb;
+    const int blk = (int)(blk_id % nb);
+    const int tok = (int)(cell / a.hkv), head = (int)(cell % a.hkv);
+    int page, slot;
+    locate(a, tok, page, slot);
+    const size_t tile = (size_t)page * a.hkv + head;
+    if constexpr (BITS == 3) {
+      const int cb = nb * 48;
+      if (lane < 48) {
+        const int t = lane / 3;                        // 3 bytes hold codes 8t .. 8t+7
+        uint32_t word = 0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) word |= (uint32_t)lds_codes[wv][i][8 * t + m] << (3 * m);
+        codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 48 + lane] = (uint8_t)(word >> (8 * (lane % 3)));
+      }
+      if (lane == 0) norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = f32_to_f16_bits(norm[i]);
+    } else {
+      const int cb = nb * 64;                          // byte j: code 2j (low nibble), 2j + 1 (high)
+      codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 64 + lane] =
+          (uint8_t)(lds_codes[wv][i][2 * lane] | (lds_codes[wv][i][2 * lane + 1] << 4));
+      if (lane == 0) reinterpret_cast<float*>(norms)[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = norm[i];
     }
-    if (lane == 0) norms[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = f32_to_f16_bits(norm);
-  } else {
-    const int cb = nb * 64;                            // byte j: code 2j (low nibble), 2j + 1 (high)
-    codes[(tile * KVQ_PAGE_SIZE + slot) * cb + blk * 64 + lane] =
-        (uint8_t)(lds_codes[wv][2 * lane] | (lds_codes[wv][2 * lane + 1] << 4));
-    if (lane == 0) reinterpret_cast<float*>(norms)[(tile * KVQ_PAGE_SIZE + slot) * nb + blk] = norm;
   }
 }
 
 // Blocks needed by one store's encoder for n_tok tokens (256 threads per block).
-// `passes`: cells per thread of the int8 and q4_0 encoders (FP32 and ISO take one).
+// `passes`: cells per thread of the int8 and q4_0 encoders, 128-value blocks per wave of the ISO
+// encoders (FP32 takes one).
 long blocks_for(int fmt, int D, long cells, int passes) {
   if (fmt == KVQ_FMT_INT8_G64 || fmt == KVQ_FMT_F32) {
     const int cpb = 256 / (D / 4) * (fmt == KVQ_FMT_INT8_G64 ? passes : 1);
     return (cells + cpb - 1) / cpb;
   }
   if (fmt == KVQ_FMT_Q4_0_H256) return (cells + 4 * passes - 1) / (4 * passes);
-  return (cells * (D / 128) + 3) / 4;             // ISO3 / ISO4: one wave per 128-value block
+  return (cells * (D / 128) + 4 * passes - 1) / (4 * passes);   // ISO3 / ISO4: one wave per 128-value block and pass
 }
 
 struct StoreArgs {
@@ -290,7 +305,8 @@ struct StoreArgs {
 
 // One launch encodes both stores: blockIdx.y picks K (0) or V (1); blocks past a store's count exit.
 // PLAIN instantiates the int8, q4_0 and FP32 encoders, ISO the ISO3 / ISO4 ones (their registers
-// and code stay out of each other's kernels); PASSES is the int8 and q4_0 encoders' cells per thread.
+// and code stay out of each other's kernels); PASSES is the encoders' cells (ISO: blocks) per thread
+// (FP32: one).
 template <bool PLAIN, bool ISO, int PASSES>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a, StoreArgs k, StoreArgs v, int D, float qw, float qx,
                                                 float qy, float qz) {
@@ -309,8 +325,8 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, StoreArgs k, Store
   }
   if constexpr (ISO) {
     const float quat[4] = {qw, qx, qy, qz};
-    if (st.fmt == KVQ_FMT_ISO4) append_iso<4>(a, st.x, st.codes, st.scales, D, quat, (int)lb);
-    else if (st.fmt == KVQ_FMT_ISO3) append_iso<3>(a, st.x, st.codes, st.scales, D, quat, (int)lb);
+    if (st.fmt == KVQ_FMT_ISO4) append_iso<4, PASSES>(a, st.x, st.codes, st.scales, D, quat, (int)lb);
+    else if (st.fmt == KVQ_FMT_ISO3) append_iso<3, PASSES>(a, st.x, st.codes, st.scales, D, quat, (int)lb);
   }
 }
 
@@ -321,10 +337,11 @@ hipError_t launch_append_kv(int fmt_k, const uint16_t* xk, uint8_t* codes_k, uin
                             const AppendArgs& a, hipStream_t s) {
   const long cells = (long)a.n_tok * a.hkv;
   if (cells == 0 || (!xk && !xv)) return hipSuccess;
-  // A multi-token append of more than about two rounds of the CUs (one thread per 4 values of a
-  // cell) streams from HBM: then each int8 / q4_0 thread takes 4 cells, all their loads in flight
-  // together (a cache fill of 131,072 tokens: 307 -> 212 us).  A decode step's append keeps one
-  // cell per thread, the shortest path.
+  // A multi-token append of more than about two rounds of the CUs at one cell (ISO: one 128-value
+  // block per wave) per thread streams from HBM: then each int8 / q4_0 thread takes 4 cells with
+  // all their loads in flight together (a cache fill of 131,072 tokens: 307 -> 212 us), and each
+  // ISO wave 4 blocks whose latency-bound chains overlap.  A decode step's append keeps one cell
+  // per thread, the shortest path.
   auto is_iso = [](int f) { return f == KVQ_FMT_ISO3 || f == KVQ_FMT_ISO4; };
   const long one_pass = (long)(xk ? blocks_for(fmt_k, D, cells, 1) : 0) + (xv ? blocks_for(fmt_v, D, cells, 1) : 0);
   const int passes = one_pass > 16L * device_cu_count() ? 4 : 1;
@@ -343,7 +360,8 @@ hipError_t launch_append_kv(int fmt_k, const uint16_t* xk, uint8_t* codes_k, uin
     if (passes == 4) k_append<true, true, 4><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
     else k_append<true, true, 1><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
   } else if (iso) {
-    k_append<false, true, 1><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
+    if (passes == 4) k_append<false, true, 4><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
+    else k_append<false, true, 1><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
   } else {
     if (passes == 4) k_append<true, false, 4><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);
     else k_append<true, false, 1><<<grid, dim3(256), 0, s>>>(a, k, v, D, qw, qx, qy, qz);

@@ -71,14 +71,15 @@ def test_append_decode_gather_stay_inside(fk, fv, D):
     assert_slabs_equal(cache, sk, sv)
 
 
-BULK = [("int8", "int8", 128), ("int8", "q4h", 256), ("q4h", "q4h", 256), ("int8", "f32", 256), ("f32", "int8", 256)]
+BULK = [("int8", "int8", 128), ("int8", "q4h", 256), ("q4h", "q4h", 256), ("int8", "f32", 256), ("f32", "int8", 256),
+        ("iso3", "iso3", 128), ("iso3", "iso3", 256), ("iso4", "iso4", 256)]
 
 
 @pytest.mark.parametrize("fk,fv,D", BULK, ids=[f"{a}-{b}-{d}" for a, b, d in BULK])
 def test_bulk_append_stays_inside(fk, fv, D):
-    """A multi-token append large enough that the int8 and q4_0 encoders take 4 cells per thread
-    (more than two rounds of the CUs at one cell per thread), with ragged sequence ends; in the mixed
-    cases the two stores' grids differ in size."""
+    """A multi-token append large enough that the int8 and q4_0 encoders take 4 cells per thread and
+    the ISO encoders 4 blocks per wave (more than two rounds of the CUs at one per thread), with
+    ragged sequence ends; in the mixed cases the two stores' grids differ in size."""
     import quantized_paged_kv_kvq_amd as kvq
     w = synth.ragged_decode(fk, fv, [8191, 3, 4100], seed=34, n_q_heads=8, n_kv_heads=2, head_dim=D)
     print(f"[guard] bulk append {fk}/{fv} D={D}", flush=True)
